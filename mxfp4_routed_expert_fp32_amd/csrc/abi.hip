@@ -1,0 +1,503 @@
+// C ABI of libmoe_mxfp4: argument validation, workspace carving and launch
+// sequencing.  Every check runs on the host before the first launch, so an
+// invalid call enqueues nothing (after "Deltafin's custom compiled runtime",
+// section "Configuration and device selection": explicit unsupported requests
+// fail early; and section "Model contract and pack authentication": lengths and
+// offsets use checked arithmetic).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/moe_mxfp4.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxHidden = 8192;
+constexpr int kMaxInter = 8192;
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 64;
+constexpr int64_t kMaxTokens = 1 << 20;
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool mul_ok(size_t a, size_t b, size_t* r) { return !__builtin_mul_overflow(a, b, r); }
+inline bool add_ok(size_t a, size_t b, size_t* r) { return !__builtin_add_overflow(a, b, r); }
+
+int check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->abi_version != MOE_ABI_VERSION || d->struct_size != sizeof(moe_layer_desc)) return MOE_ERR_ABI;
+  if (d->reserved != 0) return MOE_ERR_ABI;
+  if (d->layout != MOE_LAYOUT_ROWMAJOR_V1) return MOE_ERR_LAYOUT;
+  if (d->hidden < 32 || d->inter < 32 || d->n_experts < 1 || d->top_k_max < 1) return MOE_ERR_SHAPE;
+  if (d->hidden % 32 || d->inter % 32) return MOE_ERR_SHAPE;
+  if (d->top_k_max > d->n_experts || d->top_k_max > kMaxTopK) return MOE_ERR_SHAPE;
+  if (d->hidden > kMaxHidden || d->inter > kMaxInter || d->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Per-expert byte counts; checked.
+int expert_bytes(const moe_layer_desc* d, size_t* cb, size_t* sb) {
+  size_t hi;
+  if (!mul_ok((size_t)d->hidden, (size_t)d->inter, &hi)) return MOE_ERR_OVERFLOW;
+  if (!mul_ok(hi, 3, &hi)) return MOE_ERR_OVERFLOW;
+  *cb = hi / 2;
+  *sb = hi / 32;
+  return MOE_OK;
+}
+
+// Workspace carve: a bump allocator over the caller's buffer, 256-byte aligned.
+struct Carve {
+  size_t off = 0;
+  bool overflow = false;
+  size_t take(size_t bytes) {
+    size_t a = (off + 255) & ~size_t(255);
+    if (a < off) overflow = true;
+    size_t end;
+    if (!add_ok(a, bytes, &end)) overflow = true;
+    off = end;
+    return a;
+  }
+};
+
+struct FwdLayout {
+  size_t logits, idx, w, h, y, offsets, pairs, total;
+};
+
+int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
+  size_t TE, Tk, TkI, TkH;
+  if (!mul_ok((size_t)T, (size_t)d->n_experts, &TE) || !mul_ok((size_t)T, (size_t)k, &Tk) ||
+      !mul_ok(Tk, (size_t)d->inter, &TkI) || !mul_ok(Tk, (size_t)d->hidden, &TkH))
+    return MOE_ERR_OVERFLOW;
+  size_t b[7];
+  if (!mul_ok(TE, 4, &b[0]) || !mul_ok(Tk, 4, &b[1]) || !mul_ok(Tk, 4, &b[2]) || !mul_ok(TkI, 4, &b[3]) ||
+      !mul_ok(TkH, 4, &b[4]) || !mul_ok((size_t)d->n_experts + 1, 4, &b[5]) || !mul_ok(Tk, 4, &b[6]))
+    return MOE_ERR_OVERFLOW;
+  Carve c;
+  L->logits = c.take(b[0]);
+  L->idx = c.take(b[1]);
+  L->w = c.take(b[2]);
+  L->h = c.take(b[3]);
+  L->y = c.take(b[4]);
+  L->offsets = c.take(b[5]);
+  L->pairs = c.take(b[6]);
+  L->total = c.take(0);
+  if (c.overflow) return MOE_ERR_OVERFLOW;
+  // pair indices are int32 on the device
+  if (Tk > (size_t)INT32_MAX) return MOE_ERR_OVERFLOW;
+  return MOE_OK;
+}
+
+inline int dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+#define MOE_TRY(expr)             \
+  do {                            \
+    int rc_ = (expr);             \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
+  if (T < 1 || T > kMaxTokens) return MOE_ERR_SHAPE;
+  if (k < 1 || k > d->top_k_max) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// A5..A9 given routing (idx, w on the device).  For one token the pairs are
+// the k ranks of that token and idx itself is the pair -> expert map.
+int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_t* idx, const float* w,
+                const void* codes, const void* scales, int32_t T, int32_t k, float* out,
+                const float* resid, char* ws, const FwdLayout& L, hipStream_t s) {
+  const int H = d->hidden, I = d->inter, E = d->n_experts;
+  const int P = T * k;
+  float* h = reinterpret_cast<float*>(ws + L.h);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  MOE_TRY(dev(moe::launch_gateup_gemv(x, x_f32, idx, P, k, c, sc, H, I, E, h, s)));
+  MOE_TRY(dev(moe::launch_down_gemv(h, idx, P, c, sc, H, I, E, y, s)));
+  MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
+  return MOE_OK;
+}
+
+int check_forward_args(const moe_layer_desc* d, const void* x, int32_t x_dtype, const void* codes,
+                       const void* scales, int32_t T, int32_t k, const float* out, const void* ws,
+                       size_t ws_bytes, FwdLayout* L) {
+  MOE_TRY(check_desc(d));
+  if (!x || !codes || !scales || !out) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  MOE_TRY(check_tokens(T, k, d));
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return MOE_ERR_ALIGN;
+  MOE_TRY(forward_layout(d, T, k, L));
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+                 const float* router_bias, const void* codes, const void* scales, int32_t T, int32_t k,
+                 float* out, float* logits_out, int32_t* idx_out, float* w_out, void* workspace,
+                 const FwdLayout& L, const float* resid, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  float* w = w_out ? w_out : reinterpret_cast<float*>(ws + L.w);
+  const bool xf = x_dtype == MOE_DTYPE_F32;
+  MOE_TRY(dev(moe::launch_router_logits(x, xf, router_w, router_bias, T, d->hidden, d->n_experts, logits, s)));
+  MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
+  return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a multiple of 32";
+    case MOE_ERR_DTYPE: return "unknown activation dtype";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAYOUT: return "unknown weight layout";
+    case MOE_ERR_UNSUPPORTED: return "request outside what the kernels implement";
+    case MOE_ERR_OVERFLOW: return "a size computation overflows";
+    case MOE_ERR_DEVICE: return "a HIP call or kernel launch failed";
+    case MOE_ERR_ABI: return "descriptor ABI version or size mismatch";
+    case MOE_ERR_RANGE: return "an index argument is out of range";
+    default: return "unknown status";
+  }
+}
+
+int moe_layer_check(const moe_layer_desc* desc) { return check_desc(desc); }
+
+int moe_mxfp4_packed_bytes(const moe_layer_desc* d, size_t* codes_bytes, size_t* scales_bytes) {
+  MOE_TRY(check_desc(d));
+  if (!codes_bytes || !scales_bytes) return MOE_ERR_NULL;
+  size_t cb, sb;
+  MOE_TRY(expert_bytes(d, &cb, &sb));
+  size_t tc, ts;
+  if (!mul_ok(cb, (size_t)d->n_experts, &tc) || !mul_ok(sb, (size_t)d->n_experts, &ts)) return MOE_ERR_OVERFLOW;
+  *codes_bytes = tc;
+  *scales_bytes = ts;
+  return MOE_OK;
+}
+
+int moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
+  MOE_TRY(check_desc(d));
+  if (!bytes) return MOE_ERR_NULL;
+  MOE_TRY(check_tokens(n_tokens, k, d));
+  FwdLayout L;
+  MOE_TRY(forward_layout(d, n_tokens, k, &L));
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_mxfp4_pack(const moe_layer_desc* d, const void* logical_codes, const void* logical_scales,
+                   int64_t expert_begin, int64_t expert_count, void* packed_codes, void* packed_scales,
+                   void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!logical_codes || !logical_scales || !packed_codes || !packed_scales) return MOE_ERR_NULL;
+  if (expert_begin < 0 || expert_count < 0 || expert_begin > d->n_experts ||
+      expert_count > d->n_experts - expert_begin)
+    return MOE_ERR_RANGE;
+  if (!aligned16(logical_codes) || !aligned16(logical_scales) || !aligned16(packed_codes) ||
+      !aligned16(packed_scales))
+    return MOE_ERR_ALIGN;
+  size_t cb, sb;
+  MOE_TRY(expert_bytes(d, &cb, &sb));
+  if (sb % 16) return MOE_ERR_UNSUPPORTED;  // 3*H*I/32 is a multiple of 96 for H, I multiples of 32
+  size_t c0, s0, cn, sn;
+  if (!mul_ok(cb, (size_t)expert_begin, &c0) || !mul_ok(sb, (size_t)expert_begin, &s0) ||
+      !mul_ok(cb, (size_t)expert_count, &cn) || !mul_ok(sb, (size_t)expert_count, &sn))
+    return MOE_ERR_OVERFLOW;
+  hipStream_t s = as_stream(stream);
+  MOE_TRY(dev(moe::launch_copy(logical_codes, static_cast<char*>(packed_codes) + c0, cn, s)));
+  MOE_TRY(dev(moe::launch_copy(logical_scales, static_cast<char*>(packed_scales) + s0, sn, s)));
+  return MOE_OK;
+}
+
+int moe_mxfp4_forward(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+                      const float* router_bias, const void* packed_codes, const void* packed_scales,
+                      int32_t n_tokens, int32_t k, float* out, float* logits_out, int32_t* topk_idx_out,
+                      float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdLayout L;
+  MOE_TRY(check_forward_args(d, x, x_dtype, packed_codes, packed_scales, n_tokens, k, out, workspace,
+                             workspace_bytes, &L));
+  if (!router_w) return MOE_ERR_NULL;
+  if (!aligned16(router_w)) return MOE_ERR_ALIGN;
+  return forward_impl(d, x, x_dtype, router_w, router_bias, packed_codes, packed_scales, n_tokens, k,
+                      out, logits_out, topk_idx_out, topk_w_out, workspace, L, nullptr, as_stream(stream));
+}
+
+int moe_mxfp4_experts(const moe_layer_desc* d, const void* x, int32_t x_dtype, const int32_t* topk_idx,
+                      const float* topk_w, const void* packed_codes, const void* packed_scales,
+                      int32_t n_tokens, int32_t k, float* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  FwdLayout L;
+  MOE_TRY(check_forward_args(d, x, x_dtype, packed_codes, packed_scales, n_tokens, k, out, workspace,
+                             workspace_bytes, &L));
+  if (!topk_idx || !topk_w) return MOE_ERR_NULL;
+  return run_experts(d, x, x_dtype == MOE_DTYPE_F32, topk_idx, topk_w, packed_codes, packed_scales,
+                     n_tokens, k, out, nullptr, static_cast<char*>(workspace), L, as_stream(stream));
+}
+
+int moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, int32_t x_dtype, const int32_t* pair_expert,
+                      int32_t n_pairs, int32_t k, const void* codes, const void* scales, float* h,
+                      void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!x || !pair_expert || !codes || !scales || !h) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (n_pairs < 1 || k < 1 || k > d->top_k_max || n_pairs > kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_gateup_gemv(x, x_dtype == MOE_DTYPE_F32, pair_expert, n_pairs, k,
+                                     static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                                     d->hidden, d->inter, d->n_experts, h, as_stream(stream)));
+}
+
+int moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t* pair_expert, int32_t n_pairs,
+                   const void* codes, const void* scales, float* y, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!h || !pair_expert || !codes || !scales || !y) return MOE_ERR_NULL;
+  if (n_pairs < 1 || n_pairs > kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_down_gemv(h, pair_expert, n_pairs, static_cast<const uint8_t*>(codes),
+                                   static_cast<const uint8_t*>(scales), d->hidden, d->inter, d->n_experts, y,
+                                   as_stream(stream)));
+}
+
+int moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden, const float* resid,
+                float* out, void* stream) {
+  if (!y || !w || !out) return MOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens || k < 1 || k > kMaxTopK || hidden < 4 || hidden % 4)
+    return MOE_ERR_SHAPE;
+  if (!aligned16(y) || !aligned16(out) || (resid && !aligned16(resid))) return MOE_ERR_ALIGN;
+  return dev(moe::launch_combine(y, w, n_tokens, k, hidden, resid, out, as_stream(stream)));
+}
+
+int moe_router_logits(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+                      const float* router_bias, int32_t n_tokens, float* logits, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!x || !router_w || !logits) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (n_tokens < 1 || n_tokens > kMaxTokens) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_router_logits(x, x_dtype == MOE_DTYPE_F32, router_w, router_bias, n_tokens,
+                                       d->hidden, d->n_experts, logits, as_stream(stream)));
+}
+
+int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* idx,
+                     float* w, void* stream) {
+  if (!logits || !idx || !w) return MOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return dev(moe::launch_topk_softmax(logits, n_tokens, n_experts, k, idx, w, as_stream(stream)));
+}
+
+int moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  *bytes = 0;  // the sort keeps its scratch in LDS
+  return MOE_OK;
+}
+
+int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_experts, int32_t k,
+                       int32_t* expert_offsets, int32_t* pair_list, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!topk_idx || !expert_offsets || !pair_list) return MOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)n_tokens * k > INT32_MAX) return MOE_ERR_OVERFLOW;
+  return dev(moe::launch_sort_by_expert(topk_idx, n_tokens, n_experts, k, expert_offsets, pair_list,
+                                        as_stream(stream)));
+}
+
+int moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
+                      int64_t expert, int32_t matrix, float* out, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!packed_codes || !packed_scales || !out) return MOE_ERR_NULL;
+  if (expert < 0 || expert >= d->n_experts || matrix < 0 || matrix > 2) return MOE_ERR_RANGE;
+  if (!aligned16(packed_codes) || !aligned16(packed_scales) || !aligned16(out)) return MOE_ERR_ALIGN;
+  size_t cb, sb;
+  MOE_TRY(expert_bytes(d, &cb, &sb));
+  const size_t mc = cb / 3, ms = sb / 3;
+  const int rows = matrix == 2 ? d->hidden : d->inter;
+  const int cols = matrix == 2 ? d->inter : d->hidden;
+  const uint8_t* c = static_cast<const uint8_t*>(packed_codes) + (size_t)expert * cb + (size_t)matrix * mc;
+  const uint8_t* s = static_cast<const uint8_t*>(packed_scales) + (size_t)expert * sb + (size_t)matrix * ms;
+  return dev(moe::launch_dequant(c, s, rows, cols, out, as_stream(stream)));
+}
+
+int moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden, float* n_out,
+                void* stream) {
+  if (!r || !gamma || !n_out) return MOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens || hidden < 4 || hidden % 4) return MOE_ERR_SHAPE;
+  if (!aligned16(r) || !aligned16(gamma) || !aligned16(n_out)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_rmsnorm(r, gamma, eps, n_tokens, hidden, n_out, as_stream(stream)));
+}
+
+int moe_residual_add(float* r, const float* dlt, int64_t n, void* stream) {
+  if (!r || !dlt) return MOE_ERR_NULL;
+  if (n < 0) return MOE_ERR_SHAPE;
+  return dev(moe::launch_residual_add(r, dlt, (size_t)n, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- stack (A10)
+
+static int stack_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L, size_t* nbuf_off,
+                        size_t* total) {
+  MOE_TRY(forward_layout(d, T, k, L));
+  size_t nb;
+  if (!mul_ok((size_t)T * (size_t)d->hidden, 4, &nb)) return MOE_ERR_OVERFLOW;
+  size_t a = (L->total + 255) & ~size_t(255);
+  size_t t;
+  if (!add_ok(a, nb, &t)) return MOE_ERR_OVERFLOW;
+  *nbuf_off = a;
+  *total = t;
+  return MOE_OK;
+}
+
+int moe_stack_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
+  MOE_TRY(check_desc(d));
+  if (!bytes) return MOE_ERR_NULL;
+  MOE_TRY(check_tokens(n_tokens, k, d));
+  FwdLayout L;
+  size_t nb_off, total;
+  MOE_TRY(stack_layout(d, n_tokens, k, &L, &nb_off, &total));
+  *bytes = total;
+  return MOE_OK;
+}
+
+static int stack_check(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+                       const void* const* scales, const float* const* router_w, const float* const* gamma,
+                       const void* x, int32_t x_dtype, int32_t T, int32_t k, const float* residual,
+                       const void* ws, size_t ws_bytes, FwdLayout* L, size_t* nb_off) {
+  MOE_TRY(check_desc(d));
+  if (n_layers < 1 || n_layers > 4096) return MOE_ERR_SHAPE;
+  if (!codes || !scales || !router_w || !gamma || !x || !residual) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  MOE_TRY(check_tokens(T, k, d));
+  for (int l = 0; l < n_layers; ++l) {
+    if (!codes[l] || !scales[l] || !router_w[l] || !gamma[l]) return MOE_ERR_NULL;
+    if (!aligned16(codes[l]) || !aligned16(scales[l]) || !aligned16(router_w[l]) || !aligned16(gamma[l]))
+      return MOE_ERR_ALIGN;
+  }
+  if (!aligned16(x) || !aligned16(residual)) return MOE_ERR_ALIGN;
+  size_t total;
+  MOE_TRY(stack_layout(d, T, k, L, nb_off, &total));
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static int stack_enqueue(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+                         const void* const* scales, const float* const* router_w,
+                         const float* const* router_bias, const float* const* gamma, float eps,
+                         const void* x, int32_t x_dtype, int32_t T, int32_t k, float* residual, void* ws,
+                         const FwdLayout& L, size_t nb_off, hipStream_t s) {
+  const size_t n = (size_t)T * d->hidden;
+  float* nbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + nb_off);
+  MOE_TRY(dev(moe::launch_widen(x, x_dtype == MOE_DTYPE_F32, n, residual, s)));
+  for (int l = 0; l < n_layers; ++l) {
+    MOE_TRY(dev(moe::launch_rmsnorm(residual, gamma[l], eps, T, d->hidden, nbuf, s)));
+    const float* b = router_bias ? router_bias[l] : nullptr;
+    MOE_TRY(forward_impl(d, nbuf, MOE_DTYPE_F32, router_w[l], b, codes[l], scales[l], T, k, residual,
+                         nullptr, nullptr, nullptr, ws, L, residual, s));
+  }
+  return MOE_OK;
+}
+
+int moe_mxfp4_stack_forward(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+                            const void* const* scales, const float* const* router_w,
+                            const float* const* router_bias, const float* const* gamma, float eps,
+                            const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k, float* residual,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  FwdLayout L;
+  size_t nb_off;
+  MOE_TRY(stack_check(d, n_layers, codes, scales, router_w, gamma, x, x_dtype, n_tokens, k, residual,
+                      workspace, workspace_bytes, &L, &nb_off));
+  return stack_enqueue(d, n_layers, codes, scales, router_w, router_bias, gamma, eps, x, x_dtype, n_tokens,
+                       k, residual, workspace, L, nb_off, as_stream(stream));
+}
+
+struct moe_stack_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+int moe_stack_graph_create(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+                           const void* const* scales, const float* const* router_w,
+                           const float* const* router_bias, const float* const* gamma, float eps,
+                           const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k, float* residual,
+                           void* workspace, size_t workspace_bytes, void* stream, moe_stack_graph** out) {
+  if (!out) return MOE_ERR_NULL;
+  *out = nullptr;
+  FwdLayout L;
+  size_t nb_off;
+  MOE_TRY(stack_check(d, n_layers, codes, scales, router_w, gamma, x, x_dtype, n_tokens, k, residual,
+                      workspace, workspace_bytes, &L, &nb_off));
+  // Capture on a private non-blocking stream (default priority) so the
+  // caller's stream, which may be the null stream, is never in capture mode.
+  hipStream_t cap = nullptr;
+  if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_DEVICE;
+  int rc = MOE_OK;
+  hipGraph_t g = nullptr;
+  if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cap);
+    return MOE_ERR_DEVICE;
+  }
+  rc = stack_enqueue(d, n_layers, codes, scales, router_w, router_bias, gamma, eps, x, x_dtype, n_tokens, k,
+                     residual, workspace, L, nb_off, cap);
+  hipError_t ec = hipStreamEndCapture(cap, &g);
+  (void)hipStreamDestroy(cap);
+  if (rc != MOE_OK || ec != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc != MOE_OK ? rc : MOE_ERR_DEVICE;
+  }
+  hipGraphExec_t ex = nullptr;
+  if (hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return MOE_ERR_DEVICE;
+  }
+  moe_stack_graph* h = new (std::nothrow) moe_stack_graph;
+  if (!h) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return MOE_ERR_DEVICE;
+  }
+  h->graph = g;
+  h->exec = ex;
+  (void)stream;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_stack_graph_launch(moe_stack_graph* g, void* stream) {
+  if (!g) return MOE_ERR_NULL;
+  return dev(hipGraphLaunch(g->exec, as_stream(stream)));
+}
+
+int moe_stack_graph_destroy(moe_stack_graph* g) {
+  if (!g) return MOE_OK;
+  int rc = MOE_OK;
+  if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = MOE_ERR_DEVICE;
+  if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = MOE_ERR_DEVICE;
+  delete g;
+  return rc;
+}
+
+}  // extern "C"

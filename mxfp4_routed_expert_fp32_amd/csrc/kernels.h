@@ -1,0 +1,34 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe_mxfp4).
+// Shapes are validated by the C ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router_logits(const void* x, bool x_f32, const float* wr, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s);
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               hipStream_t s);
+hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets,
+                                 int32_t* pairs, hipStream_t s);
+
+hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
+                              const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                              float* hbuf, hipStream_t s);
+hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
+                            const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s);
+hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,
+                          float* out, hipStream_t s);
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
+                          hipStream_t s);
+hipError_t launch_rmsnorm(const float* r, const float* gamma, float eps, int T, int H, float* out,
+                          hipStream_t s);
+hipError_t launch_residual_add(float* r, const float* d, size_t n, hipStream_t s);
+hipError_t launch_widen(const void* x, bool x_f32, size_t n, float* out, hipStream_t s);
+
+}  // namespace moe

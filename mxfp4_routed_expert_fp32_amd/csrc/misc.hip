@@ -1,0 +1,132 @@
+// Weight pack (device layout copy), dequant export, RMSNorm and residual add.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- pack
+// The device layout equals the logical row-major layout, so packing a run of
+// experts is a 16-byte-vector copy into their place in the layer buffers.
+__global__ __launch_bounds__(256) void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  k_copy16<<<dim3((unsigned)blocks), 256, 0, s>>>(static_cast<const uint4*>(src),
+                                                  static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dequant export
+// Each thread decodes 8 elements (one 32-bit word of codes) with the same
+// hardware conversion the expert kernels use.  A NaN scale gives the canonical
+// quiet NaN 0x7FC00000 (the conversion itself sets the sign bit).
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales, int rows, int cols,
+                                                 float* __restrict__ out) {
+  const size_t words = (size_t)rows * cols / 8;
+  const int wpr = cols / 8;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < words; q += (size_t)gridDim.x * 256) {
+    const size_t n = q / wpr;
+    const int c8 = (int)(q % wpr);
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[q];
+    const uint32_t sbyte = scales[n * (cols / 32) + (c8 * 8) / 32];
+    float v[8];
+    if (sbyte == 0xFFu) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(0x7FC00000u);
+    } else {
+      const float s = e8m0_operand(sbyte);
+      f32x2 a = fp4x2_to_f32<0>(w, s), b = fp4x2_to_f32<1>(w, s);
+      f32x2 c = fp4x2_to_f32<2>(w, s), d = fp4x2_to_f32<3>(w, s);
+      v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y; v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
+    }
+    float4* o = reinterpret_cast<float4*>(out + n * cols + (size_t)c8 * 8);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
+                          hipStream_t s) {
+  const size_t words = (size_t)rows * cols / 8;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  k_dequant<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One workgroup per token: ss = sum r^2 (fixed-order block reduction),
+// n = (r * (1 / sqrt(ss / H + eps))) * gamma.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ r,
+                                                 const float* __restrict__ gamma, float eps, int H,
+                                                 float* __restrict__ out) {
+  const int t = blockIdx.x;
+  const float4* rt = reinterpret_cast<const float4*>(r + (size_t)t * H);
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    float4 v = rt[c];
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  __shared__ float red[4];
+  ss = group_sum<kWave>(ss);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  float4* ot = reinterpret_cast<float4*>(out + (size_t)t * H);
+  const float4* g = reinterpret_cast<const float4*>(gamma);
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    float4 v = rt[c], gg = g[c];
+    ot[c] = make_float4((v.x * inv) * gg.x, (v.y * inv) * gg.y, (v.z * inv) * gg.z, (v.w * inv) * gg.w);
+  }
+}
+
+hipError_t launch_rmsnorm(const float* r, const float* gamma, float eps, int T, int H, float* out,
+                          hipStream_t s) {
+  k_rmsnorm<<<dim3(T), 256, 0, s>>>(r, gamma, eps, H, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- residual / widen
+__global__ __launch_bounds__(256) void k_residual_add(float* __restrict__ r, const float* __restrict__ d,
+                                                      size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    r[i] = r[i] + d[i];
+}
+
+hipError_t launch_residual_add(float* r, const float* d, size_t n, hipStream_t s) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return hipSuccess;
+  k_residual_add<<<dim3((unsigned)blocks), 256, 0, s>>>(r, d, n);
+  return hipGetLastError();
+}
+
+// x (fp32 or bf16) -> fp32 copy.
+__global__ __launch_bounds__(256) void k_widen(const void* __restrict__ x, bool x_f32, size_t n,
+                                               float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    out[i] = x_f32 ? static_cast<const float*>(x)[i]
+                   : bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+}
+
+hipError_t launch_widen(const void* x, bool x_f32, size_t n, float* out, hipStream_t s) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return hipSuccess;
+  k_widen<<<dim3((unsigned)blocks), 256, 0, s>>>(x, x_f32, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,247 @@
+// Router logits (fp32), exact top-k with softmax over the selected logits, and
+// the stable token -> expert counting sort.
+//
+// Router: fp32 logits with fp32 accumulation and no reduced-precision products
+// ("Tarfa EXACTNESS" page, opening list).  Selection keeps all k experts in
+// route order ("Deltafin's custom compiled runtime", sections "Complete target
+// sequence tape" and "Weight fidelity").
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- router logits
+// One workgroup per (expert row, tile of TT tokens).  Each thread streams a
+// strided set of float4s of the router row and FMAs them with the same columns
+// of up to TT tokens; the block reduction order is fixed.
+template <bool XF32, int TT>
+__global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ x,
+                                                       const float* __restrict__ wr,
+                                                       const float* __restrict__ bias, int T, int H,
+                                                       int E, float* __restrict__ logits) {
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * TT;
+  const float4* wrow = reinterpret_cast<const float4*>(wr + (size_t)e * H);
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+  const int n4 = H / 4;
+  for (int c = threadIdx.x; c < n4; c += 256) {
+    float4 w = wrow[c];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t0 + t < T) {
+        float4 xv;
+        if constexpr (XF32) {
+          xv = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)(t0 + t) * H)[c];
+        } else {
+          uint2 b = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + t) * H)[c];
+          xv = make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
+                           bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
+        }
+        acc[t] = fmaf(w.x, xv.x, acc[t]);
+        acc[t] = fmaf(w.y, xv.y, acc[t]);
+        acc[t] = fmaf(w.z, xv.z, acc[t]);
+        acc[t] = fmaf(w.w, xv.w, acc[t]);
+      }
+    }
+  }
+  __shared__ float red[TT][4];
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float v = group_sum<kWave>(acc[t]);
+    if (lane == 0) red[t][wid] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < TT && t0 + (int)threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float v = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
+    if (bias) v += bias[e];
+    logits[(size_t)(t0 + t) * E + e] = v;
+  }
+}
+
+// ---------------------------------------------------------------- top-k + softmax
+// Rank key of a logit: larger key = earlier in route order.  Higher value
+// first; -0 and +0 are equal; NaN is below every number (-inf included); equal
+// values go to the lower expert id.  Key 0 is never a valid key.
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t ord;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+    ord = 0;                                  // NaN
+  } else {
+    if ((u << 1) == 0) u = 0;                 // -0 -> +0
+    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)ord << 32) | (uint32_t)(~e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wavefront per token; each lane owns experts lane + 64*v, v < MAXV.
+template <int MAXV>
+__global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E,
+                                                      int k, int32_t* __restrict__ idx,
+                                                      float* __restrict__ wout) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  uint64_t key[MAXV];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    int e = lane + kWave * v;
+    key[v] = (e < E) ? rank_key(l[e], (uint32_t)e) : 0ull;
+  }
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) best = key[v] > best ? key[v] : best;
+    uint64_t win = wave_max_u64(best);
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v)
+      if (key[v] == win) key[v] = 0;          // keys are unique: only the owner matches
+    if (lane == j) my_idx = (int)(~(uint32_t)win);
+  }
+  // softmax over the selected logits, in rank order
+  float lj = (lane < k) ? l[my_idx] : 0.0f;
+  float m = __shfl(lj, 0, kWave);
+  float ex = (lane < k) ? expf(lj - m) : 0.0f;
+  float s = group_sum<kWave>(ex);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_idx;
+    wout[(size_t)t * k + lane] = ex / s;
+  }
+}
+
+// ---------------------------------------------------------------- counting sort
+// Stable sort of the T*k (token, rank) pairs by expert, in one workgroup:
+// histogram -> exclusive scan -> scatter.  Within an expert the pairs are in
+// token order: each token selects an expert at most once, so a pair's place
+// is the number of earlier tokens that selected the same expert.  Tokens are
+// taken 64 at a time; a 64-bit mask per expert records which tokens of the
+// chunk selected it, and a popcount below the token's bit gives its place.
+constexpr int kSortThreads = 1024;
+
+// running[E] and mask[E] live in LDS (E <= 4096: 48 KB).
+__global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* __restrict__ idx,
+                                                                 int T, int E, int k,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ pairs) {
+  extern __shared__ unsigned long long sort_lds[];
+  unsigned long long* mask = sort_lds;                               // [E]
+  int32_t* running = reinterpret_cast<int32_t*>(sort_lds + E);       // [E]
+  __shared__ int32_t part[kSortThreads];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) { running[e] = 0; mask[e] = 0ull; }
+  __syncthreads();
+  const int P = T * k;
+  for (int p = tid; p < P; p += kSortThreads) {
+    int e = idx[p];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    atomicAdd(&running[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the counts: each thread owns `per` consecutive experts
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  const int e0 = tid * per;
+  int32_t local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) local += running[e];
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kSortThreads; off <<= 1) {
+    int32_t v = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t base = part[tid] - local;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    int32_t c = running[e];
+    offsets[e] = base;
+    running[e] = base;
+    base += c;
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+  for (int c0 = 0; c0 < T; c0 += 64) {
+    const int np = min(64, T - c0) * k;
+    const int32_t* ic = idx + (size_t)c0 * k;
+    for (int p = tid; p < np; p += kSortThreads) {
+      int e = ic[p];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      atomicOr(&mask[e], 1ull << (p / k));
+    }
+    __syncthreads();
+    for (int p = tid; p < np; p += kSortThreads) {
+      int e = ic[p];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      const int tl = p / k;
+      const unsigned long long m = mask[e];
+      const unsigned long long below = m & ((1ull << tl) - 1ull);
+      pairs[running[e] + __popcll(below)] = c0 * k + p;
+    }
+    __syncthreads();
+    // the pair of the lowest token of each expert advances that expert's cursor
+    for (int p = tid; p < np; p += kSortThreads) {
+      int e = ic[p];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      const int tl = p / k;
+      const unsigned long long m = mask[e];
+      if ((m & ((1ull << tl) - 1ull)) == 0ull) running[e] += __popcll(m);
+    }
+    __syncthreads();
+    for (int p = tid; p < np; p += kSortThreads) {
+      int e = ic[p];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      mask[e] = 0ull;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_router_logits(const void* x, bool x_f32, const float* wr, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s) {
+  constexpr int TT = 4;
+  dim3 grid(E, (T + TT - 1) / TT);
+  if (x_f32)
+    k_router_logits<true, TT><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
+  else
+    k_router_logits<false, TT><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               hipStream_t s) {
+  dim3 grid((T + 3) / 4);
+  if (E <= 64 * 4)
+    k_topk_softmax<4><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  else if (E <= 64 * 16)
+    k_topk_softmax<16><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  else
+    k_topk_softmax<64><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets,
+                                 int32_t* pairs, hipStream_t s) {
+  size_t lds = (size_t)E * (sizeof(unsigned long long) + sizeof(int32_t));
+  k_sort_by_expert<<<1, kSortThreads, lds, s>>>(idx, T, E, k, offsets, pairs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moe_mxfp4.h declares, and rejects invalid arguments
+before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mxfp4_routed_expert_fp32_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe_mxfp4.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(moe_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_abi_version_and_strings():
+    L = moe.lib()
+    assert L.moe_abi_version() == moe.MOE_ABI_VERSION
+    for code in moe.STATUS:
+        assert L.moe_status_string(code)
+    assert L.moe_status_string(12345) == b"unknown status"
+
+
+def D(**kw):
+    base = dict(hidden=7168, inter=1536, n_experts=896, top_k_max=16)
+    base.update(kw)
+    return moe.LayerDesc.make(**base)
+
+
+def rc_check(desc):
+    return moe.lib().moe_layer_check(ctypes.byref(desc) if desc is not None else None)
+
+
+def test_descriptor_validation():
+    assert rc_check(D()) == 0
+    assert rc_check(None) == -1
+    d = D(); d.abi_version = 2
+    assert rc_check(d) == -10
+    d = D(); d.struct_size = 16
+    assert rc_check(d) == -10
+    d = D(); d.layout = 7
+    assert rc_check(d) == -6
+    assert rc_check(D(hidden=7000)) == -2
+    assert rc_check(D(inter=100)) == -2
+    assert rc_check(D(top_k_max=0)) == -2
+    assert rc_check(D(top_k_max=65, n_experts=896)) == -2
+    assert rc_check(D(n_experts=8, top_k_max=9)) == -2
+    assert rc_check(D(hidden=16384)) == -7
+    assert rc_check(D(n_experts=5000)) == -7
+
+
+def test_sizes():
+    c, s = moe.packed_bytes(D())
+    assert c == 896 * 3 * 7168 * 1536 // 2 and s == 896 * 3 * 7168 * 1536 // 32
+    assert c + s == 896 * 17547264
+    ws1 = moe.workspace_bytes(D(), 1, 16)
+    ws64 = moe.workspace_bytes(D(), 64, 16)
+    assert 0 < ws1 < ws64
+    with pytest.raises(moe.MoeError) as e:
+        moe.workspace_bytes(D(), 0, 16)
+    assert e.value.status == -2
+    with pytest.raises(moe.MoeError) as e:
+        moe.workspace_bytes(D(), 1, 17)
+    assert e.value.status == -2
+
+
+def call_forward(desc, x=16, wr=16, codes=16, scales=16, T=1, k=2, out=16, ws=16, ws_bytes=1 << 30,
+                 dtype=1):
+    return moe.lib().moe_mxfp4_forward(ctypes.byref(desc), x, dtype, wr, None, codes, scales, T, k, out,
+                                       None, None, None, ws, ws_bytes, None)
+
+
+def test_forward_rejects_before_launch():
+    d = D()
+    assert call_forward(d, x=None) == -1
+    assert call_forward(d, codes=None) == -1
+    assert call_forward(d, wr=None) == -1
+    assert call_forward(d, dtype=5) == -3
+    assert call_forward(d, T=0) == -2
+    assert call_forward(d, k=0) == -2
+    assert call_forward(d, k=17) == -2
+    assert call_forward(d, x=8) == -4
+    assert call_forward(d, out=24) == -4
+    assert call_forward(d, ws=None) == -5
+    assert call_forward(d, ws_bytes=100) == -5
+    bad = D(); bad.abi_version = 9
+    assert call_forward(bad) == -10
+
+
+def test_other_entry_points_reject_before_launch():
+    L = moe.lib()
+    d = D()
+    assert L.moe_mxfp4_pack(ctypes.byref(d), 16, 16, 0, 897, 16, 16, None) == -11
+    assert L.moe_mxfp4_pack(ctypes.byref(d), 16, 16, -1, 1, 16, 16, None) == -11
+    assert L.moe_mxfp4_pack(ctypes.byref(d), 8, 16, 0, 1, 16, 16, None) == -4
+    assert L.moe_mxfp4_dequant(ctypes.byref(d), 16, 16, 896, 0, 16, None) == -11
+    assert L.moe_mxfp4_dequant(ctypes.byref(d), 16, 16, 0, 3, 16, None) == -11
+    assert L.moe_topk_softmax(16, 1, 896, 65, 16, 16, None) == -2
+    assert L.moe_topk_softmax(16, 1, 8, 9, 16, 16, None) == -2
+    assert L.moe_topk_softmax(16, 1, 5000, 4, 16, 16, None) == -7
+    assert L.moe_topk_softmax(None, 1, 8, 2, 16, 16, None) == -1
+    assert L.moe_sort_by_expert(16, 0, 8, 2, 16, 16, None, 0, None) == -2
+    assert L.moe_rmsnorm(16, 16, ctypes.c_float(1e-6), 1, 7, 16, None) == -2
+    assert L.moe_residual_add(16, None, 4, None) == -1
+    g = ctypes.c_void_p()
+    assert L.moe_stack_graph_create(ctypes.byref(d), 0, 16, 16, 16, None, 16, ctypes.c_float(1e-6), 16, 1,
+                                    1, 16, 16, 16, 1 << 30, None, ctypes.byref(g)) == -2
+    assert L.moe_stack_graph_destroy(None) == 0
