@@ -10,7 +10,7 @@
 
 #include <new>
 
-#include "../../include/moe_mxfp4.h"
+#include "moe_mxfp4.h"
 #include "kernels.h"
 
 namespace {

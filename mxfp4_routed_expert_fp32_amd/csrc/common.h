@@ -69,3 +69,43 @@ __device__ __forceinline__ uint4 load_u4_stream(const uint8_t* p) {
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
 }  // namespace moe
+
+namespace moe {
+
+// DPP lane permutations (GFX9 encodings): quad_perm, row mirrors, row
+// broadcasts.  update_dpp with old = 0 leaves lanes of disabled rows at 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Every lane of each 16-lane row receives the row's sum (fixed order).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Sum over groups of G = 4, 8 or 16 consecutive lanes, every lane of a group
+// receiving its group's sum.
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(G == 4 || G == 8 || G == 16, "group size");
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  if constexpr (G >= 8) v += dpp_f<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+
+// Full-wavefront sum, returned in every lane (uniform).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+}  // namespace moe

@@ -1,21 +1,59 @@
-// Decode-form expert kernels (one token): HBM-streaming MXFP4 GEMVs that decode
-// the 4-bit codes in registers, plus the rank-ordered combine.
+// Decode-form expert kernels: HBM-streaming MXFP4 GEMVs that decode the 4-bit
+// codes in registers, plus the rank-ordered combine.
 //
 // The fused dequant + GEMV follows brain.bigb.es "deltafin", section "The
-// techniques that bought the 82x" (table decode of E2M1, E8M0 scale applied to
-// the fp32 exponent, one pass over the weights).  Here the decode is the
-// gfx950 scaled FP4 conversion, which yields exactly E2M1(code) * 2^(S-127).
+// techniques that bought the 82x" (E2M1 decode through a 16-entry table, E8M0
+// scale applied to the fp32 exponent, one pass over the weights).  Here the
+// decode is the gfx950 scaled FP4 conversion, which yields exactly
+// E2M1(code) * 2^(S-127) (checked bit for bit by the dequant export tests).
 //
 // Weight layout (row-major, per expert gate | up | down): a row of a
-// [rows][K] matrix is K/2 code bytes followed, in the scale buffer, by K/32
-// scale bytes.  Lane l of a wave owns the 32-element blocks b = c + LPR*m of
-// its row (c = l % LPR), so every load instruction of a wave reads LPR
-// consecutive 16-byte blocks of each of 64/LPR rows, and the lane's slice of
-// the activation vector stays in registers for all rows the wave streams.
+// [rows][K] matrix is K/2 code bytes, plus K/32 scale bytes in the scale
+// buffer.  Lane l of a wave owns the 32-element blocks b = c + LPR*m of its row
+// (c = l % LPR, m < NBL), so each 16-byte load instruction of a wave reads LPR
+// consecutive blocks of each of 64/LPR rows, and the lane's slice of the
+// activation vector stays in registers for every row the wave streams.
+//
+// Work split: a workgroup (4 waves) owns one (token, rank) pair and a share of
+// its rows; the grid is sized to the number of workgroups the GPU holds at
+// once (occupancy x CUs), so every workgroup runs once and there is no tail.
+// Rows are interleaved across the pair's waves, so at any moment the waves of
+// a pair stream neighbouring rows.  Weight loads run ahead of the compute
+// (two rows for gate/up, three row groups for down).
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+// Workgroups of `fn` (256 threads, `lds` bytes of LDS) the current device holds
+// at once.  Queried once per (kernel, LDS size, device) and remembered.
+static int resident_wgs_query(const void* fn, size_t lds) {
+  struct Entry { const void* fn; size_t lds; int dev; int value; };
+  static std::mutex mu;
+  static std::vector<Entry> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry& e : table)
+      if (e.fn == fn && e.lds == lds && e.dev == dev) return e.value;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int v = cus * per_cu;
+  std::lock_guard<std::mutex> g(mu);
+  table.push_back(Entry{fn, lds, dev, v});
+  return v;
+}
+
+template <typename F>
+static int resident_wgs(F fn, size_t lds) {
+  return resident_wgs_query(reinterpret_cast<const void*>(fn), lds);
+}
 
 // 32 products of one block: codes q (16 bytes = 32 nibbles), scale operand s,
 // activations as 16 bf16 pairs.  Weights are exact bf16, products exact fp32.
@@ -68,162 +106,247 @@ __device__ __forceinline__ float block_dot_f32(uint4 q, float s, const uint32_t*
   return acc;
 }
 
-// ---------------------------------------------------------------- gate/up + SwiGLU
-// Grid: P (token, rank) pairs x `tiles` row tiles; 4 waves per workgroup, RPW
-// rows of gate and up per wave.  Lanes: LPR = 64 (one row at a time, 64 blocks
-// per load).  Output hbuf[p][i] = silu(g_i) * u_i for pair p = t*k + j.
-constexpr int kGU_RPW = 4;
-constexpr int kGU_ROWS = 4 * kGU_RPW;
+// One row's worth of a lane's blocks: NBL 16-byte code blocks + scale bytes.
+template <int NBL>
+struct RowBlocks {
+  uint4 q[NBL];
+  uint32_t s[NBL];
+};
 
+// Loads blocks b = c + LPR*m of one row; blocks past the row end are zero
+// (zero codes times zero activations add nothing) and are never read.
+template <int LPR, int NBL>
+__device__ __forceinline__ void load_row(RowBlocks<NBL>& r, const uint8_t* row_codes,
+                                         const uint8_t* row_scales, int c, int nb) {
+#pragma unroll
+  for (int m = 0; m < NBL; ++m) {
+    const int b = c + LPR * m;
+    if (b < nb) {
+      r.q[m] = load_u4_stream(row_codes + 16 * b);
+      r.s[m] = row_scales[b];
+    } else {
+      r.q[m] = make_uint4(0u, 0u, 0u, 0u);
+      r.s[m] = 0u;
+    }
+  }
+}
+
+template <bool XF32, int NBL>
+__device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t (*xr)[XF32 ? 32 : 16]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NBL; ++m) {
+    const float s = e8m0_operand(r.s[m]);
+    if constexpr (XF32)
+      acc = block_dot_f32(r.q[m], s, xr[m], acc);
+    else
+      acc = block_dot_bf16(r.q[m], s, xr[m], acc);
+  }
+  return acc;
+}
+
+// Sum over LPR-lane groups; valid at least in the last lane of each group.
+template <int LPR>
+__device__ __forceinline__ float group_reduce(float v) {
+  if constexpr (LPR <= 16) {
+    return lane_group_sum<LPR>(v);
+  } else if constexpr (LPR == 32) {
+    v = row16_sum(v);
+    return v + dpp_f<0x142, 0xA>(v);
+  } else {
+    v = row16_sum(v);
+    v += dpp_f<0x142, 0xA>(v);
+    return v + dpp_f<0x143, 0xC>(v);
+  }
+}
+
+// ---------------------------------------------------------------- gate/up + SwiGLU
+// Workgroup (pair p, part): wave w takes rows part*4 + w, + 4*parts, ... of
+// the gate and up matrices of expert route[p], LPR = 64 (one row per step),
+// the next row loaded while the current one is computed.
+// hbuf[p][i] = silu(g_i) * u_i, pair p = t*k + j uses token t = p / k.
 template <bool XF32, int NBL>
 __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
                                                      const int32_t* __restrict__ route,
                                                      const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales, int H, int I,
-                                                     int E, int k, int tiles, float* __restrict__ hbuf) {
+                                                     int E, int k, int parts, int rpw,
+                                                     float* __restrict__ hbuf) {
   extern __shared__ uint4 xs_lds[];
-  const int j = blockIdx.x / tiles;     // pair (token j / k, rank j % k)
-  const int tile = blockIdx.x % tiles;
-  int e = route[j];
+  constexpr int XW = XF32 ? 32 : 16;  // registers per block of activations
+  const int p = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  int e = route[p];
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nb = H / 32;
-  const int xbytes = XF32 ? H * 4 : H * 2;
-  const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (size_t)(j / k) * xbytes);
-  for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
-  __syncthreads();
-
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  constexpr int XW = XF32 ? 32 : 16;  // registers per block of activations
-  uint32_t xr[NBL][XW];
-#pragma unroll
-  for (int m = 0; m < NBL; ++m) {
-    const int b = lane + kWave * m;
-    if (b < nb) {
-      const uint4* src = xs_lds + b * (XW / 4);
-#pragma unroll
-      for (int v = 0; v < XW / 4; ++v) {
-        uint4 u = src[v];
-        xr[m][4 * v] = u.x; xr[m][4 * v + 1] = u.y; xr[m][4 * v + 2] = u.z; xr[m][4 * v + 3] = u.w;
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < XW; ++v) xr[m][v] = 0u;
-    }
-  }
-
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint8_t* gcod = codes + (size_t)e * cb;
   const uint8_t* ucod = gcod + (size_t)I * H / 2;
   const uint8_t* gsc = scales + (size_t)e * sb;
   const uint8_t* usc = gsc + (size_t)I * H / 32;
   const int rb = H / 2, rs = H / 32;
-  const int i0 = tile * kGU_ROWS + wid * kGU_RPW;
+  // rows interleaved across the pair's waves: step r of wave (part, wid)
+  // takes row r*parts*4 + part*4 + wid, so the pair's waves stream
+  // neighbouring rows at any moment
+  const int i_begin = part * 4 + wid;
+  const int i_step = parts * 4;
+  const int i_end = I;
+
+  RowBlocks<NBL> g0, u0, g1, u1;
+  if (i_begin < i_end) {
+    load_row<kWave, NBL>(g0, gcod + (size_t)i_begin * rb, gsc + (size_t)i_begin * rs, lane, nb);
+    load_row<kWave, NBL>(u0, ucod + (size_t)i_begin * rb, usc + (size_t)i_begin * rs, lane, nb);
+  }
+
+  // stage this token's activations, then keep the lane's blocks in registers
+  const int xbytes = XF32 ? H * 4 : H * 2;
+  const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (size_t)(p / k) * xbytes);
+  for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
+  __syncthreads();
+  uint32_t xr[NBL][XW];
 #pragma unroll
-  for (int r = 0; r < kGU_RPW; ++r) {
-    const int i = i0 + r;
-    if (i >= I) break;
-    float ag = 0.0f, au = 0.0f;
+  for (int m = 0; m < NBL; ++m) {
+    const int b = lane + kWave * m;
 #pragma unroll
-    for (int m = 0; m < NBL; ++m) {
-      const int b = lane + kWave * m;
-      if (b < nb) {
-        const uint4 qg = load_u4_stream(gcod + (size_t)i * rb + 16 * b);
-        const uint4 qu = load_u4_stream(ucod + (size_t)i * rb + 16 * b);
-        const float sg = e8m0_operand(gsc[(size_t)i * rs + b]);
-        const float su = e8m0_operand(usc[(size_t)i * rs + b]);
-        if constexpr (XF32) {
-          ag = block_dot_f32(qg, sg, xr[m], ag);
-          au = block_dot_f32(qu, su, xr[m], au);
-        } else {
-          ag = block_dot_bf16(qg, sg, xr[m], ag);
-          au = block_dot_bf16(qu, su, xr[m], au);
-        }
-      }
+    for (int v = 0; v < XW / 4; ++v) {
+      uint4 u = (b < nb) ? xs_lds[b * (XW / 4) + v] : make_uint4(0u, 0u, 0u, 0u);
+      xr[m][4 * v] = u.x; xr[m][4 * v + 1] = u.y; xr[m][4 * v + 2] = u.z; xr[m][4 * v + 3] = u.w;
     }
-    ag = group_sum<kWave>(ag);
-    au = group_sum<kWave>(au);
-    if (lane == 0) hbuf[(size_t)j * I + i] = silu_mul(ag, au);
+  }
+
+  for (int i = i_begin; i < i_end; i += 2 * i_step) {
+    const int i1 = i + i_step, i2 = i + 2 * i_step;
+    const bool has1 = i1 < i_end;
+    if (has1) {
+      load_row<kWave, NBL>(g1, gcod + (size_t)i1 * rb, gsc + (size_t)i1 * rs, lane, nb);
+      load_row<kWave, NBL>(u1, ucod + (size_t)i1 * rb, usc + (size_t)i1 * rs, lane, nb);
+    }
+    float ag = wave_sum(row_dot<XF32, NBL>(g0, xr));
+    float au = wave_sum(row_dot<XF32, NBL>(u0, xr));
+    if (lane == 0) hbuf[(size_t)p * I + i] = silu_mul(ag, au);
+    if (!has1) break;
+    if (i2 < i_end) {
+      load_row<kWave, NBL>(g0, gcod + (size_t)i2 * rb, gsc + (size_t)i2 * rs, lane, nb);
+      load_row<kWave, NBL>(u0, ucod + (size_t)i2 * rb, usc + (size_t)i2 * rs, lane, nb);
+    }
+    ag = wave_sum(row_dot<XF32, NBL>(g1, xr));
+    au = wave_sum(row_dot<XF32, NBL>(u1, xr));
+    if (lane == 0) hbuf[(size_t)p * I + i1] = silu_mul(ag, au);
   }
 }
 
 // ---------------------------------------------------------------- down
-// Grid: P pairs x `tiles` row tiles of Wd [H][I]; the pair's h row is staged in
-// LDS and each lane keeps its NBL2 blocks of it in registers.  LPR lanes per
-// row, 64/LPR rows per load step, kDN_STEPS steps per wave.
-constexpr int kDN_STEPS = 4;
-
+// Workgroup (pair p, part): rows of Wd [H][I] of expert pair_expert[p]; LPR
+// lanes per row, RPS = 64/LPR rows per step, `steps` steps per wave, row
+// groups interleaved across the pair's waves, weights loaded three steps
+// ahead from a ring of four.  The pair's h row is staged in LDS and each lane
+// keeps its NBL2 blocks in registers.
 template <int LPR, int NBL2>
 __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbuf,
                                                    const int32_t* __restrict__ pair_expert,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales, int H, int I,
-                                                   int E, int tiles, float* __restrict__ ybuf) {
+                                                   int E, int parts, int steps, float* __restrict__ ybuf) {
   extern __shared__ float hs_lds[];
   constexpr int RPS = kWave / LPR;
-  constexpr int ROWS_W = RPS * kDN_STEPS;
-  constexpr int ROWS_G = 4 * ROWS_W;
-  const int j = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
-  int e = pair_expert[j];
-  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-  const float4* hsrc = reinterpret_cast<const float4*>(hbuf + (size_t)j * I);
-  for (int c = threadIdx.x; c < I / 4; c += 256) reinterpret_cast<float4*>(hs_lds)[c] = hsrc[c];
-  __syncthreads();
-
+  const int p = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int c = lane % LPR, rsub = lane / LPR;
+  int e = pair_expert[p];
+  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nbk = I / 32;
+  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
+  const uint8_t* dcod = codes + (size_t)e * cb + (size_t)I * H;
+  const uint8_t* dsc = scales + (size_t)e * sb + (size_t)2 * I * H / 32;
+  const int rb = I / 2, rs = I / 32;
+  // row groups interleaved across the pair's waves (see k_gateup_gemv)
+  const int n_begin = (part * 4 + wid) * RPS;
+  const int n_step = parts * 4 * RPS;
+
+  const float4* hsrc = reinterpret_cast<const float4*>(hbuf + (size_t)p * I);
+  for (int q = threadIdx.x; q < I / 4; q += 256) reinterpret_cast<float4*>(hs_lds)[q] = hsrc[q];
+  __syncthreads();
   uint32_t hr[NBL2][32];
 #pragma unroll
   for (int m = 0; m < NBL2; ++m) {
     const int b = c + LPR * m;
 #pragma unroll
-    for (int v = 0; v < 32; ++v) hr[m][v] = (b < nbk) ? __float_as_uint(hs_lds[32 * b + v]) : 0u;
-  }
-  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint8_t* dcod = codes + (size_t)e * cb + (size_t)I * H;
-  const uint8_t* dsc = scales + (size_t)e * sb + (size_t)2 * I * H / 32;
-  const int rb = I / 2, rs = I / 32;
-  const int n0 = tile * ROWS_G + wid * ROWS_W;
-#pragma unroll
-  for (int s = 0; s < kDN_STEPS; ++s) {
-    const int n = n0 + s * RPS + rsub;
-    float acc = 0.0f;
-    if (n < H) {
-#pragma unroll
-      for (int m = 0; m < NBL2; ++m) {
-        const int b = c + LPR * m;
-        if (b < nbk) {
-          const uint4 q = load_u4_stream(dcod + (size_t)n * rb + 16 * b);
-          const float sc = e8m0_operand(dsc[(size_t)n * rs + b]);
-          acc = block_dot_f32(q, sc, hr[m], acc);
-        }
-      }
+    for (int v = 0; v < 8; ++v) {
+      float4 f = (b < nbk) ? reinterpret_cast<const float4*>(hs_lds)[b * 8 + v] : make_float4(0.f, 0.f, 0.f, 0.f);
+      hr[m][4 * v] = __float_as_uint(f.x); hr[m][4 * v + 1] = __float_as_uint(f.y);
+      hr[m][4 * v + 2] = __float_as_uint(f.z); hr[m][4 * v + 3] = __float_as_uint(f.w);
     }
-    acc = group_sum<LPR>(acc);
-    if (c == 0 && n < H) ybuf[(size_t)j * H + n] = acc;
+  }
+
+  constexpr int D = 4;  // weight loads run D-1 steps ahead
+  RowBlocks<NBL2> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+#pragma unroll
+    for (int m = 0; m < NBL2; ++m) { ring[d].q[m] = make_uint4(0u, 0u, 0u, 0u); ring[d].s[m] = 0u; }
+  }
+  {
+    const int n = n_begin + rsub;
+    if (n < H) load_row<LPR, NBL2>(ring[0], dcod + (size_t)n * rb, dsc + (size_t)n * rs, c, nbk);
+  }
+#pragma unroll
+  for (int d = 1; d < D - 1; ++d) {
+    const int n = n_begin + d * n_step + rsub;
+    if (d < steps && n < H) load_row<LPR, NBL2>(ring[d], dcod + (size_t)n * rb, dsc + (size_t)n * rs, c, nbk);
+  }
+  for (int s0 = 0; s0 < steps; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int s = s0 + d;
+      if (s >= steps) break;
+      const int nx = s + D - 1;
+      const int nn = n_begin + nx * n_step + rsub;
+      if (nx < steps && nn < H)
+        load_row<LPR, NBL2>(ring[(d + D - 1) % D], dcod + (size_t)nn * rb, dsc + (size_t)nn * rs, c, nbk);
+      const int n0 = n_begin + s * n_step + rsub;
+      const float acc = group_reduce<LPR>(row_dot<true, NBL2>(ring[d], hr));
+      if (c == LPR - 1 && n0 < H) ybuf[(size_t)p * H + n0] = acc;
+    }
   }
 }
 
 // ---------------------------------------------------------------- combine
-// out[t][n] = sum_j w[t][j] * y[t*k+j][n], j ascending; optionally added to a
-// residual: out = resid + sum (resid may alias out).
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ybuf,
-                                                 const float* __restrict__ w, int T, int k, int H,
-                                                 const float* resid, float* out) {
+// out[t][n] = (resid[t][n] +) sum_j w[t][j] * y[t*k+j][n], j ascending; resid
+// may alias out.  Loads are issued in groups of 8 ranks.
+__global__ __launch_bounds__(64) void k_combine(const float* __restrict__ ybuf,
+                                                const float* __restrict__ w, int T, int k, int H,
+                                                const float* resid, float* out) {
   const size_t n4 = (size_t)T * H / 4;
-  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 256) {
+  for (size_t q = (size_t)blockIdx.x * 64 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 64) {
     const size_t flat = 4 * q;
     const int t = (int)(flat / H);
     const int n = (int)(flat % H);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float wj = w[(size_t)t * k + j];
-      const float4 y = *reinterpret_cast<const float4*>(ybuf + ((size_t)t * k + j) * H + n);
-      acc.x = fmaf(wj, y.x, acc.x);
-      acc.y = fmaf(wj, y.y, acc.y);
-      acc.z = fmaf(wj, y.z, acc.z);
-      acc.w = fmaf(wj, y.w, acc.w);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float4 y[8];
+      float wj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < k) {
+          y[u] = *reinterpret_cast<const float4*>(ybuf + ((size_t)t * k + j) * H + n);
+          wj[u] = w[(size_t)t * k + j];
+        } else {
+          y[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          wj[u] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < k) {
+          acc.x = fmaf(wj[u], y[u].x, acc.x);
+          acc.y = fmaf(wj[u], y[u].y, acc.y);
+          acc.z = fmaf(wj[u], y[u].z, acc.z);
+          acc.w = fmaf(wj[u], y[u].w, acc.w);
+        }
+      }
     }
     if (resid) {
       const float4 r = *reinterpret_cast<const float4*>(resid + flat);
@@ -235,38 +358,56 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ybuf,
 
 // ---------------------------------------------------------------- launchers
 
+// Rows per wave and workgroups per pair so that about `target` workgroups
+// share all pairs equally; `unit` = rows one wave handles per step.
+static void split_rows(int rows, int P, int unit, int target, int* parts, int* per_wave) {
+  int want = (target + P - 1) / P;
+  const int max_parts = (rows + 4 * unit - 1) / (4 * unit);
+  if (want > max_parts) want = max_parts;
+  if (want < 1) want = 1;
+  int pw = (rows + 4 * want - 1) / (4 * want);     // rows per wave
+  pw = (pw + unit - 1) / unit * unit;
+  *per_wave = pw;
+  *parts = (rows + 4 * pw - 1) / (4 * pw);
+}
+
 template <bool XF32>
-static hipError_t gateup_dispatch(int nbl, dim3 grid, size_t lds, hipStream_t s, const void* x,
+static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x,
                                   const int32_t* route, const uint8_t* codes, const uint8_t* scales,
-                                  int H, int I, int E, int k, int tiles, float* hbuf) {
+                                  int H, int I, int E, int k, float* hbuf) {
+#define MOE_GU(N)                                                                              \
+  {                                                                                              \
+    int parts, rpw;                                                                              \
+    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N>, lds), &parts, &rpw);                \
+    k_gateup_gemv<XF32, N><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(x, route, codes, scales, H, I, E, \
+                                                                        k, parts, rpw, hbuf);    \
+  }
   switch (nbl) {
-    case 1: k_gateup_gemv<XF32, 1><<<grid, 256, lds, s>>>(x, route, codes, scales, H, I, E, k, tiles, hbuf); break;
-    case 2: k_gateup_gemv<XF32, 2><<<grid, 256, lds, s>>>(x, route, codes, scales, H, I, E, k, tiles, hbuf); break;
-    case 3: k_gateup_gemv<XF32, 3><<<grid, 256, lds, s>>>(x, route, codes, scales, H, I, E, k, tiles, hbuf); break;
-    case 4: k_gateup_gemv<XF32, 4><<<grid, 256, lds, s>>>(x, route, codes, scales, H, I, E, k, tiles, hbuf); break;
+    case 1: MOE_GU(1); break;
+    case 2: MOE_GU(2); break;
+    case 3: MOE_GU(3); break;
+    case 4: MOE_GU(4); break;
     default: return hipErrorInvalidValue;
   }
+#undef MOE_GU
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
                               const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
                               float* hbuf, hipStream_t s) {
-  const int nb = H / 32;
-  const int nbl = (nb + kWave - 1) / kWave;
-  const int tiles = (I + kGU_ROWS - 1) / kGU_ROWS;
-  dim3 grid(P * tiles);
+  const int nbl = (H / 32 + kWave - 1) / kWave;
   const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
-  if (x_f32) return gateup_dispatch<true>(nbl, grid, lds, s, x, route, codes, scales, H, I, E, k, tiles, hbuf);
-  return gateup_dispatch<false>(nbl, grid, lds, s, x, route, codes, scales, H, I, E, k, tiles, hbuf);
+  if (x_f32) return gateup_dispatch<true>(nbl, P, lds, s, x, route, codes, scales, H, I, E, k, hbuf);
+  return gateup_dispatch<false>(nbl, P, lds, s, x, route, codes, scales, H, I, E, k, hbuf);
 }
 
-// lanes per row and blocks per lane for a reduction length of nbk blocks:
-// the smallest LPR in {4, 8, 16, 32, 64} with nbk <= 4 * LPR and no more idle
-// lane slots than a larger LPR would leave.
+// Lanes per row and blocks per lane for a reduction length of nbk blocks:
+// the LPR in {4, 8, 16, 32, 64} with NBL2 = ceil(nbk / LPR) <= 4 that leaves
+// the fewest idle lane slots (the smallest such LPR on ties).
 void down_shape(int nbk, int* lpr, int* nbl2) {
   static const int cand[5] = {4, 8, 16, 32, 64};
-  int best = -1, best_idle = 1 << 30;
+  int best = 4, best_idle = 1 << 30;
   for (int i = 0; i < 5; ++i) {
     const int L = cand[i];
     const int nb = (nbk + L - 1) / L;
@@ -278,13 +419,14 @@ void down_shape(int nbk, int* lpr, int* nbl2) {
   *nbl2 = (nbk + *lpr - 1) / *lpr;
 }
 
-#define MOE_DOWN_CASE(L, N)                                                                        \
-  if (lpr == L && nbl2 == N) {                                                                   \
-    constexpr int ROWS_G = 4 * (kWave / L) * kDN_STEPS;                                           \
-    const int tiles = (H + ROWS_G - 1) / ROWS_G;                                                  \
-    k_down_gemv<L, N><<<dim3(P * tiles), 256, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E, \
-                                                        tiles, ybuf);                              \
-    return hipGetLastError();                                                                      \
+#define MOE_DOWN_CASE(L, N)                                                                          \
+  if (lpr == L && nbl2 == N) {                                                                     \
+    int parts, rpw;                                                                                \
+    split_rows(H, P, kWave / L, resident_wgs(k_down_gemv<L, N>, lds), &parts, &rpw);              \
+    k_down_gemv<L, N><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(hbuf, pair_expert, codes, scales, \
+                                                                   H, I, E, parts, rpw / (kWave / L), \
+                                                                   ybuf);                            \
+    return hipGetLastError();                                                                        \
   }
 
 hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
@@ -303,9 +445,9 @@ hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P
 hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,
                           float* out, hipStream_t s) {
   const size_t n4 = (size_t)T * H / 4;
-  size_t blocks = (n4 + 255) / 256;
+  size_t blocks = (n4 + 63) / 64;
   if (blocks > 4096) blocks = 4096;
-  k_combine<<<dim3((unsigned)blocks), 256, 0, s>>>(ybuf, w, T, k, H, resid, out);
+  k_combine<<<dim3((unsigned)blocks), 64, 0, s>>>(ybuf, w, T, k, H, resid, out);
   return hipGetLastError();
 }
 

@@ -11,38 +11,57 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router logits
-// One workgroup per (expert row, tile of TT tokens).  Each thread streams a
-// strided set of float4s of the router row and FMAs them with the same columns
-// of up to TT tokens; the block reduction order is fixed.
-template <bool XF32, int TT>
+// One workgroup per (expert row, tile of TT tokens).  Thread i owns float4
+// columns i + 256*c (c < NW) of the router row; all of the row's loads are
+// issued before the FMAs.  The reduction order (DPP within a wave, then the 4
+// wave sums in a fixed order) does not depend on timing.
+template <bool XF32, int TT, int NW>
 __global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ x,
                                                        const float* __restrict__ wr,
                                                        const float* __restrict__ bias, int T, int H,
                                                        int E, float* __restrict__ logits) {
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * TT;
+  const int n4 = H / 4;
   const float4* wrow = reinterpret_cast<const float4*>(wr + (size_t)e * H);
+  float4 w[NW];
+#pragma unroll
+  for (int c = 0; c < NW; ++c) {
+    const int q = threadIdx.x + 256 * c;
+    if (q < n4) {
+      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wrow + q));
+      w[c] = make_float4(v.x, v.y, v.z, v.w);
+    } else {
+      w[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   float acc[TT];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
-  const int n4 = H / 4;
-  for (int c = threadIdx.x; c < n4; c += 256) {
-    float4 w = wrow[c];
+  for (int t = 0; t < TT; ++t) {
+    acc[t] = 0.0f;
+    if (t0 + t < T) {
+      float4 xv[NW];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t0 + t < T) {
-        float4 xv;
-        if constexpr (XF32) {
-          xv = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)(t0 + t) * H)[c];
+      for (int c = 0; c < NW; ++c) {
+        const int q = threadIdx.x + 256 * c;
+        if (q < n4) {
+          if constexpr (XF32) {
+            xv[c] = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)(t0 + t) * H)[q];
+          } else {
+            uint2 b = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + t) * H)[q];
+            xv[c] = make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
+                                bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
+          }
         } else {
-          uint2 b = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + t) * H)[c];
-          xv = make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
-                           bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
+          xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        acc[t] = fmaf(w.x, xv.x, acc[t]);
-        acc[t] = fmaf(w.y, xv.y, acc[t]);
-        acc[t] = fmaf(w.z, xv.z, acc[t]);
-        acc[t] = fmaf(w.w, xv.w, acc[t]);
+      }
+#pragma unroll
+      for (int c = 0; c < NW; ++c) {
+        acc[t] = fmaf(w[c].x, xv[c].x, acc[t]);
+        acc[t] = fmaf(w[c].y, xv[c].y, acc[t]);
+        acc[t] = fmaf(w[c].z, xv[c].z, acc[t]);
+        acc[t] = fmaf(w[c].w, xv[c].w, acc[t]);
       }
     }
   }
@@ -50,7 +69,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ 
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    float v = group_sum<kWave>(acc[t]);
+    float v = wave_sum(acc[t]);
     if (lane == 0) red[t][wid] = v;
   }
   __syncthreads();
@@ -78,18 +97,31 @@ __device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
   return ((uint64_t)ord << 32) | (uint32_t)(~e);
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Largest 64-bit key of the wavefront, returned in every lane.  Lanes of rows
+// a broadcast does not reach receive 0, which never wins.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = umax64(v, dpp_u64<0xB1>(v));
+  v = umax64(v, dpp_u64<0x4E>(v));
+  v = umax64(v, dpp_u64<0x141>(v));
+  v = umax64(v, dpp_u64<0x140>(v));
+  v = umax64(v, dpp_u64<0x142, 0xA>(v));
+  v = umax64(v, dpp_u64<0x143, 0xC>(v));
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // One wavefront per token; each lane owns experts lane + 64*v, v < MAXV.
+// Round j takes the largest remaining key over the wave (its owner clears it).
 template <int MAXV>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E,
                                                       int k, int32_t* __restrict__ idx,
@@ -98,28 +130,34 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   const float* l = logits + (size_t)t * E;
+  float lv[MAXV];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int e = lane + kWave * v;
+    lv[v] = (e < E) ? l[e] : 0.0f;
+  }
   uint64_t key[MAXV];
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
-    int e = lane + kWave * v;
-    key[v] = (e < E) ? rank_key(l[e], (uint32_t)e) : 0ull;
+    const int e = lane + kWave * v;
+    key[v] = (e < E) ? rank_key(lv[v], (uint32_t)e) : 0ull;
   }
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int v = 0; v < MAXV; ++v) best = key[v] > best ? key[v] : best;
-    uint64_t win = wave_max_u64(best);
+    for (int v = 0; v < MAXV; ++v) best = umax64(best, key[v]);
+    const uint64_t win = wave_max_u64(best);
 #pragma unroll
     for (int v = 0; v < MAXV; ++v)
       if (key[v] == win) key[v] = 0;          // keys are unique: only the owner matches
     if (lane == j) my_idx = (int)(~(uint32_t)win);
   }
   // softmax over the selected logits, in rank order
-  float lj = (lane < k) ? l[my_idx] : 0.0f;
-  float m = __shfl(lj, 0, kWave);
-  float ex = (lane < k) ? expf(lj - m) : 0.0f;
-  float s = group_sum<kWave>(ex);
+  const float lj = (lane < k) ? l[my_idx] : 0.0f;
+  const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
+  const float ex = (lane < k) ? expf(lj - m) : 0.0f;
+  const float s = wave_sum(ex);
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_idx;
     wout[(size_t)t * k + lane] = ex / s;
@@ -214,15 +252,37 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* 
 
 // ---------------------------------------------------------------- launchers
 
+template <bool XF32, int TT>
+static hipError_t router_dispatch(dim3 grid, hipStream_t s, const void* x, const float* wr, const float* bias,
+                                  int T, int H, int E, float* logits) {
+  const int nw = (H / 4 + 255) / 256;
+#define MOE_RT(N) k_router_logits<XF32, TT, N><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits)
+  switch (nw) {
+    case 1: MOE_RT(1); break;
+    case 2: MOE_RT(2); break;
+    case 3: MOE_RT(3); break;
+    case 4: MOE_RT(4); break;
+    case 5: MOE_RT(5); break;
+    case 6: MOE_RT(6); break;
+    case 7: MOE_RT(7); break;
+    case 8: MOE_RT(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_RT
+  return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const void* x, bool x_f32, const float* wr, const float* bias, int T,
                                 int H, int E, float* logits, hipStream_t s) {
+  if (T == 1) {
+    const dim3 grid(E, 1);
+    return x_f32 ? router_dispatch<true, 1>(grid, s, x, wr, bias, T, H, E, logits)
+                 : router_dispatch<false, 1>(grid, s, x, wr, bias, T, H, E, logits);
+  }
   constexpr int TT = 4;
-  dim3 grid(E, (T + TT - 1) / TT);
-  if (x_f32)
-    k_router_logits<true, TT><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
-  else
-    k_router_logits<false, TT><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
-  return hipGetLastError();
+  const dim3 grid(E, (T + TT - 1) / TT);
+  return x_f32 ? router_dispatch<true, TT>(grid, s, x, wr, bias, T, H, E, logits)
+               : router_dispatch<false, TT>(grid, s, x, wr, bias, T, H, E, logits);
 }
 
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
