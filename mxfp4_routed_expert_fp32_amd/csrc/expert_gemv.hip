@@ -106,28 +106,36 @@ __device__ __forceinline__ float block_dot_f32(uint4 q, float s, const uint32_t*
   return acc;
 }
 
+// Weights are read through raw buffer loads: a resource per matrix (base in
+// SGPRs, byte range = the matrix) and a 32-bit offset per lane.  An offset
+// past the range returns zeros, which is how blocks past a row's end and rows
+// past a matrix's end are read: zero codes with scale byte 0 (a finite
+// 2^-127) add exactly 0.  No clamps or branches sit around the loads.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // One row's worth of a lane's blocks: NBL 16-byte code blocks + scale bytes.
 template <int NBL>
 struct RowBlocks {
-  uint4 q[NBL];
+  u32x4 q[NBL];
   uint32_t s[NBL];
 };
 
-// Loads blocks b = c + LPR*m of one row; blocks past the row end are zero
-// (zero codes times zero activations add nothing) and are never read.
+// Blocks b = c + LPR*m of row `row` (row < 0: none) of a [rows][nb*32] matrix.
 template <int LPR, int NBL>
-__device__ __forceinline__ void load_row(RowBlocks<NBL>& r, const uint8_t* row_codes,
-                                         const uint8_t* row_scales, int c, int nb) {
+__device__ __forceinline__ void load_row(RowBlocks<NBL>& r, rsrc_t codes, rsrc_t scales, int row, int c,
+                                         int nb) {
+  const uint32_t rc = (uint32_t)row * (uint32_t)(nb * 16), rsc = (uint32_t)row * (uint32_t)nb;
 #pragma unroll
   for (int m = 0; m < NBL; ++m) {
     const int b = c + LPR * m;
-    if (b < nb) {
-      r.q[m] = load_u4_stream(row_codes + 16 * b);
-      r.s[m] = row_scales[b];
-    } else {
-      r.q[m] = make_uint4(0u, 0u, 0u, 0u);
-      r.s[m] = 0u;
-    }
+    const bool ok = row >= 0 && b < nb;
+    r.q[m] = __builtin_amdgcn_raw_buffer_load_b128(codes, ok ? rc + 16u * b : kOOB, 0, 2 /* nt */);
+    r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(scales, ok ? rsc + b : kOOB, 0, 0);
   }
 }
 
@@ -137,10 +145,11 @@ __device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t
 #pragma unroll
   for (int m = 0; m < NBL; ++m) {
     const float s = e8m0_operand(r.s[m]);
+    const uint4 q = make_uint4(r.q[m].x, r.q[m].y, r.q[m].z, r.q[m].w);
     if constexpr (XF32)
-      acc = block_dot_f32(r.q[m], s, xr[m], acc);
+      acc = block_dot_f32(q, s, xr[m], acc);
     else
-      acc = block_dot_bf16(r.q[m], s, xr[m], acc);
+      acc = block_dot_bf16(q, s, xr[m], acc);
   }
   return acc;
 }
@@ -177,27 +186,23 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  int e = route[p];
+  int e = __builtin_amdgcn_readfirstlane(route[p]);
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nb = H / 32;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint8_t* gcod = codes + (size_t)e * cb;
-  const uint8_t* ucod = gcod + (size_t)I * H / 2;
-  const uint8_t* gsc = scales + (size_t)e * sb;
-  const uint8_t* usc = gsc + (size_t)I * H / 32;
-  const int rb = H / 2, rs = H / 32;
-  // rows interleaved across the pair's waves: step r of wave (part, wid)
-  // takes row r*parts*4 + part*4 + wid, so the pair's waves stream
-  // neighbouring rows at any moment
-  const int i_begin = part * 4 + wid;
-  const int i_step = parts * 4;
-  const int i_end = I;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const rsrc_t gcod = make_rsrc(codes + (size_t)e * cb, mc);
+  const rsrc_t ucod = make_rsrc(codes + (size_t)e * cb + mc, mc);
+  const rsrc_t gsc = make_rsrc(scales + (size_t)e * sb, ms);
+  const rsrc_t usc = make_rsrc(scales + (size_t)e * sb + ms, ms);
+  // rows interleaved across the pair's waves
+  const int i0 = part * 4 + wid;
+  const int istep = parts * 4;
+  const int nsteps = i0 < I ? (I - i0 + istep - 1) / istep : 0;
 
   RowBlocks<NBL> g0, u0, g1, u1;
-  if (i_begin < i_end) {
-    load_row<kWave, NBL>(g0, gcod + (size_t)i_begin * rb, gsc + (size_t)i_begin * rs, lane, nb);
-    load_row<kWave, NBL>(u0, ucod + (size_t)i_begin * rb, usc + (size_t)i_begin * rs, lane, nb);
-  }
+  load_row<kWave, NBL>(g0, gcod, gsc, nsteps > 0 ? i0 : -1, lane, nb);
+  load_row<kWave, NBL>(u0, ucod, usc, nsteps > 0 ? i0 : -1, lane, nb);
 
   // stage this token's activations, then keep the lane's blocks in registers
   const int xbytes = XF32 ? H * 4 : H * 2;
@@ -215,21 +220,18 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
     }
   }
 
-  for (int i = i_begin; i < i_end; i += 2 * i_step) {
-    const int i1 = i + i_step, i2 = i + 2 * i_step;
-    const bool has1 = i1 < i_end;
-    if (has1) {
-      load_row<kWave, NBL>(g1, gcod + (size_t)i1 * rb, gsc + (size_t)i1 * rs, lane, nb);
-      load_row<kWave, NBL>(u1, ucod + (size_t)i1 * rb, usc + (size_t)i1 * rs, lane, nb);
-    }
+  for (int st = 0; st < nsteps; st += 2) {
+    const int i = i0 + st * istep, i1 = i + istep, i2 = i1 + istep;
+    const bool has1 = st + 1 < nsteps;
+    load_row<kWave, NBL>(g1, gcod, gsc, has1 ? i1 : -1, lane, nb);
+    load_row<kWave, NBL>(u1, ucod, usc, has1 ? i1 : -1, lane, nb);
     float ag = wave_sum(row_dot<XF32, NBL>(g0, xr));
     float au = wave_sum(row_dot<XF32, NBL>(u0, xr));
     if (lane == 0) hbuf[(size_t)p * I + i] = silu_mul(ag, au);
     if (!has1) break;
-    if (i2 < i_end) {
-      load_row<kWave, NBL>(g0, gcod + (size_t)i2 * rb, gsc + (size_t)i2 * rs, lane, nb);
-      load_row<kWave, NBL>(u0, ucod + (size_t)i2 * rb, usc + (size_t)i2 * rs, lane, nb);
-    }
+    const bool has2 = st + 2 < nsteps;
+    load_row<kWave, NBL>(g0, gcod, gsc, has2 ? i2 : -1, lane, nb);
+    load_row<kWave, NBL>(u0, ucod, usc, has2 ? i2 : -1, lane, nb);
     ag = wave_sum(row_dot<XF32, NBL>(g1, xr));
     au = wave_sum(row_dot<XF32, NBL>(u1, xr));
     if (lane == 0) hbuf[(size_t)p * I + i1] = silu_mul(ag, au);
@@ -250,20 +252,28 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
                                                    int E, int parts, int steps, float* __restrict__ ybuf) {
   extern __shared__ float hs_lds[];
   constexpr int RPS = kWave / LPR;
+  constexpr int D = 4;  // weight loads run D-1 steps ahead
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int c = lane % LPR, rsub = lane / LPR;
-  int e = pair_expert[p];
+  int e = __builtin_amdgcn_readfirstlane(pair_expert[p]);
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nbk = I / 32;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint8_t* dcod = codes + (size_t)e * cb + (size_t)I * H;
-  const uint8_t* dsc = scales + (size_t)e * sb + (size_t)2 * I * H / 32;
-  const int rb = I / 2, rs = I / 32;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const rsrc_t dcod = make_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
+  const rsrc_t dsc = make_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
   // row groups interleaved across the pair's waves (see k_gateup_gemv)
-  const int n_begin = (part * 4 + wid) * RPS;
+  const int n_begin = (part * 4 + wid) * RPS + rsub;
   const int n_step = parts * 4 * RPS;
+
+  RowBlocks<NBL2> ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    const int n = n_begin + d * n_step;
+    load_row<LPR, NBL2>(ring[d], dcod, dsc, (d < steps && n < H) ? n : -1, c, nbk);
+  }
 
   const float4* hsrc = reinterpret_cast<const float4*>(hbuf + (size_t)p * I);
   for (int q = threadIdx.x; q < I / 4; q += 256) reinterpret_cast<float4*>(hs_lds)[q] = hsrc[q];
@@ -280,32 +290,15 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
     }
   }
 
-  constexpr int D = 4;  // weight loads run D-1 steps ahead
-  RowBlocks<NBL2> ring[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-#pragma unroll
-    for (int m = 0; m < NBL2; ++m) { ring[d].q[m] = make_uint4(0u, 0u, 0u, 0u); ring[d].s[m] = 0u; }
-  }
-  {
-    const int n = n_begin + rsub;
-    if (n < H) load_row<LPR, NBL2>(ring[0], dcod + (size_t)n * rb, dsc + (size_t)n * rs, c, nbk);
-  }
-#pragma unroll
-  for (int d = 1; d < D - 1; ++d) {
-    const int n = n_begin + d * n_step + rsub;
-    if (d < steps && n < H) load_row<LPR, NBL2>(ring[d], dcod + (size_t)n * rb, dsc + (size_t)n * rs, c, nbk);
-  }
   for (int s0 = 0; s0 < steps; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int s = s0 + d;
-      if (s >= steps) break;
-      const int nx = s + D - 1;
-      const int nn = n_begin + nx * n_step + rsub;
-      if (nx < steps && nn < H)
-        load_row<LPR, NBL2>(ring[(d + D - 1) % D], dcod + (size_t)nn * rb, dsc + (size_t)nn * rs, c, nbk);
-      const int n0 = n_begin + s * n_step + rsub;
+      const int st = s0 + d;
+      if (st >= steps) break;
+      const int sn = st + D - 1;
+      const int nn = n_begin + sn * n_step;
+      load_row<LPR, NBL2>(ring[(d + D - 1) % D], dcod, dsc, (sn < steps && nn < H) ? nn : -1, c, nbk);
+      const int n0 = n_begin + st * n_step;
       const float acc = group_reduce<LPR>(row_dot<true, NBL2>(ring[d], hr));
       if (c == LPR - 1 && n0 < H) ybuf[(size_t)p * H + n0] = acc;
     }

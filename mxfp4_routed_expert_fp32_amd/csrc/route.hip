@@ -120,14 +120,35 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Number of lanes whose 64-bit key is larger than this lane's (keys unique).
+__device__ __forceinline__ int rank_in_wave(uint64_t v) {
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < kWave; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
+    r += ((((uint64_t)hi << 32) | lo) > v) ? 1 : 0;
+  }
+  return r;
+}
+
 // One wavefront per token; each lane owns experts lane + 64*v, v < MAXV.
-// Round j takes the largest remaining key over the wave (its owner clears it).
+// Selection: let L be the k-th largest of the 64 lane maxima.  The k largest
+// lane maxima are k keys >= L, so the top k keys are all >= L; these
+// candidates (usually a few more than k) are gathered into one key per lane
+// and each one's rank among them is its place in the route.  When more than
+// 64 keys are >= L (heavy skew inside a few lanes) the wave falls back to k
+// rounds of "take the largest remaining key".  Both give the unique order
+// defined by rank_key.
 template <int MAXV>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E,
                                                       int k, int32_t* __restrict__ idx,
                                                       float* __restrict__ wout) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  __shared__ uint64_t cand[4][kWave];
+  __shared__ uint32_t ncand[4];
+  __shared__ uint32_t sel_e[4][kWave];
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   const float* l = logits + (size_t)t * E;
   float lv[MAXV];
@@ -137,29 +158,72 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
     lv[v] = (e < E) ? l[e] : 0.0f;
   }
   uint64_t key[MAXV];
+  uint64_t lmax = 0;
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
     const int e = lane + kWave * v;
     key[v] = (e < E) ? rank_key(lv[v], (uint32_t)e) : 0ull;
+    lmax = umax64(lmax, key[v]);
   }
-  int my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) best = umax64(best, key[v]);
-    const uint64_t win = wave_max_u64(best);
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v)
-      if (key[v] == win) key[v] = 0;          // keys are unique: only the owner matches
-    if (lane == j) my_idx = (int)(~(uint32_t)win);
+  // L = k-th largest lane maximum (the lane of rank k-1); 0 if fewer lanes hold keys
+  const int lrank = rank_in_wave(lmax);
+  const uint64_t sel_lane = __builtin_amdgcn_ballot_w64(lrank == k - 1);
+  uint64_t L = 0;
+  if (sel_lane) {
+    const int src = __builtin_ctzll(sel_lane);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)lmax, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(lmax >> 32), src);
+    L = ((uint64_t)hi << 32) | lo;
   }
+  // candidates: keys >= L
+  int mine = 0;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) mine += (key[v] != 0ull && key[v] >= L) ? 1 : 0;
+  int total = mine;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) total += __shfl_xor(total, m, kWave);
+
+  int my_rank = kWave;          // rank of this lane's entry (>= k: not selected)
+  uint32_t my_e = 0;
+  if (total <= kWave) {
+    if (lane == 0) ncand[wid] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      if (key[v] != 0ull && key[v] >= L) {
+        const uint32_t pos = atomicAdd(&ncand[wid], 1u);
+        cand[wid][pos] = key[v];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const uint64_t c = (lane < total) ? cand[wid][lane] : 0ull;
+    const int r = rank_in_wave(c);
+    if (lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int v = 0; v < MAXV; ++v) best = umax64(best, key[v]);
+      const uint64_t win = wave_max_u64(best);
+#pragma unroll
+      for (int v = 0; v < MAXV; ++v)
+        if (key[v] == win) key[v] = 0;
+      if (lane == j) { my_rank = j; my_e = ~(uint32_t)win; }
+    }
+  }
+  // lane r < k receives the entry of rank r
+  if (my_rank < k) sel_e[wid][my_rank] = my_e;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int sel = (lane < k) ? (int)sel_e[wid][lane] : 0;
   // softmax over the selected logits, in rank order
-  const float lj = (lane < k) ? l[my_idx] : 0.0f;
+  const float lj = (lane < k) ? l[sel] : 0.0f;
   const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
   const float ex = (lane < k) ? expf(lj - m) : 0.0f;
   const float s = wave_sum(ex);
   if (lane < k) {
-    idx[(size_t)t * k + lane] = my_idx;
+    idx[(size_t)t * k + lane] = sel;
     wout[(size_t)t * k + lane] = ex / s;
   }
 }
