@@ -65,7 +65,8 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t logits, idx, w, h, y, offsets, pairs, total;
+  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, total;
+  int max_blocks;
 };
 
 int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
@@ -85,10 +86,13 @@ int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) 
   L->y = c.take(b[4]);
   L->offsets = c.take(b[5]);
   L->pairs = c.take(b[6]);
+  L->max_blocks = moe::max_expert_blocks((int)Tk, d->n_experts);
+  L->blocks = c.take((size_t)L->max_blocks * 16);
+  L->nblocks = c.take(4);
   L->total = c.take(0);
   if (c.overflow) return MOE_ERR_OVERFLOW;
-  // pair indices are int32 on the device
-  if (Tk > (size_t)INT32_MAX) return MOE_ERR_OVERFLOW;
+  // pair indices are int32 on the device; MFMA-path byte offsets are 32-bit
+  if (Tk > (size_t)INT32_MAX / 8) return MOE_ERR_OVERFLOW;
   return MOE_OK;
 }
 
@@ -117,6 +121,21 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  if (T > 1 && !x_f32 && H % 128 == 0 && I % 128 == 0) {
+    // prefill form: sort pairs by expert, grouped GEMMs on MFMA, combine
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
+    int4* blocks = reinterpret_cast<int4*>(ws + L.blocks);
+    int32_t* nblocks = reinterpret_cast<int32_t*>(ws + L.nblocks);
+    uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][P][I] bf16, same bytes as h
+    MOE_TRY(dev(moe::launch_sort_by_expert(idx, T, E, k, offsets, pairs, s)));
+    MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, blocks, nblocks, s)));
+    MOE_TRY(dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), pairs, blocks, nblocks, L.max_blocks, c, sc,
+                                        H, I, k, P, hterm, s)));
+    MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, P, y, s)));
+    MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
+    return MOE_OK;
+  }
   MOE_TRY(dev(moe::launch_gateup_gemv(x, x_f32, idx, P, k, c, sc, H, I, E, h, s)));
   MOE_TRY(dev(moe::launch_down_gemv(h, idx, P, c, sc, H, I, E, y, s)));
   MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));

@@ -250,3 +250,30 @@ def test_rmsnorm_and_residual():
     moe.moe_residual_add(rd, d)
     torch.cuda.synchronize()
     assert np.array_equal(rd.cpu().numpy(), oracle.residual_add(r, r[::-1]))
+
+
+# ------------------------------------------------------------------ prefill form (grouped GEMM on MFMA)
+
+@pytest.mark.parametrize("H,I,E,k,T,hot", [(256, 128, 8, 2, 37, False), (512, 256, 16, 4, 65, False),
+                                           (256, 128, 4, 2, 300, True), (1024, 384, 12, 3, 130, True)])
+def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
+    """T > 1 with bf16 activations runs the sort + MFMA grouped GEMMs; expert
+    blocks are ragged, and `hot` makes one expert take more than 128 tokens."""
+    w = synth.Workload("g", 63, T, H, I, E, k, "bf16", weight_seed=7500 + H + E + T)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    b = np.zeros(E, np.float32)
+    if hot:
+        b[1] = 8.0  # expert 1 is selected by (nearly) every token
+    bias = torch.from_numpy(b).to(DEV)
+    out, logits, idx, wt = run_forward(desc, w, x, wr, bias, codes, scales, k)
+    if hot:
+        assert np.sum(idx == 1) > 128
+    xf = synth.tokens_f32(w, range(T))
+    r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, b, logits)
+    assert np.array_equal(idx, r_idx)
+    P.assert_weights_close(wt, r_w, k)
+    err = P.assert_out_close(out, r_out)
+    assert err < 1e-5, err
