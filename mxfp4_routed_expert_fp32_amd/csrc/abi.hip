@@ -110,6 +110,15 @@ int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
   return MOE_OK;
 }
 
+// Router logits: many bf16 tokens go to the MFMA kernel (fp32 weights split
+// into three exact bf16 terms), a few tokens or fp32 tokens to the GEMV.
+hipError_t router(const moe_layer_desc* d, const void* x, bool x_f32, const float* wr, const float* bias,
+                  int32_t T, float* logits, hipStream_t s) {
+  if (T > 8 && !x_f32 && d->hidden % 128 == 0)
+    return moe::launch_router_mfma(static_cast<const uint16_t*>(x), wr, bias, T, d->hidden, d->n_experts, logits, s);
+  return moe::launch_router_logits(x, x_f32, wr, bias, T, d->hidden, d->n_experts, logits, s);
+}
+
 // A5..A9 given routing (idx, w on the device).  For one token the pairs are
 // the k ranks of that token and idx itself is the pair -> expert map.
 int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_t* idx, const float* w,
@@ -166,7 +175,7 @@ int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   float* w = w_out ? w_out : reinterpret_cast<float*>(ws + L.w);
   const bool xf = x_dtype == MOE_DTYPE_F32;
-  MOE_TRY(dev(moe::launch_router_logits(x, xf, router_w, router_bias, T, d->hidden, d->n_experts, logits, s)));
+  MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, s)));
   MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
   return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);
 }
@@ -308,8 +317,7 @@ int moe_router_logits(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (n_tokens < 1 || n_tokens > kMaxTokens) return MOE_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_ALIGN;
-  return dev(moe::launch_router_logits(x, x_dtype == MOE_DTYPE_F32, router_w, router_bias, n_tokens,
-                                       d->hidden, d->n_experts, logits, as_stream(stream)));
+  return dev(router(d, x, x_dtype == MOE_DTYPE_F32, router_w, router_bias, n_tokens, logits, as_stream(stream)));
 }
 
 int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* idx,

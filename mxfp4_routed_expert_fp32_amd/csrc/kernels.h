@@ -35,6 +35,10 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int P,
                             float* ybuf, hipStream_t s);
 
+// Router logits for many bf16 tokens on MFMA (H a multiple of 128).
+hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
+                              float* logits, hipStream_t s);
+
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
                           hipStream_t s);

@@ -140,6 +140,25 @@ def test_router_logits_within_bound(name):
     P.assert_logits_close(logits.cpu().numpy(), oracle.router_logits(xf, wr_h), xf, wr_h)
 
 
+@pytest.mark.parametrize("T,H,E", [(9, 256, 8), (130, 512, 33), (300, 7168, 896), (4096, 7168, 896)])
+def test_router_mfma_logits_within_bound(T, H, E):
+    """Many bf16 tokens take the MFMA router (fp32 weights as three bf16
+    terms): ragged token and expert tiles, the decode model's shape and the
+    4096-token prefill batch (sampled tokens)."""
+    w = synth.Workload("rt", 64, T, H, 128, E, 2, "bf16", weight_seed=7600 + T + E)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    b = np.random.default_rng(T).standard_normal(E).astype(np.float32)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    moe.moe_router_logits(sd.desc_for(w), x, wr, torch.from_numpy(b).to(DEV), logits)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 300 else np.unique(np.r_[0, 1, 127, 128, T - 1, np.random.default_rng(1).integers(0, T, 40)])
+    xf = synth.tokens_f32(w, rows)
+    wr_h = wr.cpu().numpy()
+    got = logits.cpu().numpy()[rows]
+    P.assert_logits_close(got, oracle.router_logits(xf, wr_h, bias=b), xf, wr_h, bias=b)
+
+
 def test_sort_by_expert_matches_stable_sort():
     rng = np.random.default_rng(9)
     for T, E, k in [(1, 8, 2), (64, 896, 16), (4096, 896, 16), (130, 50, 5)]:
@@ -272,6 +291,7 @@ def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     if hot:
         assert np.sum(idx == 1) > 128
     xf = synth.tokens_f32(w, range(T))
+    P.assert_logits_close(logits, oracle.router_logits(xf, wr.cpu().numpy(), bias=b), xf, wr.cpu().numpy(), bias=b)
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, b, logits)
     assert np.array_equal(idx, r_idx)
     P.assert_weights_close(wt, r_w, k)
