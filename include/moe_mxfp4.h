@@ -113,7 +113,7 @@ int moe_mxfp4_packed_bytes(const moe_layer_desc* desc, size_t* codes_bytes, size
 int moe_workspace_bytes(const moe_layer_desc* desc, int32_t n_tokens, int32_t k, size_t* bytes);
 
 /*
- * A0 -- pack `expert_count` experts given back to back in the logical layout
+ * Pack -- copy `expert_count` experts given back to back in the logical layout
  * (device buffers logical_codes / logical_scales) into the device layout
  * buffers packed_codes / packed_scales at experts expert_begin ..
  * expert_begin + expert_count - 1.  Identity on values.  Lets a caller upload
@@ -124,7 +124,8 @@ int moe_mxfp4_pack(const moe_layer_desc* desc, const void* logical_codes, const 
                    void* stream);
 
 /*
- * A2..A9 -- the whole layer for n_tokens tokens.
+ * The whole layer (router logits, top-k, softmax, token -> expert sort, expert
+ * gate/up + SwiGLU, expert down, rank-ordered combine) for n_tokens tokens.
  *   x            [n_tokens][H], fp32 or bf16 (x_dtype), 16-byte aligned
  *   router_w     [E][H] fp32 row-major
  *   router_bias  [E] fp32 or NULL; added to the logits (moves selection and weights)
@@ -145,7 +146,7 @@ int moe_mxfp4_forward(const moe_layer_desc* desc, const void* x, int32_t x_dtype
                       size_t workspace_bytes, void* stream);
 
 /*
- * A5..A9 with the routing given: topk_idx [n_tokens][k] int32 (each row k
+ * The expert part of the layer with the routing given: topk_idx [n_tokens][k] int32 (each row k
  * distinct expert ids in [0, E)) and topk_w [n_tokens][k] fp32.  Same output
  * and workspace contract as moe_mxfp4_forward.  Expert ids are not range
  * checked on the device beyond clamping; out-of-range ids give unspecified
@@ -160,10 +161,10 @@ int moe_mxfp4_experts(const moe_layer_desc* desc, const void* x, int32_t x_dtype
  * Decode-form stages alone (the kernels moe_mxfp4_forward runs for one token),
  * for stage-level checks and timing.  A pair p = t*k + j is token t = p / k of
  * x with expert pair_expert[p] in [0, E).
- * A7: h [n_pairs][I] fp32, h[p][i] = silu(g) * u with g = Wg[i] . x[t],
+ * gate/up: h [n_pairs][I] fp32, h[p][i] = silu(g) * u with g = Wg[i] . x[t],
  *     u = Wu[i] . x[t], silu(g) = g / (1 + exp(-g)).
- * A8: y [n_pairs][H] fp32, y[p][n] = Wd[n] . h[p].
- * A9: out[t][n] = (resid[t][n] +) sum_{j<k} w[t][j] * y[t*k+j][n], j ascending;
+ * down:    y [n_pairs][H] fp32, y[p][n] = Wd[n] . h[p].
+ * combine: out[t][n] = (resid[t][n] +) sum_{j<k} w[t][j] * y[t*k+j][n], j ascending;
  *     resid may be NULL or alias out.
  */
 int moe_mxfp4_gate_up(const moe_layer_desc* desc, const void* x, int32_t x_dtype,
@@ -175,18 +176,18 @@ int moe_mxfp4_down(const moe_layer_desc* desc, const float* h, const int32_t* pa
 int moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden,
                 const float* resid, float* out, void* stream);
 
-/* A2 alone: logits [n_tokens][E] = x . router_w^T (+ bias), fp32 accumulation. */
+/* Router logits alone: logits [n_tokens][E] = x . router_w^T (+ bias), fp32 accumulation. */
 int moe_router_logits(const moe_layer_desc* desc, const void* x, int32_t x_dtype,
                       const float* router_w, const float* router_bias, int32_t n_tokens,
                       float* logits, void* stream);
 
-/* A3+A4 alone, from given logits [n_tokens][n_experts]: idx [n_tokens][k] in
+/* Top-k + softmax alone, from given logits [n_tokens][n_experts]: idx [n_tokens][k] in
  * rank order and softmax weights w [n_tokens][k].  1 <= k <= min(E, 64),
  * E <= 4096. */
 int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                      int32_t* idx, float* w, void* stream);
 
-/* A5 alone: stable counting sort of the (token, rank) pairs by expert.
+/* Token -> expert sort alone: stable counting sort of the (token, rank) pairs by expert.
  *   expert_offsets [E+1]: pairs of expert e are pair_list[offsets[e] .. offsets[e+1])
  *   pair_list [n_tokens*k]: pair id t*k + j, ordered by expert, then token
  * The workspace must hold moe_sort_workspace_bytes(E, n_tokens, k) bytes. */
@@ -195,23 +196,23 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
                        int32_t* expert_offsets, int32_t* pair_list, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* A6 alone: dequantise one matrix of one expert from the device layout to
+/* Dequantisation alone: dequantise one matrix of one expert from the device layout to
  * fp32, exactly: out = E2M1(code) * 2^(scale - 127), subnormals kept, +-inf on
  * overflow, scale byte 0xFF -> NaN 0x7FC00000.  matrix 0 = gate [I][H],
  * 1 = up [I][H], 2 = down [H][I]. */
 int moe_mxfp4_dequant(const moe_layer_desc* desc, const void* packed_codes, const void* packed_scales,
                       int64_t expert, int32_t matrix, float* out, void* stream);
 
-/* A1: RMSNorm with gain, n = r / sqrt(mean(r^2) + eps) * gamma, per token.
+/* RMSNorm with gain, n = r / sqrt(mean(r^2) + eps) * gamma, per token.
  * r, n: [n_tokens][hidden] fp32; gamma [hidden] fp32; hidden % 4 == 0. */
 int moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden,
                 float* n_out, void* stream);
 
-/* A9 residual: r[i] += d[i] for i < n (fp32). */
+/* Residual add: r[i] += d[i] for i < n (fp32). */
 int moe_residual_add(float* r, const float* d, int64_t n, void* stream);
 
 /*
- * A10 -- a stack of n_layers pre-norm MoE layers on one residual stream:
+ * Stack -- a stack of n_layers pre-norm MoE layers on one residual stream:
  *   r = upcast(x); for each layer l: r = r + MoE_l(RMSNorm_l(r))
  * Host arrays of n_layers device pointers give each layer's packed codes,
  * packed scales, router weights (and optional biases, NULL array or NULL
@@ -228,7 +229,7 @@ int moe_mxfp4_stack_forward(const moe_layer_desc* desc, int32_t n_layers,
                             size_t workspace_bytes, void* stream);
 
 /*
- * A10 graph form: capture moe_mxfp4_stack_forward once into a HIP graph and
+ * Stack, graph form: capture moe_mxfp4_stack_forward once into a HIP graph and
  * replay it.  The graph binds the pointers given at creation; a replay
  * recomputes the stack from the current contents of x and the weights.
  * moe_stack_graph_create returns an opaque handle in *graph (free it with

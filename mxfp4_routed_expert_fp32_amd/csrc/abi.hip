@@ -119,7 +119,7 @@ hipError_t router(const moe_layer_desc* d, const void* x, bool x_f32, const floa
   return moe::launch_router_logits(x, x_f32, wr, bias, T, d->hidden, d->n_experts, logits, s);
 }
 
-// A5..A9 given routing (idx, w on the device).  For one token the pairs are
+// Expert part of the layer given the routing (idx, w on the device).  For one token the pairs are
 // the k ranks of that token and idx itself is the pair -> expert map.
 int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_t* idx, const float* w,
                 const void* codes, const void* scales, int32_t T, int32_t k, float* out,
@@ -382,7 +382,7 @@ int moe_residual_add(float* r, const float* dlt, int64_t n, void* stream) {
   return dev(moe::launch_residual_add(r, dlt, (size_t)n, as_stream(stream)));
 }
 
-// ---------------------------------------------------------------- stack (A10)
+// ---------------------------------------------------------------- layer stack + graph
 
 static int stack_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L, size_t* nbuf_off,
                         size_t* total) {

@@ -57,7 +57,7 @@ def run_forward(desc, w, x, wr, bias, codes, scales, k):
     return out.cpu().numpy(), logits.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()
 
 
-# ------------------------------------------------------------------ A6 dequant
+# ------------------------------------------------------------------ dequant
 
 def test_dequant_enumeration_bitexact():
     """Gate matrix [32][256]: block (r, b) has scale byte 8r + b, codes 0..15 twice."""
@@ -97,7 +97,7 @@ def test_dequant_real_shape_bitexact():
             assert np.array_equal(P.bits(out.cpu().numpy()), P.bits(ref)), (e, m)
 
 
-# ------------------------------------------------------------------ A2..A4 routing
+# ------------------------------------------------------------------ routing
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (64, 896, 16), (33, 300, 7), (5, 64, 64), (3, 4096, 16)])
 def test_topk_softmax_given_logits(T, E, k):
@@ -217,7 +217,7 @@ def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
 
 
 def test_experts_entry_with_given_routing():
-    """A5..A9 on constructed routes: every token on the same experts, reversed rank order."""
+    """Expert part on constructed routes: every token on the same experts, reversed rank order."""
     w = synth.Workload("r", 61, 5, 256, 128, 8, 3, "f32", weight_seed=7300)
     c, s, ex = experts_host(w)
     desc, codes, scales = pack_whole(w, c, s)
