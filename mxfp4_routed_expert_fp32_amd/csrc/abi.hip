@@ -130,7 +130,11 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  if (T > 1 && !x_f32 && H % 128 == 0 && I % 128 == 0) {
+  // The grouped GEMMs address activations with 32-bit buffer offsets and an
+  // out-of-range sentinel at 1 GiB: x and the two bf16 terms of h must each
+  // stay below that.
+  const bool mfma_fits = (size_t)T * H * 2 < (1u << 30) && (size_t)P * I * 4 < (1u << 30);
+  if (T > 1 && !x_f32 && H % 128 == 0 && I % 128 == 0 && mfma_fits) {
     // prefill form: sort pairs by expert, grouped GEMMs on MFMA, combine
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
@@ -139,8 +143,8 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
     uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][P][I] bf16, same bytes as h
     MOE_TRY(dev(moe::launch_sort_by_expert(idx, T, E, k, offsets, pairs, s)));
     MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, blocks, nblocks, s)));
-    MOE_TRY(dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), pairs, blocks, nblocks, L.max_blocks, c, sc,
-                                        H, I, k, P, hterm, s)));
+    MOE_TRY(dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), T, pairs, blocks, nblocks, L.max_blocks, c,
+                                        sc, H, I, k, P, hterm, s)));
     MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, P, y, s)));
     MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
     return MOE_OK;

@@ -127,7 +127,6 @@ __device__ __forceinline__ void stage_store(const AStage& a, uint16_t* lds) {
 }
 
 constexpr int kTile = kMB * kLdsRow;  // bf16 elements of one LDS activation tile
-constexpr int kDB = 4;                // weight chunks in flight (ring)
 
 // One chunk of one weight row for a lane: 16 code bytes + the block's scale.
 struct BChunk {
@@ -137,223 +136,413 @@ struct BChunk {
 
 __device__ __forceinline__ BChunk load_bchunk(rsrc_t rc, rsrc_t rs, uint32_t boff, uint32_t soff, int c, bool ok) {
   BChunk b;
-  b.q = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)c * 64u : 0x80000000u, 0, 2);
+  // Normal cache policy, not streaming: a row's 128-byte line is split across
+  // two consecutive chunks and the second half must still hit in L2.
+  b.q = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)c * 64u : 0x80000000u, 0, 0);
   b.s = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? soff + (uint32_t)c * 4u : 0x80000000u, 0, 0);
   return b;
 }
 
-// ---------------------------------------------------------------- gate/up + SwiGLU
-// Row tile = 128 rows of gate and the same 128 rows of up; wave w (of 8) owns
-// rows 16w .. 16w+15 of the tile in both matrices.  Per K chunk: weights of
-// chunk c+3 are requested, the activations of chunk c+1 move global -> regs ->
-// LDS (double buffer), chunk c is multiplied, one barrier.  Output: h as two
-// bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo, for each pair p.
-constexpr int kGU_NT = 128;
+// ---------------------------------------------------------------- grouped GEMM pipeline
+// Both expert kernels run 8 waves (two per SIMD, so one covers the other's
+// waits) over one expert block (<= 128 pairs, MT m-tiles of 16) times one
+// tile of output rows.  Wave layout, picked once per workgroup from MT:
+//   small blocks (MT <= 2): wave w owns 2 n-tiles (16-row tiles of output)
+//     and every m-tile;
+//   large blocks: wave w owns 4 n-tiles (row group w % 4) and half of the
+//     m-tiles (w / 4), so each activation fragment read from LDS feeds four
+//     MFMAs and the accumulators stay within one wave's registers.
+// Per K chunk c (128 wide):
+//   1. activation rows are requested into registers, for chunk c+2 (A2) or
+//      chunk c+1;
+//   2. the weights of chunk c+DB-1 are requested (register ring, DB chunks);
+//   3. chunk c is multiplied: weights decoded to bf16 (exact), activation
+//      fragments read from LDS buffer c % 2 one MFMA step ahead;
+//   4. the activation rows of chunk c+1 are written to LDS buffer (c+1) % 2
+//      (last read in chunk c-1, before the previous barrier);
+//   5. one barrier.
+// Every load is an unconditional raw buffer load; rows past the block and
+// chunks past K use an out-of-range offset and read 0, so the loop has no
+// data-dependent branch and the compiler can count loads in flight exactly.
+constexpr int kThr = 512;           // threads per workgroup (8 waves)
+constexpr uint32_t kOOB = 0x80000000u;
 
-__global__ __launch_bounds__(kThreads, 1) void k_gateup_mfma(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
-    const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int H, int I, int k, int P, int ntiles,
-    uint16_t* __restrict__ hterm) {
-  extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
-  __shared__ int32_t tok[kMB], pid[kMB];
-  int eb, nt;
-  decode_item(ntiles, &eb, &nt);
-  if (eb >= *nblocks) return;
-  const int4 blk = blocks[eb];
-  const int e = blk.x, cnt = blk.z;
-  for (int i = threadIdx.x; i < kMB; i += kThreads) {
-    const int p = i < cnt ? pairs[blk.y + i] : -1;
-    pid[i] = p;
-    tok[i] = p >= 0 ? p / k : -1;
+// Rows of a chunk staged per thread: pieces q = t + 512 v (v < NV), row q/16,
+// piece q%16 (16 bytes).  aoff[v] = byte offset of that piece at K origin
+// (row base + 16 * piece), or kFar for a row past the block; `kbyte` = byte
+// offset of the chunk in the row, or kFar for a chunk past K.  Activation
+// buffers are smaller than kFar bytes, so any sum involving kFar is out of
+// range (reads 0) and no sum wraps.
+constexpr uint32_t kFar = 0x40000000u;
+
+template <int NV>
+struct ARegs {
+  u32x4 v[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ void a_offsets(uint32_t* aoff, const uint32_t* row_base) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int q = threadIdx.x + kThr * v;
+    aoff[v] = row_base[q >> 4] + (uint32_t)(q & 15) * 16u;
   }
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const int nl = lane % 16, g = lane / 16;
-  const int mtiles = (cnt + 15) / 16;
+}
+
+template <int NV>
+__device__ __forceinline__ void a_fetch(ARegs<NV>& a, rsrc_t r, const uint32_t* aoff, uint32_t kbyte) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) a.v[v] = __builtin_amdgcn_raw_buffer_load_b128(r, aoff[v] + kbyte, 0, 0);
+}
+
+template <int NV>
+__device__ __forceinline__ void a_put(const ARegs<NV>& a, uint16_t* buf) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int q = threadIdx.x + kThr * v;
+    *reinterpret_cast<u32x4*>(buf + (q >> 4) * kLdsRow + (q & 15) * 8) = a.v[v];
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* buf, int row, int col) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(buf + row * kLdsRow + col));
+}
+
+// Shape of one block's work for a given m-tile count.
+template <int MT>
+struct Shape {
+  static constexpr bool kSmall = MT <= 2;
+  static constexpr int NT = kSmall ? 2 : 4;                 // n-tiles per wave
+  static constexpr int MW = kSmall ? MT : (MT + 1) / 2;     // m-tiles per wave
+  static constexpr int MS = kSmall ? 2 : 2 * MW;            // m-tiles staged (rows past the block read 0)
+  static constexpr int NV = MS * 16 * 16 / kThr;            // 16-byte pieces per thread per chunk and term
+};
+
+// ---------------------------------------------------------------- gate/up + SwiGLU
+// Row tile = 128 rows of gate and the same 128 rows of up.
+//   small: wave w, n-tile 0 = gate rows 16w + 0..15, n-tile 1 = the same up rows;
+//   large: row group r = w % 4, n-tiles 0, 1 = gate rows 32r + 0..15, 16..31,
+//          n-tiles 2, 3 = the same up rows.
+// Output: h as two bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo.
+constexpr int kGU_NT = 128;
+constexpr int kGU_DB = 4;
+
+template <int MT>
+__device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
+                                             const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                             const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
+                                             uint16_t* __restrict__ hterm) {
+  using S = Shape<MT>;
+  constexpr int NT = S::NT, MW = S::MW, NV = S::NV, DB = kGU_DB;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int m0 = S::kSmall ? 0 : (wid >> 2) * MW;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t rcg = mk_rsrc(codes + (size_t)e * cb, mc), rcu = mk_rsrc(codes + (size_t)e * cb + mc, mc);
   const rsrc_t rsg = mk_rsrc(scales + (size_t)e * sb, ms), rsu = mk_rsrc(scales + (size_t)e * sb + ms, ms);
   const int nb = H / 32;
-  const int row = nt * kGU_NT + wid * 16 + nl;
-  const bool rok = row < I;
-  const uint32_t boff = (uint32_t)row * (uint32_t)(nb * 16) + 16u * g;
-  const uint32_t soff = (uint32_t)row * (uint32_t)nb + g;
-  const int nchunks = H / kKC;
-  BChunk rg[kDB], ru[kDB];
+  constexpr int NR = NT / 2;  // rows per matrix per lane
+  int row[NR];
+  uint32_t boff[NR], soff[NR];
 #pragma unroll
-  for (int d = 0; d < kDB - 1; ++d) {
-    rg[d] = load_bchunk(rcg, rsg, boff, soff, d, rok && d < nchunks);
-    ru[d] = load_bchunk(rcu, rsu, boff, soff, d, rok && d < nchunks);
+  for (int j = 0; j < NR; ++j) {
+    row[j] = nt * kGU_NT + (S::kSmall ? wid * 16 : (wid & 3) * 32 + 16 * j) + nl;
+    const bool ok = row[j] < I;
+    boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nb * 16) + 16u * g : kOOB;
+    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nb + g : kOOB;
   }
-  __syncthreads();  // tok[] ready
-  AStage st;
-  stage_load(st, x, (size_t)H, tok, cnt, 0);
-  stage_store(st, a_lds);
+  const int nchunks = H / kKC;
+  uint16_t* buf0 = lds;
+  uint16_t* buf1 = lds + kTile;
+
+  // n-tile j < NR: gate row j; NR + j: up row j
+  BChunk rb[DB][NT];
+  auto bfetch = [&](BChunk* dst, int c) {
+    const bool ok = c < nchunks;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      dst[j] = load_bchunk(rcg, rsg, boff[j], soff[j], c, ok);
+      dst[NR + j] = load_bchunk(rcu, rsu, boff[j], soff[j], c, ok);
+    }
+  };
+  uint32_t aoff[NV];
+  a_offsets<NV>(aoff, row_base);
+  ARegs<NV> s0, s1;
+  a_fetch<NV>(s0, rx, aoff, 0);
+  a_fetch<NV>(s1, rx, aoff, nchunks > 1 ? kKC * 2 : kFar);
+#pragma unroll
+  for (int d = 0; d < DB - 1; ++d) bfetch(rb[d], d);
+  a_put<NV>(s0, buf0);
   __syncthreads();
 
-  f32x4 acc[8][2];
+  f32x4 acc[MW][NT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < nchunks; c0 += kDB) {
+  for (int c0 = 0; c0 < nchunks; c0 += DB) {
 #pragma unroll
-    for (int d = 0; d < kDB; ++d) {
+    for (int d = 0; d < DB; ++d) {
       const int c = c0 + d;
-      if (c >= nchunks) break;
-      const int cn = c + kDB - 1;
-      rg[(d + kDB - 1) % kDB] = load_bchunk(rcg, rsg, boff, soff, cn, rok && cn < nchunks);
-      ru[(d + kDB - 1) % kDB] = load_bchunk(rcu, rsu, boff, soff, cn, rok && cn < nchunks);
-      const bool more = c + 1 < nchunks;
-      if (more) stage_load(st, x, (size_t)H, tok, cnt, (c + 1) * kKC);
-      const uint16_t* A = a_lds + (d % 2) * kTile;
-      const float sg = e8m0_operand(rg[d].s), su = e8m0_operand(ru[d].s);
+      const uint32_t kb2 = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
+      if (d % 2 == 0)
+        a_fetch<NV>(s0, rx, aoff, kb2);
+      else
+        a_fetch<NV>(s1, rx, aoff, kb2);
+      bfetch(rb[(d + DB - 1) % DB], c + DB - 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+      const uint16_t* A = (d % 2 == 0) ? buf0 : buf1;
+      float sc[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) sc[j] = e8m0_operand(rb[d][j].s);
+      bf16x8 fa[2][MW];
+#pragma unroll
+      for (int m = 0; m < MW; ++m) fa[0][m] = lds_frag(A, (m0 + m) * 16 + nl, 32 * g);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 bg = decode8(rg[d].q[s], sg), bu = decode8(ru[d].q[s], su);
+        if (s < 3) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          if (m < mtiles) {
-            const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(A + (m * 16 + nl) * kLdsRow + 32 * g + 8 * s));
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bg, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bu, acc[m][1], 0, 0, 0);
-          }
+          for (int m = 0; m < MW; ++m) fa[(s + 1) & 1][m] = lds_frag(A, (m0 + m) * 16 + nl, 32 * g + 8 * (s + 1));
         }
+        bf16x8 bt[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) bt[j] = decode8(rb[d][j].q[s], sc[j]);
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bt[j], acc[m][j], 0, 0, 0);
       }
-      if (more) stage_store(st, a_lds + ((d + 1) % 2) * kTile);
+      // activations of chunk c+1 (fetched one chunk ago) into the other buffer
+      if (d % 2 == 0)
+        a_put<NV>(s1, buf1);
+      else
+        a_put<NV>(s0, buf0);
       __syncthreads();
     }
   }
-  // epilogue: h = silu(g) * u; lane holds row `row` for tokens 4g..4g+3 of each m-tile
+  // lane holds rows row[j] for slots (m0 + m)*16 + 4g + r
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m < mtiles) {
+  for (int m = 0; m < MW; ++m) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int slot = m * 16 + 4 * g + r;
-        const int p = slot < cnt ? pid[slot] : -1;
-        if (p >= 0 && rok) {
-          const float h = silu_mul(acc[m][0][r], acc[m][1][r]);
-          const uint16_t hi = f32_to_bf16_rne(h);
-          const uint16_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
-          hterm[(size_t)p * I + row] = hi;
-          hterm[(size_t)P * I + (size_t)p * I + row] = lo;
+    for (int r = 0; r < 4; ++r) {
+      const int p = pid[(m0 + m) * 16 + 4 * g + r];
+      if (p >= 0) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          if (row[j] < I) {
+            const float h = silu_mul(acc[m][j][r], acc[m][NR + j][r]);
+            const uint16_t hi = f32_to_bf16_rne(h);
+            const uint16_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
+            hterm[(size_t)p * I + row[j]] = hi;
+            hterm[(size_t)P * I + (size_t)p * I + row[j]] = lo;
+          }
         }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- down
-// Row tile = 256 rows of Wd [H][I]; wave w (of 8) owns rows 32w .. 32w+31
-// (two n-tiles).  A = the two bf16 terms of h for the block's pairs, both
-// staged in LDS (double buffered); each MFMA step runs once per term into the
-// same accumulator.  Output y[p][n] (fp32).
-constexpr int kDN_NT = 256;
-
-__global__ __launch_bounds__(kThreads, 1) void k_down_mfma(
-    const uint16_t* __restrict__ hterm, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
+__global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int H, int I, int P, int ntiles, float* __restrict__ ybuf) {
-  extern __shared__ uint16_t a_lds[];  // [2 buffers][2 terms][kMB][kLdsRow]
+    const uint8_t* __restrict__ scales, int T, int H, int I, int k, int P, int ntiles,
+    uint16_t* __restrict__ hterm) {
+  extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
   __shared__ int32_t pid[kMB];
+  __shared__ uint32_t row_base[kMB];
   int eb, nt;
   decode_item(ntiles, &eb, &nt);
   if (eb >= *nblocks) return;
   const int4 blk = blocks[eb];
   const int e = blk.x, cnt = blk.z;
-  for (int i = threadIdx.x; i < kMB; i += kThreads) pid[i] = i < cnt ? pairs[blk.y + i] : -1;
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const int nl = lane % 16, g = lane / 16;
-  const int mtiles = (cnt + 15) / 16;
+  for (int i = threadIdx.x; i < kMB; i += kThr) {
+    const int p = i < cnt ? pairs[blk.y + i] : -1;
+    pid[i] = p;
+    row_base[i] = p >= 0 ? (uint32_t)(p / k) * (uint32_t)(H * 2) : kFar;
+  }
+  __syncthreads();
+  const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
+  switch ((cnt + 15) / 16) {
+    case 1: gateup_block<1>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 2: gateup_block<2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 3: gateup_block<3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 4: gateup_block<4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 5: gateup_block<5>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 6: gateup_block<6>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 7: gateup_block<7>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    default: gateup_block<8>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+  }
+}
+
+// ---------------------------------------------------------------- down
+// Row tile = 256 rows of Wd [H][I].
+//   small: wave w owns rows 32w + 0..15, 16..31 (2 n-tiles);
+//   large: row group r = w % 4 owns rows 64r .. 64r+63 (4 n-tiles).
+// The activations are the two bf16 terms of h for the block's pairs; each
+// MFMA step runs once per term into the same accumulator.  Small blocks keep
+// a 4-deep weight ring and fetch activations two chunks ahead; large blocks,
+// whose chunk of multiplies outlasts a load, use a 2-deep ring and one chunk
+// ahead to leave registers for the accumulators.  Output y[p][n] (fp32).
+constexpr int kDN_NT = 256;
+
+template <int MT>
+__device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, rsrc_t rh,
+                                           const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                           const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
+                                           float* __restrict__ ybuf) {
+  using S = Shape<MT>;
+  constexpr int NT = S::NT, MW = S::MW, NV = S::NV;
+  constexpr bool A2 = S::kSmall;
+  constexpr int DB = S::kSmall ? 4 : 2;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int m0 = S::kSmall ? 0 : (wid >> 2) * MW;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t rc = mk_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
   const rsrc_t rs = mk_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
   const int nbk = I / 32;
-  int rows[2];
-  bool rok[2];
-  uint32_t boff[2], soff[2];
+  int row[NT];
+  uint32_t boff[NT], soff[NT];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    rows[j] = nt * kDN_NT + wid * 32 + 16 * j + nl;
-    rok[j] = rows[j] < H;
-    boff[j] = (uint32_t)rows[j] * (uint32_t)(nbk * 16) + 16u * g;
-    soff[j] = (uint32_t)rows[j] * (uint32_t)nbk + g;
+  for (int j = 0; j < NT; ++j) {
+    row[j] = nt * kDN_NT + (S::kSmall ? wid * 32 : (wid & 3) * 64) + 16 * j + nl;
+    const bool ok = row[j] < H;
+    boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nbk * 16) + 16u * g : kOOB;
+    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nbk + g : kOOB;
   }
   const int nchunks = I / kKC;
-  BChunk rb[kDB][2];
+  const uint32_t lo_off = (uint32_t)((size_t)P * I * 2);  // byte offset of the lo term
+  // LDS: buffer b, term t at lds + (2b + t) * kTile
+  BChunk rb[DB][NT];
+  auto bfetch = [&](BChunk* dst, int c) {
+    const bool ok = c < nchunks;
 #pragma unroll
-  for (int d = 0; d < kDB - 1; ++d)
+    for (int j = 0; j < NT; ++j) dst[j] = load_bchunk(rc, rs, boff[j], soff[j], c, ok);
+  };
+  uint32_t aoff[NV];
+  a_offsets<NV>(aoff, row_base);
+  ARegs<NV> h0, l0, h1, l1;
+  a_fetch<NV>(h0, rh, aoff, 0);
+  a_fetch<NV>(l0, rh, aoff, lo_off);
+  if (A2) {
+    const uint32_t kb1 = nchunks > 1 ? kKC * 2 : kFar;
+    a_fetch<NV>(h1, rh, aoff, kb1);
+    a_fetch<NV>(l1, rh, aoff, lo_off + kb1);
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) rb[d][j] = load_bchunk(rc, rs, boff[j], soff[j], d, rok[j] && d < nchunks);
-  __syncthreads();  // pid[] ready
-  const uint16_t* hlo = hterm + (size_t)P * I;
-  AStage sh, sl;
-  stage_load(sh, hterm, (size_t)I, pid, cnt, 0);
-  stage_load(sl, hlo, (size_t)I, pid, cnt, 0);
-  stage_store(sh, a_lds);
-  stage_store(sl, a_lds + kTile);
+  for (int d = 0; d < DB - 1; ++d) bfetch(rb[d], d);
+  a_put<NV>(h0, lds);
+  a_put<NV>(l0, lds + kTile);
   __syncthreads();
 
-  f32x4 acc[8][2];
+  f32x4 acc[MW][NT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < nchunks; c0 += kDB) {
+  for (int c0 = 0; c0 < nchunks; c0 += DB) {
 #pragma unroll
-    for (int d = 0; d < kDB; ++d) {
+    for (int d = 0; d < DB; ++d) {
       const int c = c0 + d;
-      if (c >= nchunks) break;
-      const int cn = c + kDB - 1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        rb[(d + kDB - 1) % kDB][j] = load_bchunk(rc, rs, boff[j], soff[j], cn, rok[j] && cn < nchunks);
-      const bool more = c + 1 < nchunks;
-      if (more) {
-        stage_load(sh, hterm, (size_t)I, pid, cnt, (c + 1) * kKC);
-        stage_load(sl, hlo, (size_t)I, pid, cnt, (c + 1) * kKC);
+      if (A2) {
+        const uint32_t kb2 = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
+        if (d % 2 == 0) {
+          a_fetch<NV>(h0, rh, aoff, kb2);
+          a_fetch<NV>(l0, rh, aoff, lo_off + kb2);
+        } else {
+          a_fetch<NV>(h1, rh, aoff, kb2);
+          a_fetch<NV>(l1, rh, aoff, lo_off + kb2);
+        }
+      } else {
+        const uint32_t kb1 = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
+        a_fetch<NV>(h0, rh, aoff, kb1);
+        a_fetch<NV>(l0, rh, aoff, lo_off + kb1);
       }
-      const uint16_t* Ah = a_lds + (d % 2) * 2 * kTile;
+      bfetch(rb[(d + DB - 1) % DB], c + DB - 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+      const uint16_t* Ah = lds + (d % 2) * 2 * kTile;
       const uint16_t* Al = Ah + kTile;
-      const float s0 = e8m0_operand(rb[d][0].s), s1 = e8m0_operand(rb[d][1].s);
+      float sc[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) sc[j] = e8m0_operand(rb[d][j].s);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 b0 = decode8(rb[d][0].q[s], s0), b1 = decode8(rb[d][1].q[s], s1);
+        bf16x8 bt[NT];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          if (m < mtiles) {
-            const int off = (m * 16 + nl) * kLdsRow + 32 * g + 8 * s;
-            const bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(Ah + off));
-            const bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(Al + off));
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b0, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b1, acc[m][1], 0, 0, 0);
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b0, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b1, acc[m][1], 0, 0, 0);
+        for (int j = 0; j < NT; ++j) bt[j] = decode8(rb[d][j].q[s], sc[j]);
+        bf16x8 fh[MW], fl[MW];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+          fh[m] = lds_frag(Ah, (m0 + m) * 16 + nl, 32 * g + 8 * s);
+          fl[m] = lds_frag(Al, (m0 + m) * 16 + nl, 32 * g + 8 * s);
+        }
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh[m], bt[j], acc[m][j], 0, 0, 0);
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[m], bt[j], acc[m][j], 0, 0, 0);
           }
         }
       }
-      if (more) {
-        uint16_t* nxt = a_lds + ((d + 1) % 2) * 2 * kTile;
-        stage_store(sh, nxt);
-        stage_store(sl, nxt + kTile);
+      uint16_t* nxt = lds + ((d + 1) % 2) * 2 * kTile;
+      if (!A2 || d % 2 == 1) {
+        a_put<NV>(h0, nxt);
+        a_put<NV>(l0, nxt + kTile);
+      } else {
+        a_put<NV>(h1, nxt);
+        a_put<NV>(l1, nxt + kTile);
       }
       __syncthreads();
     }
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m < mtiles) {
+  for (int m = 0; m < MW; ++m) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int r = 0; r < 4; ++r) {
+      const int p = pid[(m0 + m) * 16 + 4 * g + r];
+      if (p >= 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int slot = m * 16 + 4 * g + r;
-          const int p = slot < cnt ? pid[slot] : -1;
-          if (p >= 0 && rok[j]) ybuf[(size_t)p * H + rows[j]] = acc[m][j][r];
-        }
+        for (int j = 0; j < NT; ++j)
+          if (row[j] < H) ybuf[(size_t)p * H + row[j]] = acc[m][j][r];
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(kThr, 1) void k_down_mfma(
+    const uint16_t* __restrict__ hterm, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
+    const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, int H, int I, int P, int ntiles, float* __restrict__ ybuf) {
+  extern __shared__ uint16_t a_lds[];  // [2 buffers][2 terms][kMB][kLdsRow]
+  __shared__ int32_t pid[kMB];
+  __shared__ uint32_t row_base[kMB];
+  int eb, nt;
+  decode_item(ntiles, &eb, &nt);
+  if (eb >= *nblocks) return;
+  const int4 blk = blocks[eb];
+  const int e = blk.x, cnt = blk.z;
+  for (int i = threadIdx.x; i < kMB; i += kThr) {
+    const int p = i < cnt ? pairs[blk.y + i] : -1;
+    pid[i] = p;
+    row_base[i] = p >= 0 ? (uint32_t)p * (uint32_t)(I * 2) : kFar;
+  }
+  __syncthreads();
+  const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
+  switch ((cnt + 15) / 16) {
+    case 1: down_block<1>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 2: down_block<2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 3: down_block<3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 4: down_block<4>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 5: down_block<5>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 6: down_block<6>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 7: down_block<7>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    default: down_block<8>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
   }
 }
 
@@ -475,13 +664,13 @@ static unsigned items_grid(int max_blocks, int ntiles) {
   return (unsigned)rounds * 8u * (unsigned)ntiles;
 }
 
-hipError_t launch_gateup_mfma(const uint16_t* x, const int32_t* pairs, const int4* blocks, const int32_t* nblocks,
-                              int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int k,
-                              int P, uint16_t* hterm, hipStream_t s) {
+hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
+                              const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
+                              int H, int I, int k, int P, uint16_t* hterm, hipStream_t s) {
   const int ntiles = (I + kGU_NT - 1) / kGU_NT;
   const size_t lds = (size_t)2 * kTile * 2;
-  k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThreads, lds, s>>>(x, pairs, blocks, nblocks, codes,
-                                                                             scales, H, I, k, P, ntiles, hterm);
+  k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(x, pairs, blocks, nblocks, codes, scales,
+                                                                         T, H, I, k, P, ntiles, hterm);
   return hipGetLastError();
 }
 
@@ -490,8 +679,8 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             float* ybuf, hipStream_t s) {
   const int ntiles = (H + kDN_NT - 1) / kDN_NT;
   const size_t lds = (size_t)4 * kTile * 2;
-  k_down_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThreads, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
-                                                                           scales, H, I, P, ntiles, ybuf);
+  k_down_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
+                                                                       scales, H, I, P, ntiles, ybuf);
   return hipGetLastError();
 }
 
