@@ -196,6 +196,37 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
                        int32_t* expert_offsets, int32_t* pair_list, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill form, stage by stage: the kernels moe_mxfp4_forward runs for more
+ * than one bf16 token when H and I are multiples of 128 (the grouped GEMMs on
+ * bf16 MFMA), for stage-level checks and timing.  After moe_sort_by_expert:
+ *  - moe_max_expert_blocks: capacity of the block list for n_pairs pairs,
+ *    ceil(n_pairs / 128) + min(n_pairs, n_experts).
+ *  - moe_expert_blocks: cut each expert's sorted pairs into blocks of at most
+ *    128: blocks [max_blocks][4] int32 {expert, first index into pair_list,
+ *    pair count, 0} (16-byte aligned), n_blocks [1] int32 on the device.
+ *    max_blocks below the capacity is MOE_ERR_WORKSPACE.
+ *  - moe_mxfp4_grouped_gate_up: x bf16 [n_tokens][H]; pair p = t*k + j reads
+ *    token t = p / k.  hterm [2][n_tokens*k][I] bf16 receives h = silu(g) * u
+ *    as two terms, hterm[0] = bf16(h) and hterm[1] = bf16(h - hterm[0]) (both
+ *    round to nearest even), for every pair named by a block.
+ *  - moe_mxfp4_grouped_down: y [n_pairs][H] fp32, y[p] = Wd . (hterm[0][p] +
+ *    hterm[1][p]), for every pair named by a block.
+ * Blocks that do not name a valid expert and pair range, and pair ids outside
+ * [0, n_pairs), are skipped on the device.  MOE_ERR_UNSUPPORTED if H or I is
+ * not a multiple of 128 or x or hterm reaches 1 GiB.
+ */
+int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks);
+int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,
+                      int32_t max_blocks, int32_t* n_blocks, void* stream);
+int moe_mxfp4_grouped_gate_up(const moe_layer_desc* desc, const void* x, int32_t n_tokens, int32_t k,
+                              const int32_t* pair_list, const int32_t* blocks, const int32_t* n_blocks,
+                              int32_t max_blocks, const void* packed_codes, const void* packed_scales, void* hterm,
+                              void* stream);
+int moe_mxfp4_grouped_down(const moe_layer_desc* desc, const void* hterm, int32_t n_pairs, const int32_t* pair_list,
+                           const int32_t* blocks, const int32_t* n_blocks, int32_t max_blocks,
+                           const void* packed_codes, const void* packed_scales, float* y, void* stream);
+
 /* Dequantisation alone: dequantise one matrix of one expert from the device layout to
  * fp32, exactly: out = E2M1(code) * 2^(scale - 127), subnormals kept, +-inf on
  * overflow, scale byte 0xFF -> NaN 0x7FC00000.  matrix 0 = gate [I][H],

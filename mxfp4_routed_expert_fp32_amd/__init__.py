@@ -29,6 +29,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_mxfp4_pack", "moe_mxfp4_forward", "moe_mxfp4_experts",
     "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_combine",
     "moe_router_logits", "moe_topk_softmax", "moe_sort_workspace_bytes", "moe_sort_by_expert",
+    "moe_max_expert_blocks", "moe_expert_blocks", "moe_mxfp4_grouped_gate_up", "moe_mxfp4_grouped_down",
     "moe_mxfp4_dequant", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_bytes",
     "moe_mxfp4_stack_forward", "moe_stack_graph_create", "moe_stack_graph_launch",
     "moe_stack_graph_destroy",
@@ -85,6 +86,10 @@ def lib():
                 "moe_topk_softmax": ([vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
                 "moe_sort_workspace_bytes": ([i32, i32, i32, P(sz)], ctypes.c_int),
                 "moe_sort_by_expert": ([vp, i32, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+                "moe_max_expert_blocks": ([i32, i32, P(i32)], ctypes.c_int),
+                "moe_expert_blocks": ([vp, i32, i32, vp, i32, vp, vp], ctypes.c_int),
+                "moe_mxfp4_grouped_gate_up": ([D, vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
+                "moe_mxfp4_grouped_down": ([D, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_dequant": ([D, vp, vp, i64, i32, vp, vp], ctypes.c_int),
                 "moe_rmsnorm": ([vp, vp, ctypes.c_float, i32, i32, vp, vp], ctypes.c_int),
                 "moe_residual_add": ([vp, vp, i64, vp], ctypes.c_int),
@@ -217,6 +222,34 @@ def moe_sort_by_expert(topk_idx, n_experts, expert_offsets, pair_list, workspace
     _check("moe_sort_by_expert", lib().moe_sort_by_expert(
         _ptr(topk_idx), topk_idx.shape[0], n_experts, topk_idx.shape[1], _ptr(expert_offsets),
         _ptr(pair_list), _ptr(workspace), nb, _stream(stream)))
+
+
+def max_expert_blocks(n_experts: int, n_pairs: int) -> int:
+    m = ctypes.c_int32()
+    _check("moe_max_expert_blocks", lib().moe_max_expert_blocks(n_experts, n_pairs, ctypes.byref(m)))
+    return m.value
+
+
+def moe_expert_blocks(expert_offsets, n_pairs, blocks, n_blocks, stream=None):
+    """blocks: int32 [max_blocks, 4]; n_blocks: int32 [1] (device)."""
+    _check("moe_expert_blocks", lib().moe_expert_blocks(
+        _ptr(expert_offsets), expert_offsets.numel() - 1, n_pairs, _ptr(blocks), blocks.shape[0], _ptr(n_blocks),
+        _stream(stream)))
+
+
+def moe_mxfp4_grouped_gate_up(desc, x, k, pair_list, blocks, n_blocks, packed_codes, packed_scales, hterm,
+                              stream=None):
+    """x: bf16 [T, H]; hterm: bf16 (or int16) [2, T*k, I]."""
+    _check("moe_mxfp4_grouped_gate_up", lib().moe_mxfp4_grouped_gate_up(
+        ctypes.byref(desc), _ptr(x), x.shape[0], k, _ptr(pair_list), _ptr(blocks), _ptr(n_blocks), blocks.shape[0],
+        _ptr(packed_codes), _ptr(packed_scales), _ptr(hterm), _stream(stream)))
+
+
+def moe_mxfp4_grouped_down(desc, hterm, pair_list, blocks, n_blocks, packed_codes, packed_scales, y, stream=None):
+    """hterm: [2, P, I] bf16 terms; y: fp32 [P, H]."""
+    _check("moe_mxfp4_grouped_down", lib().moe_mxfp4_grouped_down(
+        ctypes.byref(desc), _ptr(hterm), pair_list.numel(), _ptr(pair_list), _ptr(blocks), _ptr(n_blocks),
+        blocks.shape[0], _ptr(packed_codes), _ptr(packed_scales), _ptr(y), _stream(stream)))
 
 
 def moe_mxfp4_dequant(desc, packed_codes, packed_scales, expert, matrix, out, stream=None):

@@ -110,6 +110,14 @@ int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
   return MOE_OK;
 }
 
+// The grouped GEMMs tile K by 128 and address activations with 32-bit buffer
+// offsets and an out-of-range sentinel at 1 GiB: x (bf16) and the two bf16
+// terms of h must each stay below that.
+bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
+  return d->hidden % 128 == 0 && d->inter % 128 == 0 && T * d->hidden * 2 < (int64_t{1} << 30) &&
+         P * d->inter * 4 < (int64_t{1} << 30);
+}
+
 // Router logits: many bf16 tokens go to the MFMA kernel (fp32 weights split
 // into three exact bf16 terms), a few tokens or fp32 tokens to the GEMV.
 hipError_t router(const moe_layer_desc* d, const void* x, bool x_f32, const float* wr, const float* bias,
@@ -130,11 +138,7 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  // The grouped GEMMs address activations with 32-bit buffer offsets and an
-  // out-of-range sentinel at 1 GiB: x and the two bf16 terms of h must each
-  // stay below that.
-  const bool mfma_fits = (size_t)T * H * 2 < (1u << 30) && (size_t)P * I * 4 < (1u << 30);
-  if (T > 1 && !x_f32 && H % 128 == 0 && I % 128 == 0 && mfma_fits) {
+  if (T > 1 && !x_f32 && grouped_fits(d, T, P)) {
     // prefill form: sort pairs by expert, grouped GEMMs on MFMA, combine
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
@@ -142,10 +146,10 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
     int32_t* nblocks = reinterpret_cast<int32_t*>(ws + L.nblocks);
     uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][P][I] bf16, same bytes as h
     MOE_TRY(dev(moe::launch_sort_by_expert(idx, T, E, k, offsets, pairs, s)));
-    MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, blocks, nblocks, s)));
+    MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
     MOE_TRY(dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), T, pairs, blocks, nblocks, L.max_blocks, c,
-                                        sc, H, I, k, P, hterm, s)));
-    MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, P, y, s)));
+                                        sc, H, I, E, k, P, hterm, s)));
+    MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, P, y, s)));
     MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
     return MOE_OK;
   }
@@ -354,6 +358,62 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
   if ((int64_t)n_tokens * k > INT32_MAX) return MOE_ERR_OVERFLOW;
   return dev(moe::launch_sort_by_expert(topk_idx, n_tokens, n_experts, k, expert_offsets, pair_list,
                                         as_stream(stream)));
+}
+
+int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks) {
+  if (!max_blocks) return MOE_ERR_NULL;
+  if (n_experts < 1 || n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  *max_blocks = moe::max_expert_blocks(n_pairs, n_experts);
+  return MOE_OK;
+}
+
+int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,
+                      int32_t max_blocks, int32_t* n_blocks, void* stream) {
+  if (!expert_offsets || !blocks || !n_blocks) return MOE_ERR_NULL;
+  if (n_experts < 1 || n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (max_blocks < moe::max_expert_blocks(n_pairs, n_experts)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(blocks)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_expert_blocks(expert_offsets, n_experts, max_blocks, reinterpret_cast<int4*>(blocks),
+                                       n_blocks, as_stream(stream)));
+}
+
+int moe_mxfp4_grouped_gate_up(const moe_layer_desc* d, const void* x, int32_t n_tokens, int32_t k,
+                              const int32_t* pair_list, const int32_t* blocks, const int32_t* n_blocks,
+                              int32_t max_blocks, const void* packed_codes, const void* packed_scales, void* hterm,
+                              void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!x || !pair_list || !blocks || !n_blocks || !packed_codes || !packed_scales || !hterm) return MOE_ERR_NULL;
+  MOE_TRY(check_tokens(n_tokens, k, d));
+  const int64_t P = (int64_t)n_tokens * k;
+  if (!grouped_fits(d, n_tokens, P)) return MOE_ERR_UNSUPPORTED;
+  if (max_blocks < 1) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(blocks) || !aligned16(packed_codes) || !aligned16(packed_scales) ||
+      !aligned16(hterm))
+    return MOE_ERR_ALIGN;
+  return dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), n_tokens, pair_list,
+                                     reinterpret_cast<const int4*>(blocks), n_blocks, max_blocks,
+                                     static_cast<const uint8_t*>(packed_codes),
+                                     static_cast<const uint8_t*>(packed_scales), d->hidden, d->inter, d->n_experts,
+                                     k, (int)P, static_cast<uint16_t*>(hterm), as_stream(stream)));
+}
+
+int moe_mxfp4_grouped_down(const moe_layer_desc* d, const void* hterm, int32_t n_pairs, const int32_t* pair_list,
+                           const int32_t* blocks, const int32_t* n_blocks, int32_t max_blocks,
+                           const void* packed_codes, const void* packed_scales, float* y, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!hterm || !pair_list || !blocks || !n_blocks || !packed_codes || !packed_scales || !y) return MOE_ERR_NULL;
+  if (n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (!grouped_fits(d, 1, n_pairs)) return MOE_ERR_UNSUPPORTED;
+  if (max_blocks < 1) return MOE_ERR_SHAPE;
+  if (!aligned16(hterm) || !aligned16(blocks) || !aligned16(packed_codes) || !aligned16(packed_scales) ||
+      !aligned16(y))
+    return MOE_ERR_ALIGN;
+  return dev(moe::launch_down_mfma(static_cast<const uint16_t*>(hterm), pair_list,
+                                   reinterpret_cast<const int4*>(blocks), n_blocks, max_blocks,
+                                   static_cast<const uint8_t*>(packed_codes), static_cast<const uint8_t*>(packed_scales),
+                                   d->hidden, d->inter, d->n_experts, n_pairs, y, as_stream(stream)));
 }
 
 int moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,

@@ -38,8 +38,9 @@ __device__ __forceinline__ rsrc_t mk_rsrc(const void* base, uint32_t bytes) {
 
 // ---------------------------------------------------------------- expert blocks
 // blocks[b] = {expert, first index into the sorted pair list, pair count, 0};
-// *nblocks = number of blocks.  One workgroup.
-__global__ __launch_bounds__(1024) void k_expert_blocks(const int32_t* __restrict__ offsets, int E,
+// *nblocks = number of blocks (at most max_blocks are written).  One
+// workgroup.
+__global__ __launch_bounds__(1024) void k_expert_blocks(const int32_t* __restrict__ offsets, int E, int max_blocks,
                                                         int4* __restrict__ blocks,
                                                         int32_t* __restrict__ nblocks) {
   __shared__ int32_t part[1024];
@@ -59,9 +60,10 @@ __global__ __launch_bounds__(1024) void k_expert_blocks(const int32_t* __restric
   int32_t b = part[tid] - local;
   for (int e = e0; e < e0 + per && e < E; ++e) {
     const int32_t beg = offsets[e], cnt = offsets[e + 1] - beg;
-    for (int32_t m0 = 0; m0 < cnt; m0 += kMB) blocks[b++] = make_int4(e, beg + m0, min(kMB, cnt - m0), 0);
+    for (int32_t m0 = 0; m0 < cnt; m0 += kMB, ++b)
+      if (b < max_blocks) blocks[b] = make_int4(e, beg + m0, min(kMB, cnt - m0), 0);
   }
-  if (tid == 1023) *nblocks = part[1023];
+  if (tid == 1023) *nblocks = min(part[1023], max_blocks);
 }
 
 // Workgroup -> (expert block, row tile): row tiles of one block on one XCD.
@@ -348,18 +350,20 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
 __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int T, int H, int I, int k, int P, int ntiles,
+    const uint8_t* __restrict__ scales, int T, int H, int I, int E, int k, int P, int max_blocks, int ntiles,
     uint16_t* __restrict__ hterm) {
   extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
   __shared__ int32_t pid[kMB];
   __shared__ uint32_t row_base[kMB];
   int eb, nt;
   decode_item(ntiles, &eb, &nt);
-  if (eb >= *nblocks) return;
+  if (eb >= min(*nblocks, max_blocks)) return;
   const int4 blk = blocks[eb];
   const int e = blk.x, cnt = blk.z;
+  if (e < 0 || e >= E || cnt < 1 || cnt > kMB || blk.y < 0 || blk.y > P - cnt) return;  // malformed block
   for (int i = threadIdx.x; i < kMB; i += kThr) {
-    const int p = i < cnt ? pairs[blk.y + i] : -1;
+    int p = i < cnt ? pairs[blk.y + i] : -1;
+    if (p >= P) p = -1;
     pid[i] = p;
     row_base[i] = p >= 0 ? (uint32_t)(p / k) * (uint32_t)(H * 2) : kFar;
   }
@@ -518,17 +522,20 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
 __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
     const uint16_t* __restrict__ hterm, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int H, int I, int P, int ntiles, float* __restrict__ ybuf) {
+    const uint8_t* __restrict__ scales, int H, int I, int E, int P, int max_blocks, int ntiles,
+    float* __restrict__ ybuf) {
   extern __shared__ uint16_t a_lds[];  // [2 buffers][2 terms][kMB][kLdsRow]
   __shared__ int32_t pid[kMB];
   __shared__ uint32_t row_base[kMB];
   int eb, nt;
   decode_item(ntiles, &eb, &nt);
-  if (eb >= *nblocks) return;
+  if (eb >= min(*nblocks, max_blocks)) return;
   const int4 blk = blocks[eb];
   const int e = blk.x, cnt = blk.z;
+  if (e < 0 || e >= E || cnt < 1 || cnt > kMB || blk.y < 0 || blk.y > P - cnt) return;  // malformed block
   for (int i = threadIdx.x; i < kMB; i += kThr) {
-    const int p = i < cnt ? pairs[blk.y + i] : -1;
+    int p = i < cnt ? pairs[blk.y + i] : -1;
+    if (p >= P) p = -1;
     pid[i] = p;
     row_base[i] = p >= 0 ? (uint32_t)p * (uint32_t)(I * 2) : kFar;
   }
@@ -654,8 +661,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_router_mfma(const uint16_t* __r
 
 int max_expert_blocks(int P, int E) { return (P + kMB - 1) / kMB + (P < E ? P : E); }
 
-hipError_t launch_expert_blocks(const int32_t* offsets, int E, int4* blocks, int32_t* nblocks, hipStream_t s) {
-  k_expert_blocks<<<1, 1024, 0, s>>>(offsets, E, blocks, nblocks);
+hipError_t launch_expert_blocks(const int32_t* offsets, int E, int max_blocks, int4* blocks, int32_t* nblocks,
+                                hipStream_t s) {
+  k_expert_blocks<<<1, 1024, 0, s>>>(offsets, E, max_blocks, blocks, nblocks);
   return hipGetLastError();
 }
 
@@ -666,21 +674,21 @@ static unsigned items_grid(int max_blocks, int ntiles) {
 
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
                               const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
-                              int H, int I, int k, int P, uint16_t* hterm, hipStream_t s) {
+                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s) {
   const int ntiles = (I + kGU_NT - 1) / kGU_NT;
   const size_t lds = (size_t)2 * kTile * 2;
-  k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(x, pairs, blocks, nblocks, codes, scales,
-                                                                         T, H, I, k, P, ntiles, hterm);
+  k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(
+      x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, hterm);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const int4* blocks, const int32_t* nblocks,
-                            int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int P,
+                            int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s) {
   const int ntiles = (H + kDN_NT - 1) / kDN_NT;
   const size_t lds = (size_t)4 * kTile * 2;
   k_down_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
-                                                                       scales, H, I, P, ntiles, ybuf);
+                                                                       scales, H, I, E, P, max_blocks, ntiles, ybuf);
   return hipGetLastError();
 }
 

@@ -27,12 +27,13 @@ hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H
 // at most 128 sorted pairs, gate/up + SwiGLU and down grouped GEMMs on MFMA.
 // hterm holds h as two bf16 terms, [2][P][I].
 int max_expert_blocks(int P, int E);
-hipError_t launch_expert_blocks(const int32_t* offsets, int E, int4* blocks, int32_t* nblocks, hipStream_t s);
+hipError_t launch_expert_blocks(const int32_t* offsets, int E, int max_blocks, int4* blocks, int32_t* nblocks,
+                                hipStream_t s);
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
                               const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
-                              int H, int I, int k, int P, uint16_t* hterm, hipStream_t s);
+                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s);
 hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const int4* blocks, const int32_t* nblocks,
-                            int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int P,
+                            int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s);
 
 // Router logits for many bf16 tokens on MFMA (H a multiple of 128).

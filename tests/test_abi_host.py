@@ -127,3 +127,31 @@ def test_other_entry_points_reject_before_launch():
     assert L.moe_stack_graph_create(ctypes.byref(d), 0, 16, 16, 16, None, 16, ctypes.c_float(1e-6), 16, 1,
                                     1, 16, 16, 16, 1 << 30, None, ctypes.byref(g)) == -2
     assert L.moe_stack_graph_destroy(None) == 0
+
+
+def test_grouped_stage_entry_points_reject_before_launch():
+    L = moe.lib()
+    d = D()
+    m = ctypes.c_int32()
+    assert L.moe_max_expert_blocks(896, 65536, ctypes.byref(m)) == 0
+    assert m.value == 512 + 896
+    assert L.moe_max_expert_blocks(8, 3, ctypes.byref(m)) == 0 and m.value == 1 + 3
+    assert L.moe_max_expert_blocks(0, 3, ctypes.byref(m)) == -2
+    assert L.moe_max_expert_blocks(8, 3, None) == -1
+    # capacity below what the sort can produce
+    assert L.moe_expert_blocks(16, 896, 65536, 16, 1407, 16, None) == -5
+    assert L.moe_expert_blocks(16, 896, 65536, 8, 1408, 16, None) == -4
+    assert L.moe_expert_blocks(None, 896, 65536, 16, 1408, 16, None) == -1
+    args = (16, 4096, 16, 16, 16, 16, 1408, 16, 16, 16, None)
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), None, *args[1:]) == -1
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 4096, 17, *args[3:]) == -2
+    odd = D(hidden=7168 + 32)
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(odd), *args) == -7
+    # x of 40000 x 7168 bf16 tokens reaches 1 GiB
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 40000, 16, *args[3:]) == -7
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 4096, 16, 16, 8, 16, 1408, 16, 16, 16, None) == -4
+    dn = (16, 65536, 16, 16, 16, 1408, 16, 16, 16, None)
+    assert L.moe_mxfp4_grouped_down(ctypes.byref(d), None, *dn[1:]) == -1
+    assert L.moe_mxfp4_grouped_down(ctypes.byref(odd), *dn) == -7
+    assert L.moe_mxfp4_grouped_down(ctypes.byref(d), 16, 0, *dn[2:]) == -2
+    assert L.moe_mxfp4_grouped_down(ctypes.byref(d), 16, 65536, 16, 16, 16, 1408, 16, 16, 24, None) == -4

@@ -297,3 +297,55 @@ def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     P.assert_weights_close(wt, r_w, k)
     err = P.assert_out_close(out, r_out)
     assert err < 1e-5, err
+
+
+def test_grouped_stages_equal_forward_and_skip_malformed_blocks():
+    """The prefill form run stage by stage through its own entry points (sort,
+    expert blocks, grouped gate/up, grouped down, combine) gives the forward's
+    output bit for bit; the block list matches a host recomputation from the
+    sort's offsets; blocks naming no valid expert or pair range are skipped."""
+    H, I, E, k, T = 512, 256, 16, 4, 165
+    w = synth.Workload("gs", 65, T, H, I, E, k, "bf16", weight_seed=7700)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    b = np.zeros(E, np.float32)
+    b[3] = 8.0                                   # expert 3 takes every token: > 128 pairs, two blocks
+    bias = torch.from_numpy(b).to(DEV)
+    out, logits, idx, wt = run_forward(desc, w, x, wr, bias, codes, scales, k)
+    Pn = T * k
+    offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pairs = torch.empty(Pn, dtype=torch.int32, device=DEV)
+    moe.moe_sort_by_expert(torch.from_numpy(idx).to(DEV), E, offs, pairs)
+    mb = moe.max_expert_blocks(E, Pn)
+    blocks = torch.zeros(mb, 4, dtype=torch.int32, device=DEV)
+    nb = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.moe_expert_blocks(offs, Pn, blocks, nb)
+    hterm = torch.empty(2, Pn, I, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(Pn, H, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_grouped_gate_up(desc, x, k, pairs, blocks, nb, codes, scales, hterm)
+    moe.moe_mxfp4_grouped_down(desc, hterm, pairs, blocks, nb, codes, scales, y)
+    o2 = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    moe.moe_combine(y, torch.from_numpy(wt).to(DEV), o2)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.bits(o2.cpu().numpy()), P.bits(out))
+
+    offs_h = offs.cpu().numpy()
+    want = []
+    for e in range(E):
+        for m0 in range(offs_h[e], offs_h[e + 1], 128):
+            want.append([e, m0, min(128, offs_h[e + 1] - m0), 0])
+    n = int(nb.cpu().item())
+    assert n == len(want) and len(want) > E - 1
+    assert np.array_equal(blocks.cpu().numpy()[:n], np.array(want, np.int32))
+
+    bad = torch.tensor([[E, 0, 4, 0], [0, Pn - 2, 4, 0], [1, 0, 0, 0], [-1, 0, 1, 0], [2, 0, 129, 0]],
+                       dtype=torch.int32, device=DEV)
+    nbad = torch.tensor([5], dtype=torch.int32, device=DEV)
+    y2 = torch.full((Pn, H), 7.0, dtype=torch.float32, device=DEV)
+    h2 = torch.full((2, Pn, I), 3.0, dtype=torch.bfloat16, device=DEV)
+    moe.moe_mxfp4_grouped_gate_up(desc, x, k, pairs, bad, nbad, codes, scales, h2)
+    moe.moe_mxfp4_grouped_down(desc, hterm, pairs, bad, nbad, codes, scales, y2)
+    torch.cuda.synchronize()
+    assert bool((y2 == 7.0).all()) and bool((h2 == 3.0).all())
