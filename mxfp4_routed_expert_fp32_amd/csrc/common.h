@@ -47,6 +47,31 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// 8 bf16 weights: dword `dw` of a 16-byte code block (8 codes) times the
+// block scale, exact.
+__device__ __forceinline__ bf16x8 decode8(uint32_t dw, float s) {
+  const bf16x2 a = fp4x2_to_bf16<0>(dw, s), b = fp4x2_to_bf16<1>(dw, s);
+  const bf16x2 c = fp4x2_to_bf16<2>(dw, s), d = fp4x2_to_bf16<3>(dw, s);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+
 // Sum over groups of G consecutive lanes (G a power of two <= 64); every lane
 // of a group ends with the group's sum.  The butterfly order is fixed, so the
 // result is deterministic.

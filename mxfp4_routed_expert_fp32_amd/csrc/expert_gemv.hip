@@ -21,6 +21,7 @@
 // a pair stream neighbouring rows.  Weight loads run ahead of the compute
 // (two rows for gate/up, three row groups for down).
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -53,6 +54,21 @@ static int resident_wgs_query(const void* fn, size_t lds) {
 template <typename F>
 static int resident_wgs(F fn, size_t lds) {
   return resident_wgs_query(reinterpret_cast<const void*>(fn), lds);
+}
+
+// Compute units of the current device (remembered per device).
+static int cu_count() {
+  static std::mutex mu;
+  static std::vector<std::pair<int, int>> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  for (const auto& e : table)
+    if (e.first == dev) return e.second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  table.emplace_back(dev, cus);
+  return cus;
 }
 
 // 32 products of one block: codes q (16 bytes = 32 nibbles), scale operand s,
@@ -305,6 +321,80 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
   }
 }
 
+// ---------------------------------------------------------------- down, K split across waves
+constexpr int kDnKsRing = 4;   // weight steps in flight + 1 (measured best of 2..8)
+constexpr int kDnKsPerCu = 8;  // workgroups per CU the grid aims at (measured best of 2..12)
+// For I = 512*KS (I/32 = 16*KS blocks per row): wave ks of a workgroup takes
+// blocks 16*ks .. 16*ks+15 of every row of the workgroup's row range, 16
+// lanes per row and 4 rows per step (256 contiguous code bytes per row), so a
+// lane keeps one 32-element block of h in registers (32 fp32) instead of
+// three and the kernel runs several waves per SIMD, which lets the weight
+// stream and the conversion + FMA work overlap.  Each wave reduces its 16
+// lanes per row and leaves the partial sum in LDS; at the end the workgroup
+// adds the KS partials of each row in wave order (a fixed order, so results
+// are deterministic).  Weight loads run D-1 steps ahead; rows_per_wg is a
+// multiple of 4*D, so the unrolled ring has no exit inside.
+template <int KS, int D>
+__global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ hbuf,
+                                                     const int32_t* __restrict__ pair_expert,
+                                                     const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int H, int I, int E,
+                                                     int parts, int rows_per_wg, float* __restrict__ ybuf) {
+  extern __shared__ float partial[];  // [rows_per_wg][KS]
+  const int p = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
+  const int lane = threadIdx.x % kWave, ks = threadIdx.x / kWave;
+  const int c = lane % 16, rsub = lane / 16;
+  int e = __builtin_amdgcn_readfirstlane(pair_expert[p]);
+  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  const int nbk = I / 32;
+  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const rsrc_t dcod = make_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
+  const rsrc_t dsc = make_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
+  const int b = ks * 16 + c;  // this lane's block of every row
+  const int r0 = part * rows_per_wg;
+  const int steps = rows_per_wg / 4;
+
+  auto load = [&](RowBlocks<1>& r, int st) {
+    const int n = r0 + 4 * st + rsub;
+    const bool ok = st < steps && n < H;
+    r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(dcod, ok ? (uint32_t)n * (uint32_t)(I / 2) + 16u * b : kOOB, 0, 2);
+    r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 0);
+  };
+  RowBlocks<1> ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) load(ring[d], d);
+  uint32_t hr[1][32];
+  const float4* hp = reinterpret_cast<const float4*>(hbuf + (size_t)p * I + 32 * b);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const float4 f = hp[v];
+    hr[0][4 * v] = __float_as_uint(f.x); hr[0][4 * v + 1] = __float_as_uint(f.y);
+    hr[0][4 * v + 2] = __float_as_uint(f.z); hr[0][4 * v + 3] = __float_as_uint(f.w);
+  }
+
+  for (int s0 = 0; s0 < steps; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int st = s0 + d;
+      load(ring[(d + D - 1) % D], st + D - 1);
+      const float v = lane_group_sum<16>(row_dot<true, 1>(ring[d], hr));
+      if (c == 15) partial[(4 * st + rsub) * KS + ks] = v;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < rows_per_wg; i += 64 * KS) {
+    const int n = r0 + i;
+    if (n < H) {
+      float acc = partial[i * KS];
+#pragma unroll
+      for (int k2 = 1; k2 < KS; ++k2) acc += partial[i * KS + k2];
+      ybuf[(size_t)p * H + n] = acc;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
 // out[t][n] = (resid[t][n] +) sum_j w[t][j] * y[t*k+j][n], j ascending; resid
 // may alias out.  Loads are issued in groups of 8 ranks.
@@ -424,6 +514,23 @@ void down_shape(int nbk, int* lpr, int* nbl2) {
 
 hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
                             const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s) {
+  const int ks = I % 512 == 0 ? I / 512 : 0;
+  if (ks == 2 || ks == 3 || ks == 4 || ks == 6 || ks == 8) {
+    // K split across I/512 waves; about kDnKsPerCu workgroups per CU
+    constexpr int D = kDnKsRing;
+    const int want = (kDnKsPerCu * cu_count() + P - 1) / P;
+    int rows = (H + want - 1) / want;
+    rows = (rows + 4 * D - 1) / (4 * D) * (4 * D);
+    const int parts = (H + rows - 1) / rows;
+    const size_t lds = (size_t)rows * ks * 4;
+    const dim3 grid((unsigned)(P * parts));
+#define MOE_DN_KS(KS)                                                                                     \
+  if (ks == KS)                                                                                            \
+    k_down_ks<KS, D><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E, parts, rows, ybuf);
+    MOE_DN_KS(2) MOE_DN_KS(3) MOE_DN_KS(4) MOE_DN_KS(6) MOE_DN_KS(8)
+#undef MOE_DN_KS
+    return hipGetLastError();
+  }
   int lpr, nbl2;
   down_shape(I / 32, &lpr, &nbl2);
   const size_t lds = (size_t)I * 4;

@@ -73,30 +73,6 @@ __device__ __forceinline__ void decode_item(int ntiles, int* eb, int* nt) {
   *nt = r % ntiles;
 }
 
-// 8 bf16 weights: dword `dw` of a 16-byte code block (8 codes) times the
-// block scale, exact.
-__device__ __forceinline__ bf16x8 decode8(uint32_t dw, float s) {
-  const bf16x2 a = fp4x2_to_bf16<0>(dw, s), b = fp4x2_to_bf16<1>(dw, s);
-  const bf16x2 c = fp4x2_to_bf16<2>(dw, s), d = fp4x2_to_bf16<3>(dw, s);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // Stage rows [0, kMB) x K [k0, k0+kKC) of a bf16 source through registers:
 // thread t of the 512 moves 16-byte pieces q = t + 512*v (row q/16, piece
 // q%16).  Rows past `cnt` (or with a negative source row) are zero.

@@ -200,7 +200,10 @@ def test_forward_tiny_matches_oracle(seed):
 
 @pytest.mark.parametrize("H,I,E,k,T,xd", [(256, 128, 8, 2, 4, "f32"), (96, 64, 16, 4, 3, "bf16"),
                                            (64, 32, 6, 6, 2, "f32"), (512, 96, 33, 5, 7, "bf16"),
-                                           (7168, 1536, 20, 16, 2, "bf16")])
+                                           (7168, 1536, 20, 16, 2, "bf16"),
+                                           # down with K split across I/512 waves, ragged row ranges
+                                           (160, 1024, 5, 2, 1, "f32"), (96, 2048, 6, 3, 3, "f32"),
+                                           (64, 3072, 4, 2, 2, "f32"), (1056, 1536, 9, 4, 1, "bf16")])
 def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
     w = synth.Workload("s", 60, T, H, I, E, k, xd, weight_seed=7100 + H + E)
     c, s, ex = experts_host(w)
