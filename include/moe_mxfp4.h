@@ -198,7 +198,7 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
 
 /*
  * Prefill form, stage by stage: the kernels moe_mxfp4_forward runs for more
- * than one bf16 token when H and I are multiples of 128 (the grouped GEMMs on
+ * than one bf16 token when H and I are multiples of 256 (the grouped GEMMs on
  * bf16 MFMA), for stage-level checks and timing.  After moe_sort_by_expert:
  *  - moe_max_expert_blocks: capacity of the block list for n_pairs pairs,
  *    ceil(n_pairs / 128) + min(n_pairs, n_experts).
@@ -214,7 +214,7 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
  *    hterm[1][p]), for every pair named by a block.
  * Blocks that do not name a valid expert and pair range, and pair ids outside
  * [0, n_pairs), are skipped on the device.  MOE_ERR_UNSUPPORTED if H or I is
- * not a multiple of 128 or x or hterm reaches 1 GiB.
+ * not a multiple of 256 or x or hterm reaches 1 GiB.
  */
 int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks);
 int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,

@@ -397,21 +397,25 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
 
 // ---------------------------------------------------------------- combine
 // out[t][n] = (resid[t][n] +) sum_j w[t][j] * y[t*k+j][n], j ascending; resid
-// may alias out.  Loads are issued in groups of 8 ranks.
+// may alias out.  Loads are issued in groups of 16 ranks (one group for the
+// usual k <= 16), so a thread waits for memory once per group.
 __global__ __launch_bounds__(64) void k_combine(const float* __restrict__ ybuf,
                                                 const float* __restrict__ w, int T, int k, int H,
                                                 const float* resid, float* out) {
+  constexpr int G = 16;
   const size_t n4 = (size_t)T * H / 4;
   for (size_t q = (size_t)blockIdx.x * 64 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 64) {
     const size_t flat = 4 * q;
     const int t = (int)(flat / H);
     const int n = (int)(flat % H);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (resid) r = *reinterpret_cast<const float4*>(resid + flat);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      float4 y[8];
-      float wj[8];
+    for (int j0 = 0; j0 < k; j0 += G) {
+      float4 y[G];
+      float wj[G];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < G; ++u) {
         const int j = j0 + u;
         if (j < k) {
           y[u] = *reinterpret_cast<const float4*>(ybuf + ((size_t)t * k + j) * H + n);
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(64) void k_combine(const float* __restrict__ ybuf,
         }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < G; ++u) {
         if (j0 + u < k) {
           acc.x = fmaf(wj[u], y[u].x, acc.x);
           acc.y = fmaf(wj[u], y[u].y, acc.y);
@@ -432,7 +436,6 @@ __global__ __launch_bounds__(64) void k_combine(const float* __restrict__ ybuf,
       }
     }
     if (resid) {
-      const float4 r = *reinterpret_cast<const float4*>(resid + flat);
       acc.x = r.x + acc.x; acc.y = r.y + acc.y; acc.z = r.z + acc.z; acc.w = r.w + acc.w;
     }
     *reinterpret_cast<float4*>(out + flat) = acc;

@@ -106,39 +106,29 @@ __device__ __forceinline__ void stage_store(const AStage& a, uint16_t* lds) {
 
 constexpr int kTile = kMB * kLdsRow;  // bf16 elements of one LDS activation tile
 
-// One chunk of one weight row for a lane: 16 code bytes + the block's scale.
-struct BChunk {
-  u32x4 q;
-  uint32_t s;
-};
-
-__device__ __forceinline__ BChunk load_bchunk(rsrc_t rc, rsrc_t rs, uint32_t boff, uint32_t soff, int c, bool ok) {
-  BChunk b;
-  // Normal cache policy, not streaming: a row's 128-byte line is split across
-  // two consecutive chunks and the second half must still hit in L2.
-  b.q = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)c * 64u : 0x80000000u, 0, 0);
-  b.s = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? soff + (uint32_t)c * 4u : 0x80000000u, 0, 0);
-  return b;
-}
-
 // ---------------------------------------------------------------- grouped GEMM pipeline
 // Both expert kernels run 8 waves (two per SIMD, so one covers the other's
 // waits) over one expert block (<= 128 pairs, MT m-tiles of 16) times one
-// tile of output rows.  Wave layout, picked once per workgroup from MT:
-//   small blocks (MT <= 2): wave w owns 2 n-tiles (16-row tiles of output)
-//     and every m-tile;
-//   large blocks: wave w owns 4 n-tiles (row group w % 4) and half of the
-//     m-tiles (w / 4), so each activation fragment read from LDS feeds four
-//     MFMAs and the accumulators stay within one wave's registers.
-// Per K chunk c (128 wide):
-//   1. activation rows are requested into registers, for chunk c+2 (A2) or
-//      chunk c+1;
-//   2. the weights of chunk c+DB-1 are requested (register ring, DB chunks);
-//   3. chunk c is multiplied: weights decoded to bf16 (exact), activation
-//      fragments read from LDS buffer c % 2 one MFMA step ahead;
-//   4. the activation rows of chunk c+1 are written to LDS buffer (c+1) % 2
+// tile of output rows; every wave owns two 16-row n-tiles and all MT m-tiles,
+// so no weight byte is requested twice.  K runs in 128-wide chunks for the
+// activations and in 256-wide superchunks (two chunks) for the weights.
+// Per chunk c:
+//   1. the activation rows of chunk c+2 are requested into registers; at the
+//      first chunk of a superchunk the weights of the superchunk DB-1 ahead
+//      are requested too (register ring of DB superchunks: 4 for gate/up; 3
+//      for down with up to four m-tiles and 2 above, where the accumulators
+//      and both activation terms need the registers; 28 and 6 superchunks,
+//      K = 7168 and 1536, fill whole rounds of these rings);
+//   2. chunk c is multiplied: weights decoded to bf16 (exact), activation
+//      fragments read from LDS buffer c % 2;
+//   3. the activation rows of chunk c+1 are written to LDS buffer (c+1) % 2
 //      (last read in chunk c-1, before the previous barrier);
-//   5. one barrier.
+//   4. one barrier.
+// Weights: lane group g = l/16 holds code blocks g and g+4 of its row's
+// superchunk (16 bytes each, one per chunk), so the 4 groups request a whole
+// 128-byte line of each of 16 rows at once, and the superchunk's 8 scale
+// bytes in one 8-byte load.  In MFMA step s of chunk c, group g supplies
+// K = 32g + 8s .. +8 of the chunk on both operands.
 // Every load is an unconditional raw buffer load; rows past the block and
 // chunks past K use an out-of-range offset and read 0, so the loop has no
 // data-dependent branch and the compiler can count loads in flight exactly.
@@ -186,138 +176,155 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* buf, int row, int col
   return as_bf16x8(*reinterpret_cast<const uint4*>(buf + row * kLdsRow + col));
 }
 
-// Shape of one block's work for a given m-tile count.
+// Weights of one 16-row n-tile for one superchunk, for this lane.
+struct BSuper {
+  u32x4 q[2];     // code blocks g (chunk 0) and g+4 (chunk 1)
+  uint32_t s[2];  // the superchunk's 8 scale bytes
+};
+
+// boff = row * row_bytes + 16 g (or kOOB), soff = row * blocks_per_row (or
+// kOOB); blocks_per_row is a multiple of 8, so the scale load is aligned.
+__device__ __forceinline__ void load_bsuper(BSuper& b, rsrc_t rc, rsrc_t rs, uint32_t boff, uint32_t soff, int sc,
+                                            int nsc) {
+  const bool ok = sc < nsc;
+  b.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u : kOOB, 0, 0);
+  b.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u + 64u : kOOB, 0, 0);
+  const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + (uint32_t)sc * 8u : kOOB, 0, 0);
+  b.s[0] = sv[0];
+  b.s[1] = sv[1];
+}
+
+// Per-MT shape: MS m-tiles staged (even; rows past the block read 0), NV
+// 16-byte pieces per thread per chunk and activation term, FD = activation
+// fragments fetched one MFMA step ahead.  Activations are always requested two
+// chunks ahead: a wait for loads counts them in issue order, so waiting for
+// activations requested one chunk earlier would also wait for every weight
+// load of the ring issued before them.
 template <int MT>
 struct Shape {
-  static constexpr bool kSmall = MT <= 2;
-  static constexpr int NT = kSmall ? 2 : 4;                 // n-tiles per wave
-  static constexpr int MW = kSmall ? MT : (MT + 1) / 2;     // m-tiles per wave
-  static constexpr int MS = kSmall ? 2 : 2 * MW;            // m-tiles staged (rows past the block read 0)
-  static constexpr int NV = MS * 16 * 16 / kThr;            // 16-byte pieces per thread per chunk and term
+  static constexpr int MS = (MT + 1) / 2 * 2;
+  static constexpr int NV = MS * 16 * 16 / kThr;
+  static constexpr bool A2 = true;
+  static constexpr bool FD = MT <= 4;
 };
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// Row tile = 128 rows of gate and the same 128 rows of up.
-//   small: wave w, n-tile 0 = gate rows 16w + 0..15, n-tile 1 = the same up rows;
-//   large: row group r = w % 4, n-tiles 0, 1 = gate rows 32r + 0..15, 16..31,
-//          n-tiles 2, 3 = the same up rows.
-// Output: h as two bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo.
+// Row tile = 128 rows of gate and the same 128 rows of up; wave w: n-tile 0
+// = gate rows 16w + 0..15, n-tile 1 = the same up rows.  Output: h as two
+// bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo.
 constexpr int kGU_NT = 128;
-constexpr int kGU_DB = 4;
 
-template <int MT>
+template <int MT, int DB>
 __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
                                              const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                              const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
                                              uint16_t* __restrict__ hterm) {
   using S = Shape<MT>;
-  constexpr int NT = S::NT, MW = S::MW, NV = S::NV, DB = kGU_DB;
+  constexpr int NV = S::NV;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int m0 = S::kSmall ? 0 : (wid >> 2) * MW;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t rcg = mk_rsrc(codes + (size_t)e * cb, mc), rcu = mk_rsrc(codes + (size_t)e * cb + mc, mc);
   const rsrc_t rsg = mk_rsrc(scales + (size_t)e * sb, ms), rsu = mk_rsrc(scales + (size_t)e * sb + ms, ms);
   const int nb = H / 32;
-  constexpr int NR = NT / 2;  // rows per matrix per lane
-  int row[NR];
-  uint32_t boff[NR], soff[NR];
-#pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    row[j] = nt * kGU_NT + (S::kSmall ? wid * 16 : (wid & 3) * 32 + 16 * j) + nl;
-    const bool ok = row[j] < I;
-    boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nb * 16) + 16u * g : kOOB;
-    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nb + g : kOOB;
-  }
-  const int nchunks = H / kKC;
+  const int row = nt * kGU_NT + wid * 16 + nl;
+  const bool rok = row < I;
+  const uint32_t boff = rok ? (uint32_t)row * (uint32_t)(nb * 16) + 16u * g : kOOB;
+  const uint32_t soff = rok ? (uint32_t)row * (uint32_t)nb : kOOB;
+  const int nchunks = H / kKC, nsc = nchunks / 2;
   uint16_t* buf0 = lds;
   uint16_t* buf1 = lds + kTile;
 
-  // n-tile j < NR: gate row j; NR + j: up row j
-  BChunk rb[DB][NT];
-  auto bfetch = [&](BChunk* dst, int c) {
-    const bool ok = c < nchunks;
+  BSuper rg[DB], ru[DB];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      dst[j] = load_bchunk(rcg, rsg, boff[j], soff[j], c, ok);
-      dst[NR + j] = load_bchunk(rcu, rsu, boff[j], soff[j], c, ok);
-    }
-  };
+  for (int d = 0; d < DB - 1; ++d) {
+    load_bsuper(rg[d], rcg, rsg, boff, soff, d, nsc);
+    load_bsuper(ru[d], rcu, rsu, boff, soff, d, nsc);
+  }
   uint32_t aoff[NV];
   a_offsets<NV>(aoff, row_base);
   ARegs<NV> s0, s1;
   a_fetch<NV>(s0, rx, aoff, 0);
-  a_fetch<NV>(s1, rx, aoff, nchunks > 1 ? kKC * 2 : kFar);
-#pragma unroll
-  for (int d = 0; d < DB - 1; ++d) bfetch(rb[d], d);
+  if (S::A2) a_fetch<NV>(s1, rx, aoff, kKC * 2);
   a_put<NV>(s0, buf0);
   __syncthreads();
 
-  f32x4 acc[MW][NT];
+  f32x4 acc[MT][2];
 #pragma unroll
-  for (int m = 0; m < MW; ++m)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < nchunks; c0 += DB) {
+  // the ring holds whole superchunks; a phantom superchunk past K (odd nsc
+  // with DB = 2) reads zeros on both operands and adds nothing
+  for (int sc0 = 0; sc0 < nsc; sc0 += DB) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const int c = c0 + d;
-      const uint32_t kb2 = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
-      if (d % 2 == 0)
-        a_fetch<NV>(s0, rx, aoff, kb2);
-      else
-        a_fetch<NV>(s1, rx, aoff, kb2);
-      bfetch(rb[(d + DB - 1) % DB], c + DB - 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
-      const uint16_t* A = (d % 2 == 0) ? buf0 : buf1;
-      float sc[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sc[j] = e8m0_operand(rb[d][j].s);
-      bf16x8 fa[2][MW];
-#pragma unroll
-      for (int m = 0; m < MW; ++m) fa[0][m] = lds_frag(A, (m0 + m) * 16 + nl, 32 * g);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < 3) {
-#pragma unroll
-          for (int m = 0; m < MW; ++m) fa[(s + 1) & 1][m] = lds_frag(A, (m0 + m) * 16 + nl, 32 * g + 8 * (s + 1));
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * (sc0 + d) + h;  // chunk; c % 2 == h
+        if (S::A2) {
+          const uint32_t kb = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
+          if (h == 0) a_fetch<NV>(s0, rx, aoff, kb);
+          else a_fetch<NV>(s1, rx, aoff, kb);
+        } else {
+          const uint32_t kb = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
+          a_fetch<NV>(s0, rx, aoff, kb);
         }
-        bf16x8 bt[NT];
+        if (h == 0) {
+          const int sn = sc0 + d + DB - 1;
+          load_bsuper(rg[(d + DB - 1) % DB], rcg, rsg, boff, soff, sn, nsc);
+          load_bsuper(ru[(d + DB - 1) % DB], rcu, rsu, boff, soff, sn, nsc);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+        const uint16_t* A = h == 0 ? buf0 : buf1;
+        const float sgv = e8m0_operand((rg[d].s[h] >> (8 * g)) & 0xFFu);
+        const float suv = e8m0_operand((ru[d].s[h] >> (8 * g)) & 0xFFu);
+        bf16x8 fa[2][MT];
+        if (S::FD) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) bt[j] = decode8(rb[d][j].q[s], sc[j]);
+          for (int m = 0; m < MT; ++m) fa[0][m] = lds_frag(A, m * 16 + nl, 32 * g);
+        }
 #pragma unroll
-        for (int m = 0; m < MW; ++m)
+        for (int s = 0; s < 4; ++s) {
+          if (S::FD) {
+            if (s < 3) {
 #pragma unroll
-          for (int j = 0; j < NT; ++j)
-            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bt[j], acc[m][j], 0, 0, 0);
-      }
-      // activations of chunk c+1 (fetched one chunk ago) into the other buffer
-      if (d % 2 == 0)
-        a_put<NV>(s1, buf1);
-      else
-        a_put<NV>(s0, buf0);
-      __syncthreads();
-    }
-  }
-  // lane holds rows row[j] for slots (m0 + m)*16 + 4g + r
+              for (int m = 0; m < MT; ++m) fa[(s + 1) & 1][m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * (s + 1));
+            }
+          } else {
 #pragma unroll
-  for (int m = 0; m < MW; ++m) {
+            for (int m = 0; m < MT; ++m) fa[s & 1][m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * s);
+          }
+          const bf16x8 bg = decode8(rg[d].q[h][s], sgv), bu = decode8(ru[d].q[h][s], suv);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = pid[(m0 + m) * 16 + 4 * g + r];
-      if (p >= 0) {
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-          if (row[j] < I) {
-            const float h = silu_mul(acc[m][j][r], acc[m][NR + j][r]);
-            const uint16_t hi = f32_to_bf16_rne(h);
-            const uint16_t lo = f32_to_bf16_rne(h - bf16_bits_to_f32(hi));
-            hterm[(size_t)p * I + row[j]] = hi;
-            hterm[(size_t)P * I + (size_t)p * I + row[j]] = lo;
+          for (int m = 0; m < MT; ++m) {
+            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bg, acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bu, acc[m][1], 0, 0, 0);
           }
         }
+        // activations of chunk c+1 (fetched earlier) into the other buffer
+        if (S::A2) {
+          if (h == 0) a_put<NV>(s1, buf1);
+          else a_put<NV>(s0, buf0);
+        } else {
+          a_put<NV>(s0, h == 0 ? buf1 : buf0);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // lane holds row `row` for slots m*16 + 4g + r
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int p = pid[m * 16 + 4 * g + r];
+      if (p >= 0 && rok) {
+        const float hv = silu_mul(acc[m][0][r], acc[m][1][r]);
+        const uint16_t hi = f32_to_bf16_rne(hv);
+        const uint16_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
+        hterm[(size_t)p * I + row] = hi;
+        hterm[(size_t)P * I + (size_t)p * I + row] = lo;
       }
     }
   }
@@ -346,149 +353,140 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
   __syncthreads();
   const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
   switch ((cnt + 15) / 16) {
-    case 1: gateup_block<1>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 2: gateup_block<2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 3: gateup_block<3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 4: gateup_block<4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 5: gateup_block<5>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 6: gateup_block<6>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 7: gateup_block<7>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    default: gateup_block<8>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 1: gateup_block<1, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 2: gateup_block<2, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 3: gateup_block<3, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 4: gateup_block<4, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 5: gateup_block<5, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 6: gateup_block<6, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 7: gateup_block<7, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    default: gateup_block<8, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
   }
 }
 
 // ---------------------------------------------------------------- down
-// Row tile = 256 rows of Wd [H][I].
-//   small: wave w owns rows 32w + 0..15, 16..31 (2 n-tiles);
-//   large: row group r = w % 4 owns rows 64r .. 64r+63 (4 n-tiles).
-// The activations are the two bf16 terms of h for the block's pairs; each
-// MFMA step runs once per term into the same accumulator.  Small blocks keep
-// a 4-deep weight ring and fetch activations two chunks ahead; large blocks,
-// whose chunk of multiplies outlasts a load, use a 2-deep ring and one chunk
-// ahead to leave registers for the accumulators.  Output y[p][n] (fp32).
+// Row tile = 256 rows of Wd [H][I]; wave w: n-tiles = rows 32w + 0..15 and
+// 32w + 16..31.  The activations are the two bf16 terms of h for the block's
+// pairs, both staged in LDS; each MFMA step runs once per term into the same
+// accumulator.  Output y[p][n] (fp32).
 constexpr int kDN_NT = 256;
 
-template <int MT>
+template <int MT, int DB>
 __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, rsrc_t rh,
                                            const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                            const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
                                            float* __restrict__ ybuf) {
   using S = Shape<MT>;
-  constexpr int NT = S::NT, MW = S::MW, NV = S::NV;
-  constexpr bool A2 = S::kSmall;
-  constexpr int DB = S::kSmall ? 4 : 2;
+  constexpr int NV = S::NV;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int m0 = S::kSmall ? 0 : (wid >> 2) * MW;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t rc = mk_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
   const rsrc_t rs = mk_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
   const int nbk = I / 32;
-  int row[NT];
-  uint32_t boff[NT], soff[NT];
+  int row[2];
+  uint32_t boff[2], soff[2];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    row[j] = nt * kDN_NT + (S::kSmall ? wid * 32 : (wid & 3) * 64) + 16 * j + nl;
+  for (int j = 0; j < 2; ++j) {
+    row[j] = nt * kDN_NT + wid * 32 + 16 * j + nl;
     const bool ok = row[j] < H;
     boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nbk * 16) + 16u * g : kOOB;
-    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nbk + g : kOOB;
+    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nbk : kOOB;
   }
-  const int nchunks = I / kKC;
+  const int nchunks = I / kKC, nsc = nchunks / 2;
   const uint32_t lo_off = (uint32_t)((size_t)P * I * 2);  // byte offset of the lo term
   // LDS: buffer b, term t at lds + (2b + t) * kTile
-  BChunk rb[DB][NT];
-  auto bfetch = [&](BChunk* dst, int c) {
-    const bool ok = c < nchunks;
+  BSuper rb[DB][2];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) dst[j] = load_bchunk(rc, rs, boff[j], soff[j], c, ok);
-  };
+  for (int d = 0; d < DB - 1; ++d)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_bsuper(rb[d][j], rc, rs, boff[j], soff[j], d, nsc);
   uint32_t aoff[NV];
   a_offsets<NV>(aoff, row_base);
   ARegs<NV> h0, l0, h1, l1;
   a_fetch<NV>(h0, rh, aoff, 0);
   a_fetch<NV>(l0, rh, aoff, lo_off);
-  if (A2) {
-    const uint32_t kb1 = nchunks > 1 ? kKC * 2 : kFar;
-    a_fetch<NV>(h1, rh, aoff, kb1);
-    a_fetch<NV>(l1, rh, aoff, lo_off + kb1);
+  if (S::A2) {
+    a_fetch<NV>(h1, rh, aoff, kKC * 2);
+    a_fetch<NV>(l1, rh, aoff, lo_off + kKC * 2);
   }
-#pragma unroll
-  for (int d = 0; d < DB - 1; ++d) bfetch(rb[d], d);
   a_put<NV>(h0, lds);
   a_put<NV>(l0, lds + kTile);
   __syncthreads();
 
-  f32x4 acc[MW][NT];
+  f32x4 acc[MT][2];
 #pragma unroll
-  for (int m = 0; m < MW; ++m)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < nchunks; c0 += DB) {
+  for (int sc0 = 0; sc0 < nsc; sc0 += DB) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const int c = c0 + d;
-      if (A2) {
-        const uint32_t kb2 = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
-        if (d % 2 == 0) {
-          a_fetch<NV>(h0, rh, aoff, kb2);
-          a_fetch<NV>(l0, rh, aoff, lo_off + kb2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * (sc0 + d) + h;
+        if (S::A2) {
+          const uint32_t kb = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
+          if (h == 0) {
+            a_fetch<NV>(h0, rh, aoff, kb);
+            a_fetch<NV>(l0, rh, aoff, lo_off + kb);
+          } else {
+            a_fetch<NV>(h1, rh, aoff, kb);
+            a_fetch<NV>(l1, rh, aoff, lo_off + kb);
+          }
         } else {
-          a_fetch<NV>(h1, rh, aoff, kb2);
-          a_fetch<NV>(l1, rh, aoff, lo_off + kb2);
+          const uint32_t kb = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
+          a_fetch<NV>(h0, rh, aoff, kb);
+          a_fetch<NV>(l0, rh, aoff, lo_off + kb);
         }
-      } else {
-        const uint32_t kb1 = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
-        a_fetch<NV>(h0, rh, aoff, kb1);
-        a_fetch<NV>(l0, rh, aoff, lo_off + kb1);
-      }
-      bfetch(rb[(d + DB - 1) % DB], c + DB - 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
-      const uint16_t* Ah = lds + (d % 2) * 2 * kTile;
-      const uint16_t* Al = Ah + kTile;
-      float sc[NT];
+        if (h == 0) {
+          const int sn = sc0 + d + DB - 1;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sc[j] = e8m0_operand(rb[d][j].s);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 bt[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) bt[j] = decode8(rb[d][j].q[s], sc[j]);
-        bf16x8 fh[MW], fl[MW];
-#pragma unroll
-        for (int m = 0; m < MW; ++m) {
-          fh[m] = lds_frag(Ah, (m0 + m) * 16 + nl, 32 * g + 8 * s);
-          fl[m] = lds_frag(Al, (m0 + m) * 16 + nl, 32 * g + 8 * s);
+          for (int j = 0; j < 2; ++j) load_bsuper(rb[(d + DB - 1) % DB][j], rc, rs, boff[j], soff[j], sn, nsc);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+        const uint16_t* Ah = lds + h * 2 * kTile;
+        const uint16_t* Al = Ah + kTile;
+        const float s0v = e8m0_operand((rb[d][0].s[h] >> (8 * g)) & 0xFFu);
+        const float s1v = e8m0_operand((rb[d][1].s[h] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int m = 0; m < MW; ++m) {
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 b0 = decode8(rb[d][0].q[h][s], s0v), b1 = decode8(rb[d][1].q[h][s], s1v);
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh[m], bt[j], acc[m][j], 0, 0, 0);
-            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[m], bt[j], acc[m][j], 0, 0, 0);
+          for (int m = 0; m < MT; ++m) {
+            const bf16x8 fh = lds_frag(Ah, m * 16 + nl, 32 * g + 8 * s);
+            const bf16x8 fl = lds_frag(Al, m * 16 + nl, 32 * g + 8 * s);
+            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b0, acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b1, acc[m][1], 0, 0, 0);
+            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b0, acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b1, acc[m][1], 0, 0, 0);
           }
         }
+        uint16_t* nxt = lds + (h ^ 1) * 2 * kTile;
+        if (S::A2) {
+          if (h == 0) {
+            a_put<NV>(h1, nxt);
+            a_put<NV>(l1, nxt + kTile);
+          } else {
+            a_put<NV>(h0, nxt);
+            a_put<NV>(l0, nxt + kTile);
+          }
+        } else {
+          a_put<NV>(h0, nxt);
+          a_put<NV>(l0, nxt + kTile);
+        }
+        __syncthreads();
       }
-      uint16_t* nxt = lds + ((d + 1) % 2) * 2 * kTile;
-      if (!A2 || d % 2 == 1) {
-        a_put<NV>(h0, nxt);
-        a_put<NV>(l0, nxt + kTile);
-      } else {
-        a_put<NV>(h1, nxt);
-        a_put<NV>(l1, nxt + kTile);
-      }
-      __syncthreads();
     }
   }
 #pragma unroll
-  for (int m = 0; m < MW; ++m) {
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int p = pid[(m0 + m) * 16 + 4 * g + r];
+      const int p = pid[m * 16 + 4 * g + r];
       if (p >= 0) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < 2; ++j)
           if (row[j] < H) ybuf[(size_t)p * H + row[j]] = acc[m][j][r];
       }
     }
@@ -518,14 +516,14 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   __syncthreads();
   const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
   switch ((cnt + 15) / 16) {
-    case 1: down_block<1>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 2: down_block<2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 3: down_block<3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 4: down_block<4>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 5: down_block<5>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 6: down_block<6>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 7: down_block<7>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    default: down_block<8>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 1: down_block<1, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 2: down_block<2, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 3: down_block<3, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 4: down_block<4, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 5: down_block<5, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 6: down_block<6, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 7: down_block<7, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    default: down_block<8, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
   }
 }
 

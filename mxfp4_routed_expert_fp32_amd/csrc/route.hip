@@ -120,17 +120,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Number of lanes whose 64-bit key is larger than this lane's (keys unique).
-__device__ __forceinline__ int rank_in_wave(uint64_t v) {
+// Number of lanes whose 64-bit key is larger than this lane's (keys unique),
+// through a 64-entry LDS buffer of the wave: every lane writes its key, then
+// reads all 64 back two at a time (the same address in every lane, a
+// broadcast).  The buffer is free again when the function returns.
+__device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf) {
+  const int lane = threadIdx.x % kWave;
+  buf[lane] = v;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   int r = 0;
 #pragma unroll
-  for (int j = 0; j < kWave; ++j) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, j);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
-    r += ((((uint64_t)hi << 32) | lo) > v) ? 1 : 0;
+  for (int j = 0; j < kWave; j += 2) {
+    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
+    r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   return r;
 }
+
 
 // One wavefront per token; each lane owns experts lane + 64*v, v < MAXV.
 // Selection: let L be the k-th largest of the 64 lane maxima.  The k largest
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
     lmax = umax64(lmax, key[v]);
   }
   // L = k-th largest lane maximum (the lane of rank k-1); 0 if fewer lanes hold keys
-  const int lrank = rank_in_wave(lmax);
+  const int lrank = rank_in_wave_lds(lmax, cand[wid]);
   const uint64_t sel_lane = __builtin_amdgcn_ballot_w64(lrank == k - 1);
   uint64_t L = 0;
   if (sel_lane) {
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const uint64_t c = (lane < total) ? cand[wid][lane] : 0ull;
-    const int r = rank_in_wave(c);
+    const int r = rank_in_wave_lds(c, cand[wid]);
     if (lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
   } else {
     for (int j = 0; j < k; ++j) {
@@ -217,8 +226,16 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int sel = (lane < k) ? (int)sel_e[wid][lane] : 0;
-  // softmax over the selected logits, in rank order
-  const float lj = (lane < k) ? l[sel] : 0.0f;
+  // softmax over the selected logits, in rank order; each logit is read back
+  // from the registers of the lane that holds it (lane sel % 64, slot
+  // sel / 64), not from memory
+  float lj = 0.0f;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const float x = __shfl(lv[v], sel % kWave, kWave);
+    if (sel / kWave == v) lj = x;
+  }
+  if (lane >= k) lj = 0.0f;
   const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
   const float ex = (lane < k) ? expf(lj - m) : 0.0f;
   const float s = wave_sum(ex);

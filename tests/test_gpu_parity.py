@@ -203,7 +203,9 @@ def test_forward_tiny_matches_oracle(seed):
                                            (7168, 1536, 20, 16, 2, "bf16"),
                                            # down with K split across I/512 waves, ragged row ranges
                                            (160, 1024, 5, 2, 1, "f32"), (96, 2048, 6, 3, 3, "f32"),
-                                           (64, 3072, 4, 2, 2, "f32"), (1056, 1536, 9, 4, 1, "bf16")])
+                                           (64, 3072, 4, 2, 2, "f32"), (1056, 1536, 9, 4, 1, "bf16"),
+                                           # decode-form GEMVs at other widths (bf16 x, one token or I % 128 != 0)
+                                           (4096, 96, 5, 2, 3, "bf16"), (2048, 64, 4, 2, 1, "bf16")])
 def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
     w = synth.Workload("s", 60, T, H, I, E, k, xd, weight_seed=7100 + H + E)
     c, s, ex = experts_host(w)
@@ -276,10 +278,12 @@ def test_rmsnorm_and_residual():
 
 # ------------------------------------------------------------------ prefill form (grouped GEMM on MFMA)
 
-@pytest.mark.parametrize("H,I,E,k,T,hot", [(256, 128, 8, 2, 37, False), (512, 256, 16, 4, 65, False),
-                                           (256, 128, 4, 2, 300, True), (1024, 384, 12, 3, 130, True)])
+@pytest.mark.parametrize("H,I,E,k,T,hot", [(256, 256, 8, 2, 37, False), (512, 256, 16, 4, 65, False),
+                                           (256, 512, 4, 2, 300, True), (1024, 768, 12, 3, 130, True),
+                                           (768, 1280, 6, 2, 45, False)])
 def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
-    """T > 1 with bf16 activations runs the sort + MFMA grouped GEMMs; expert
+    """T > 1 with bf16 activations runs the sort + MFMA grouped GEMMs (H, I
+    multiples of 256; an odd count of 256-wide K superchunks included); expert
     blocks are ragged, and `hot` makes one expert take more than 128 tokens."""
     w = synth.Workload("g", 63, T, H, I, E, k, "bf16", weight_seed=7500 + H + E + T)
     c, s, ex = experts_host(w)
