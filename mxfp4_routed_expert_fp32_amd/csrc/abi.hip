@@ -184,8 +184,21 @@ int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const 
   float* w = w_out ? w_out : reinterpret_cast<float*>(ws + L.w);
   const bool xf = x_dtype == MOE_DTYPE_F32;
   MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, s)));
-  MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
-  return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);
+  if (T > 1 && !xf && grouped_fits(d, T, (int64_t)T * k)) {
+    // prefill form: top-k, then sort + grouped GEMMs
+    MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
+    return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);
+  }
+  // decode form: the gate/up kernel selects the experts itself (and writes
+  // idx and w for the down and combine kernels)
+  const int H = d->hidden, I = d->inter, E = d->n_experts;
+  float* h = reinterpret_cast<float*>(ws + L.h);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  MOE_TRY(dev(moe::launch_gateup_select_gemv(x, xf, logits, T, k, c, sc, H, I, E, idx, w, h, s)));
+  MOE_TRY(dev(moe::launch_down_gemv(h, idx, T * k, c, sc, H, I, E, y, s)));
+  return dev(moe::launch_combine(y, w, T, k, H, resid, out, s));
 }
 
 }  // namespace

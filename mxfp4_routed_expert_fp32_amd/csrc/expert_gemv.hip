@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -187,12 +188,21 @@ __device__ __forceinline__ float group_reduce(float v) {
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // Workgroup (pair p, part): wave w takes rows part*4 + w, + 4*parts, ... of
-// the gate and up matrices of expert route[p], LPR = 64 (one row per step),
+// the gate and up matrices of the pair's expert, LPR = 64 (one row per step),
 // the next row loaded while the current one is computed.
 // hbuf[p][i] = silu(g_i) * u_i, pair p = t*k + j uses token t = p / k.
-template <bool XF32, int NBL>
+// SEL = 0: the pair's expert is route[p].  SEL = MAXV > 0: the workgroup
+// selects it itself: wave 0 runs the exact top-k + softmax (topk.h) on the
+// token's logits while the token's activations are staged, and the expert of
+// rank j = p % k is used; workgroup (p % k == 0, part 0) also writes the
+// token's k experts to route[] and their weights to wsel[] for the later
+// kernels.  Every workgroup of a token computes the same selection from the
+// same logits with the same code, so they agree.
+template <bool XF32, int NBL, int SEL>
 __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
-                                                     const int32_t* __restrict__ route,
+                                                     int32_t* __restrict__ route,
+                                                     const float* __restrict__ logits,
+                                                     float* __restrict__ wsel,
                                                      const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales, int H, int I,
                                                      int E, int k, int parts, int rpw,
@@ -202,9 +212,33 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  int e = __builtin_amdgcn_readfirstlane(route[p]);
-  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nb = H / 32;
+  const int xbytes = XF32 ? H * 4 : H * 2;
+  const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (size_t)(p / k) * xbytes);
+  int e;
+  if constexpr (SEL > 0) {
+    __shared__ uint64_t cand[kWave];
+    __shared__ uint32_t ncand;
+    __shared__ uint32_t sel_e[kWave];
+    __shared__ int32_t chosen;
+    for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
+    if (wid == 0) {
+      const int t = p / k;
+      int sel;
+      float wv;
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &ncand, sel_e, &sel, &wv);
+      if (lane == p % k) chosen = sel;
+      if (part == 0 && p % k == 0 && lane < k) {
+        route[(size_t)t * k + lane] = sel;
+        wsel[(size_t)t * k + lane] = wv;
+      }
+    }
+    __syncthreads();
+    e = __builtin_amdgcn_readfirstlane(chosen);
+  } else {
+    e = __builtin_amdgcn_readfirstlane(route[p]);
+  }
+  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t gcod = make_rsrc(codes + (size_t)e * cb, mc);
@@ -220,11 +254,12 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   load_row<kWave, NBL>(g0, gcod, gsc, nsteps > 0 ? i0 : -1, lane, nb);
   load_row<kWave, NBL>(u0, ucod, usc, nsteps > 0 ? i0 : -1, lane, nb);
 
-  // stage this token's activations, then keep the lane's blocks in registers
-  const int xbytes = XF32 ? H * 4 : H * 2;
-  const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (size_t)(p / k) * xbytes);
-  for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
-  __syncthreads();
+  // stage this token's activations (already done when selecting), then keep
+  // the lane's blocks in registers
+  if constexpr (SEL == 0) {
+    for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
+    __syncthreads();
+  }
   uint32_t xr[NBL][XW];
 #pragma unroll
   for (int m = 0; m < NBL; ++m) {
@@ -457,16 +492,16 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
   *parts = (rows + 4 * pw - 1) / (4 * pw);
 }
 
-template <bool XF32>
-static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x,
-                                  const int32_t* route, const uint8_t* codes, const uint8_t* scales,
+template <bool XF32, int SEL>
+static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
+                                  const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
                                   int H, int I, int E, int k, float* hbuf) {
-#define MOE_GU(N)                                                                              \
-  {                                                                                              \
-    int parts, rpw;                                                                              \
-    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N>, lds), &parts, &rpw);                \
-    k_gateup_gemv<XF32, N><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(x, route, codes, scales, H, I, E, \
-                                                                        k, parts, rpw, hbuf);    \
+#define MOE_GU(N)                                                                                    \
+  {                                                                                                    \
+    int parts, rpw;                                                                                    \
+    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N, SEL>, lds), &parts, &rpw);                \
+    k_gateup_gemv<XF32, N, SEL><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(                         \
+        x, route, logits, wsel, codes, scales, H, I, E, k, parts, rpw, hbuf);                          \
   }
   switch (nbl) {
     case 1: MOE_GU(1); break;
@@ -484,8 +519,28 @@ hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, i
                               float* hbuf, hipStream_t s) {
   const int nbl = (H / 32 + kWave - 1) / kWave;
   const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
-  if (x_f32) return gateup_dispatch<true>(nbl, P, lds, s, x, route, codes, scales, H, I, E, k, hbuf);
-  return gateup_dispatch<false>(nbl, P, lds, s, x, route, codes, scales, H, I, E, k, hbuf);
+  int32_t* r = const_cast<int32_t*>(route);  // read only when SEL == 0
+  if (x_f32) return gateup_dispatch<true, 0>(nbl, P, lds, s, x, r, nullptr, nullptr, codes, scales, H, I, E, k, hbuf);
+  return gateup_dispatch<false, 0>(nbl, P, lds, s, x, r, nullptr, nullptr, codes, scales, H, I, E, k, hbuf);
+}
+
+hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* logits, int T, int k,
+                                     const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                                     int32_t* route, float* wsel, float* hbuf, hipStream_t s) {
+  const int nbl = (H / 32 + kWave - 1) / kWave;
+  const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
+  const int P = T * k;
+#define MOE_GUS(XF, MV) \
+  return gateup_dispatch<XF, MV>(nbl, P, lds, s, x, route, logits, wsel, codes, scales, H, I, E, k, hbuf);
+  if (x_f32) {
+    if (E <= 256) MOE_GUS(true, 4)
+    if (E <= 1024) MOE_GUS(true, 16)
+    MOE_GUS(true, 64)
+  }
+  if (E <= 256) MOE_GUS(false, 4)
+  if (E <= 1024) MOE_GUS(false, 16)
+  MOE_GUS(false, 64)
+#undef MOE_GUS
 }
 
 // Lanes per row and blocks per lane for a reduction length of nbk blocks:

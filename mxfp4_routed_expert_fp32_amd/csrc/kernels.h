@@ -18,6 +18,12 @@ hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
                               const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
                               float* hbuf, hipStream_t s);
+// Same with the selection fused in: each workgroup takes its pair's expert
+// from the exact top-k of its token's logits; route [T][k] and wsel [T][k]
+// receive the selection and the softmax weights.
+hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* logits, int T, int k,
+                                     const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                                     int32_t* route, float* wsel, float* hbuf, hipStream_t s);
 hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
                             const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s);
 hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,
