@@ -14,8 +14,8 @@ Zipf(1.1) router bias), `prefill4096` (4096 tokens per step, uniform routing),
 as a HIP graph).
 
 Prints one JSON line.  The roofline object describes the dominant kernel
-(decode: the gate/up GEMV, timed launch by launch with HIP events on the
-stream it runs on); `cpu_baseline` times the CPU oracle on the host cores on a
+(decode: the gate/up GEMV, timed over a run of back-to-back launches with
+HIP events on the stream it runs on); `cpu_baseline` times the CPU oracle on the host cores on a
 bounded sample of the same workload.
 """
 import argparse
@@ -50,7 +50,7 @@ DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096":
 # rocprofv3 counters is reported only while these files still hash to the
 # value recorded next to the counters.
 KERNEL_SOURCES = {
-    "k_gateup_gemv": ["expert_gemv.hip", "common.h"],
+    "k_gateup_gemv": ["expert_gemv.hip", "common.h", "topk.h"],
     "k_gateup_mfma": ["expert_mfma.hip", "common.h"],
 }
 
@@ -112,8 +112,9 @@ def common_fields(a, metric, value, unit, ms_step, config, roofline):
 
 def hold_queue(seconds):
     """Keep the GPU busy on the current stream for about `seconds` (a bounded
-    spin kernel) so that the launches enqueued next run back to back: events
-    around each launch then time the kernel, not the host's enqueue gaps."""
+    spin kernel) so that the launches enqueued next run back to back: two
+    events around a run of launches then time the kernels (and the launch
+    gaps between them), not the host's enqueue gaps."""
     import torch
     torch.cuda._sleep(int(seconds * 2.4e9))
 
@@ -173,22 +174,21 @@ def bench_decode(a):
 
     ms_step = timed(step, a.steps, a.warmup)
 
-    # dominant kernel: gate/up + SwiGLU GEMV, timed launch by launch on the
+    # dominant kernel: gate/up + SwiGLU GEMV, timed over back-to-back launches on the
     # stream it runs on, with the same routes and tokens as the steps above
     hbuf = torch.empty(k, I, dtype=torch.float32, device=dev)
     for i in range(a.warmup):
         moe.moe_mxfp4_gate_up(desc, pool[i % a.pool:i % a.pool + 1], routes[i % a.pool], k, codes, scales, hbuf)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    hold_queue(a.steps * 40e-6)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(a.steps * 100e-6)
+    e0.record()
     for i in range(a.steps):
         j = (a.warmup + i) % a.pool
-        starts[i].record()
         moe.moe_mxfp4_gate_up(desc, pool[j:j + 1], routes[j], k, codes, scales, hbuf)
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    gu_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    gu_ms = e0.elapsed_time(e1) / a.steps
     gu_bytes = k * 2 * (I * H // 2 + I * H // 32) + H * 2 + k * I * 4
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
 
@@ -202,7 +202,8 @@ def bench_decode(a):
          "global_batch": 1, "layer_bytes_per_token": layer_bytes,
          "layer_GBps": layer_bytes / (ms_step * 1e-3) / 1e9, "expert_bytes_per_token": expert_bytes,
          "parity_max_err": parity},
-        {"bound": "hbm", "kernel": "k_gateup_gemv", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        {"bound": "hbm", "kernel": "k_gateup_gemv (routes given)", "achieved": achieved, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s",
          "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("k_gateup_gemv", "decode"),
          "avg_launch_us": gu_ms * 1e3, "bytes_per_launch": gu_bytes})
     if not a.no_cpu_baseline:
@@ -262,8 +263,8 @@ def bench_batch(a):
            "touched_bytes_per_step": touched, "layer_GBps": gbps, "algorithmic_TFLOPs": tflops,
            "frac_bf16_mfma_peak": tflops / BF16_PEAK_TFLOPS, "frac_mxfp4_mfma_peak": tflops / MXFP4_PEAK_TFLOPS,
            "parity_max_err": parity}
-    # dominant kernel: the grouped gate/up GEMM (k_gateup_mfma), timed launch
-    # by launch with HIP events on the stream it runs on, over the sorted
+    # dominant kernel: the grouped gate/up GEMM (k_gateup_mfma), timed over a
+    # run of back-to-back launches with HIP events on its stream, over the sorted
     # routes of each rotating batch
     P = T * k
     mb = moe.max_expert_blocks(E, P)
@@ -287,16 +288,15 @@ def bench_batch(a):
         gate_up(i)
     torch.cuda.synchronize()
     nl = max(a.steps, 2 * nbatch)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nl)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nl)]
-    hold_queue(nl * 40e-6)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(nl * 100e-6)
+    e0.record()
     for i in range(nl):
-        starts[i].record()
         gate_up(i)
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    gu_ms = [st.elapsed_time(en) for st, en in zip(starts, ends)]
-    gu_avg_ms = float(np.mean(gu_ms))
+    gu_avg_ms = e0.elapsed_time(e1) / nl
+    gu_ms = [gu_avg_ms] * nl
     gu_w = 2 * (I * H // 2 + I * H // 32)                     # gate + up bytes of one expert
     gu_bytes = [unions[i % nbatch] * gu_w + T * H * 2 + P * I * 4 for i in range(nl)]
     gu_flops = 4.0 * H * I * P
