@@ -110,11 +110,12 @@ int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
   return MOE_OK;
 }
 
-// The grouped GEMMs tile K by 256 (weights) and 128 (activations) and address
-// activations with 32-bit buffer offsets and an out-of-range sentinel at
-// 1 GiB: x (bf16) and the two bf16 terms of h must each stay below that.
+// The grouped GEMMs tile K by 256 (weights) and 128 (activations), keep each
+// row tile's scales in LDS (which caps H and I), and address activations with
+// 32-bit buffer offsets and an out-of-range sentinel at 1 GiB: x (bf16) and
+// the two bf16 terms of h must each stay below that.
 bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
-  return d->hidden % 256 == 0 && d->inter % 256 == 0 && T * d->hidden * 2 < (int64_t{1} << 30) &&
+  return moe::grouped_shape_ok(d->hidden, d->inter) && T * d->hidden * 2 < (int64_t{1} << 30) &&
          P * d->inter * 4 < (int64_t{1} << 30);
 }
 

@@ -113,22 +113,24 @@ constexpr int kTile = kMB * kLdsRow;  // bf16 elements of one LDS activation til
 // so no weight byte is requested twice.  K runs in 128-wide chunks for the
 // activations and in 256-wide superchunks (two chunks) for the weights.
 // Per chunk c:
-//   1. the activation rows of chunk c+2 are requested into registers; at the
-//      first chunk of a superchunk the weights of the superchunk DB-1 ahead
-//      are requested too (register ring of DB superchunks: 4 for gate/up; 3
-//      for down with up to four m-tiles and 2 above, where the accumulators
-//      and both activation terms need the registers; 28 and 6 superchunks,
-//      K = 7168 and 1536, fill whole rounds of these rings);
+//   1. the activation rows of chunk c+DA are requested into a register ring
+//      of DA chunks; at the first chunk of a superchunk the weights of the
+//      superchunk DB-1 ahead are requested too (register ring of DB
+//      superchunks).  Loads complete for the wait counter in issue order, so
+//      a wait for an activation load also waits for every weight load issued
+//      before it: the activation ring must reach about as far ahead as the
+//      weight ring, or the weight ring's depth is lost;
 //   2. chunk c is multiplied: weights decoded to bf16 (exact), activation
 //      fragments read from LDS buffer c % 2;
 //   3. the activation rows of chunk c+1 are written to LDS buffer (c+1) % 2
 //      (last read in chunk c-1, before the previous barrier);
 //   4. one barrier.
 // Weights: lane group g = l/16 holds code blocks g and g+4 of its row's
-// superchunk (16 bytes each, one per chunk), so the 4 groups request a whole
-// 128-byte line of each of 16 rows at once, and the superchunk's 8 scale
-// bytes in one 8-byte load.  In MFMA step s of chunk c, group g supplies
-// K = 32g + 8s .. +8 of the chunk on both operands.
+// superchunk (16 bytes each, one per chunk), so the 4 groups request both
+// halves of a 128-byte line of each of 16 rows back to back; the
+// superchunk's 8 scale bytes per row come from the workgroup's LDS scale
+// table.  In MFMA step s of chunk c, group g supplies K = 32g + 8s .. +8 of
+// the chunk on both operands.
 // Every load is an unconditional raw buffer load; rows past the block and
 // chunks past K use an out-of-range offset and read 0, so the loop has no
 // data-dependent branch and the compiler can count loads in flight exactly.
@@ -182,29 +184,78 @@ struct BSuper {
   uint32_t s[2];  // the superchunk's 8 scale bytes
 };
 
-// boff = row * row_bytes + 16 g (or kOOB), soff = row * blocks_per_row (or
-// kOOB); blocks_per_row is a multiple of 8, so the scale load is aligned.
-__device__ __forceinline__ void load_bsuper(BSuper& b, rsrc_t rc, rsrc_t rs, uint32_t boff, uint32_t soff, int sc,
-                                            int nsc) {
+// Codes: boff = row * row_bytes + 16 g (or kOOB for a row past the matrix).
+__device__ __forceinline__ void load_bcodes(BSuper& b, rsrc_t rc, uint32_t boff, int sc, int nsc) {
   const bool ok = sc < nsc;
   b.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u : kOOB, 0, 0);
   b.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u + 64u : kOOB, 0, 0);
-  const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + (uint32_t)sc * 8u : kOOB, 0, 0);
-  b.s[0] = sv[0];
-  b.s[1] = sv[1];
+}
+
+// Scales from this row's line of the LDS scale table; a superchunk past K
+// gets scale byte 0 (its codes read 0, and 0 times 2^-127 adds nothing).
+__device__ __forceinline__ void load_bscales(BSuper& b, const uint8_t* srow, int sc, int nsc) {
+  const bool ok = sc < nsc;
+  const u32x2 v = *reinterpret_cast<const u32x2*>(srow + (ok ? sc : 0) * 8);
+  b.s[0] = ok ? v[0] : 0u;
+  b.s[1] = ok ? v[1] : 0u;
+}
+
+// ---------------------------------------------------------------- scale tables
+// A workgroup's weight rows are consecutive rows of one matrix, so their E8M0
+// scales (nb = K/32 bytes per row) form one contiguous range.  Reading each
+// superchunk's 8 scale bytes per row straight from memory touches a new
+// 64-byte sector for 8 bytes every time, and those sectors do not survive in
+// L2 between touches while the code stream passes through it (measured: HBM
+// reads grew by about eight times the scale bytes, and the stream rate fell
+// by more than half).  Instead the range is copied once per workgroup into an
+// LDS table with whole-line 16-byte loads, rows padded to nb + 8 bytes (an
+// 8-byte read per lane over 16 consecutive rows then hits distinct banks for
+// the model's nb), and every superchunk reads its 8 bytes from there.
+template <int U>
+struct SPieces {
+  u32x4 v[U];
+};
+
+__host__ __device__ constexpr int scale_row_pitch(int nb) { return nb + 8; }
+
+// Requests bytes [first, first + total) of rs as 16-byte pieces q = t + kThr*u.
+template <int U>
+__device__ __forceinline__ void scales_fetch(SPieces<U>& sp, rsrc_t rs, uint32_t first, uint32_t total) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t flat = (uint32_t)(threadIdx.x + kThr * u) * 16u;
+    sp.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, flat < total ? first + flat : kOOB, 0, 0);
+  }
+}
+
+// Writes the pieces into rows of nb bytes at pitch scale_row_pitch(nb); a
+// piece may straddle two rows (nb % 16 == 8), so each 8-byte half is placed
+// on its own.
+template <int U>
+__device__ __forceinline__ void scales_put(const SPieces<U>& sp, uint8_t* tab, int nb, uint32_t total) {
+  const int pitch = scale_row_pitch(nb);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t flat = (uint32_t)(threadIdx.x + kThr * u) * 16u;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t f = flat + 8u * half;
+      if (f < total) {
+        const uint32_t r = f / (uint32_t)nb, c = f % (uint32_t)nb;
+        *reinterpret_cast<u32x2*>(tab + r * pitch + c) =
+            half ? u32x2{sp.v[u][2], sp.v[u][3]} : u32x2{sp.v[u][0], sp.v[u][1]};
+      }
+    }
+  }
 }
 
 // Per-MT shape: MS m-tiles staged (even; rows past the block read 0), NV
 // 16-byte pieces per thread per chunk and activation term, FD = activation
-// fragments fetched one MFMA step ahead.  Activations are always requested two
-// chunks ahead: a wait for loads counts them in issue order, so waiting for
-// activations requested one chunk earlier would also wait for every weight
-// load of the ring issued before them.
+// fragments fetched one MFMA step ahead.
 template <int MT>
 struct Shape {
   static constexpr int MS = (MT + 1) / 2 * 2;
   static constexpr int NV = MS * 16 * 16 / kThr;
-  static constexpr bool A2 = true;
   static constexpr bool FD = MT <= 4;
 };
 
@@ -213,14 +264,25 @@ struct Shape {
 // = gate rows 16w + 0..15, n-tile 1 = the same up rows.  Output: h as two
 // bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo.
 constexpr int kGU_NT = 128;
+// Weight ring: 4 superchunks (K = 7168 gives 28, whole rounds).  Activation
+// ring: 4 chunks up to 64 rows of a block (the weight loads then get their
+// full ring distance, since a wait for an activation load also waits for
+// every older weight load), 2 above, where the accumulators need the
+// registers (measured: a longer activation ring does not help there).
+constexpr int kGuDB = 4;
+constexpr int gu_da(int mt) { return mt <= 4 ? 4 : 2; }
+// Scale-table pieces per thread and matrix: 128 rows x nb bytes in 16-byte
+// pieces over 512 threads covers nb <= 64 * kGuScaleU, i.e. K <= 12288.
+constexpr int kGuScaleU = 6;
 
-template <int MT, int DB>
+template <int MT, int DB, int DA>
 __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
                                              const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                              const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
                                              uint16_t* __restrict__ hterm) {
   using S = Shape<MT>;
   constexpr int NV = S::NV;
+  static_assert((2 * DB) % DA == 0, "activation ring must divide the unrolled chunks");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
@@ -231,24 +293,42 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   const int row = nt * kGU_NT + wid * 16 + nl;
   const bool rok = row < I;
   const uint32_t boff = rok ? (uint32_t)row * (uint32_t)(nb * 16) + 16u * g : kOOB;
-  const uint32_t soff = rok ? (uint32_t)row * (uint32_t)nb : kOOB;
   const int nchunks = H / kKC, nsc = nchunks / 2;
   uint16_t* buf0 = lds;
   uint16_t* buf1 = lds + kTile;
+  // scale table: gate rows, then up rows, of this row tile
+  uint8_t* tab = reinterpret_cast<uint8_t*>(lds + 2 * kTile);
+  const int pitch = scale_row_pitch(nb);
+  const uint8_t* tg = tab + (wid * 16 + nl) * pitch;
+  const uint8_t* tu = tg + kGU_NT * pitch;
+  const uint32_t tfirst = (uint32_t)(nt * kGU_NT) * (uint32_t)nb, ttotal = (uint32_t)kGU_NT * (uint32_t)nb;
+  SPieces<kGuScaleU> spg, spu;
+  scales_fetch<kGuScaleU>(spg, rsg, tfirst, ttotal);
+  scales_fetch<kGuScaleU>(spu, rsu, tfirst, ttotal);
 
+  // activation ring: slot j holds chunk c (c % DA == j) from its request
+  // until it is written to LDS at the end of chunk c - 1
+  uint32_t aoff[NV];
+  a_offsets<NV>(aoff, row_base);
+  ARegs<NV> ar[DA];
+  a_fetch<NV>(ar[0], rx, aoff, 0);
   BSuper rg[DB], ru[DB];
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d) {
-    load_bsuper(rg[d], rcg, rsg, boff, soff, d, nsc);
-    load_bsuper(ru[d], rcu, rsu, boff, soff, d, nsc);
+    load_bcodes(rg[d], rcg, boff, d, nsc);
+    load_bcodes(ru[d], rcu, boff, d, nsc);
   }
-  uint32_t aoff[NV];
-  a_offsets<NV>(aoff, row_base);
-  ARegs<NV> s0, s1;
-  a_fetch<NV>(s0, rx, aoff, 0);
-  if (S::A2) a_fetch<NV>(s1, rx, aoff, kKC * 2);
-  a_put<NV>(s0, buf0);
+#pragma unroll
+  for (int j = 1; j < DA; ++j) a_fetch<NV>(ar[j], rx, aoff, j < nchunks ? (uint32_t)j * (kKC * 2) : kFar);
+  scales_put<kGuScaleU>(spg, tab, nb, ttotal);
+  scales_put<kGuScaleU>(spu, tab + kGU_NT * pitch, nb, ttotal);
+  a_put<NV>(ar[0], buf0);
   __syncthreads();
+#pragma unroll
+  for (int d = 0; d < DB - 1; ++d) {
+    load_bscales(rg[d], tg, d, nsc);
+    load_bscales(ru[d], tu, d, nsc);
+  }
 
   f32x4 acc[MT][2];
 #pragma unroll
@@ -261,19 +341,17 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = 2 * (sc0 + d) + h;  // chunk; c % 2 == h
-        if (S::A2) {
-          const uint32_t kb = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
-          if (h == 0) a_fetch<NV>(s0, rx, aoff, kb);
-          else a_fetch<NV>(s1, rx, aoff, kb);
-        } else {
-          const uint32_t kb = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
-          a_fetch<NV>(s0, rx, aoff, kb);
+        const int cc = 2 * d + h, c = 2 * sc0 + cc;  // chunk; c % 2 == h, c % DA == cc % DA
+        {
+          const int cn = c + DA;  // refills the slot chunk c left (written to LDS before the last barrier)
+          a_fetch<NV>(ar[cc % DA], rx, aoff, cn < nchunks ? (uint32_t)cn * (kKC * 2) : kFar);
         }
         if (h == 0) {
           const int sn = sc0 + d + DB - 1;
-          load_bsuper(rg[(d + DB - 1) % DB], rcg, rsg, boff, soff, sn, nsc);
-          load_bsuper(ru[(d + DB - 1) % DB], rcu, rsu, boff, soff, sn, nsc);
+          load_bcodes(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc);
+          load_bcodes(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc);
+          load_bscales(rg[(d + DB - 1) % DB], tg, sn, nsc);
+          load_bscales(ru[(d + DB - 1) % DB], tu, sn, nsc);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint16_t* A = h == 0 ? buf0 : buf1;
@@ -302,13 +380,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
             acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bu, acc[m][1], 0, 0, 0);
           }
         }
-        // activations of chunk c+1 (fetched earlier) into the other buffer
-        if (S::A2) {
-          if (h == 0) a_put<NV>(s1, buf1);
-          else a_put<NV>(s0, buf0);
-        } else {
-          a_put<NV>(s0, h == 0 ? buf1 : buf0);
-        }
+        // activations of chunk c+1 (requested DA - 1 chunks ago) into the other buffer
+        a_put<NV>(ar[(cc + 1) % DA], h == 0 ? buf1 : buf0);
         __syncthreads();
       }
     }
@@ -353,14 +426,14 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
   __syncthreads();
   const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
   switch ((cnt + 15) / 16) {
-    case 1: gateup_block<1, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 2: gateup_block<2, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 3: gateup_block<3, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 4: gateup_block<4, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 5: gateup_block<5, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 6: gateup_block<6, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 7: gateup_block<7, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    default: gateup_block<8, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 1: gateup_block<1, kGuDB, gu_da(1)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 2: gateup_block<2, kGuDB, gu_da(2)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 3: gateup_block<3, kGuDB, gu_da(3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 4: gateup_block<4, kGuDB, gu_da(4)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 5: gateup_block<5, kGuDB, gu_da(5)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 6: gateup_block<6, kGuDB, gu_da(6)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 7: gateup_block<7, kGuDB, gu_da(7)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    default: gateup_block<8, kGuDB, gu_da(8)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
   }
 }
 
@@ -370,14 +443,21 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
 // pairs, both staged in LDS; each MFMA step runs once per term into the same
 // accumulator.  Output y[p][n] (fp32).
 constexpr int kDN_NT = 256;
+// Weight ring: 3 superchunks up to 64 rows of a block, 2 above (register
+// budget); K = 1536 gives 6 superchunks.  Activation ring: 2 chunks.
+constexpr int dn_db(int mt) { return mt <= 4 ? 3 : 2; }
+// Scale-table pieces per thread: 256 rows x nb bytes in 16-byte pieces over
+// 512 threads covers nb <= 32 * kDnScaleU, i.e. K <= 3072 (LDS caps it lower).
+constexpr int kDnScaleU = 3;
 
-template <int MT, int DB>
+template <int MT, int DB, int DA>
 __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, rsrc_t rh,
                                            const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                            const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
                                            float* __restrict__ ybuf) {
   using S = Shape<MT>;
   constexpr int NV = S::NV;
+  static_assert((2 * DB) % DA == 0, "activation ring must divide the unrolled chunks");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
@@ -386,34 +466,47 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
   const rsrc_t rs = mk_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
   const int nbk = I / 32;
   int row[2];
-  uint32_t boff[2], soff[2];
+  uint32_t boff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     row[j] = nt * kDN_NT + wid * 32 + 16 * j + nl;
     const bool ok = row[j] < H;
     boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nbk * 16) + 16u * g : kOOB;
-    soff[j] = ok ? (uint32_t)row[j] * (uint32_t)nbk : kOOB;
   }
   const int nchunks = I / kKC, nsc = nchunks / 2;
   const uint32_t lo_off = (uint32_t)((size_t)P * I * 2);  // byte offset of the lo term
-  // LDS: buffer b, term t at lds + (2b + t) * kTile
+  // LDS: buffer b, term t at lds + (2b + t) * kTile; then the row tile's scale table
+  uint8_t* tab = reinterpret_cast<uint8_t*>(lds + 4 * kTile);
+  const int pitch = scale_row_pitch(nbk);
+  const uint8_t* trow[2] = {tab + (wid * 32 + nl) * pitch, tab + (wid * 32 + 16 + nl) * pitch};
+  const uint32_t ttotal = (uint32_t)kDN_NT * (uint32_t)nbk;
+  SPieces<kDnScaleU> sp;
+  scales_fetch<kDnScaleU>(sp, rs, (uint32_t)nt * ttotal, ttotal);
+  // activation ring (both terms), as in the gate/up kernel
+  uint32_t aoff[NV];
+  a_offsets<NV>(aoff, row_base);
+  ARegs<NV> ah[DA], al[DA];
+  a_fetch<NV>(ah[0], rh, aoff, 0);
+  a_fetch<NV>(al[0], rh, aoff, lo_off);
   BSuper rb[DB][2];
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_bsuper(rb[d][j], rc, rs, boff[j], soff[j], d, nsc);
-  uint32_t aoff[NV];
-  a_offsets<NV>(aoff, row_base);
-  ARegs<NV> h0, l0, h1, l1;
-  a_fetch<NV>(h0, rh, aoff, 0);
-  a_fetch<NV>(l0, rh, aoff, lo_off);
-  if (S::A2) {
-    a_fetch<NV>(h1, rh, aoff, kKC * 2);
-    a_fetch<NV>(l1, rh, aoff, lo_off + kKC * 2);
+    for (int j = 0; j < 2; ++j) load_bcodes(rb[d][j], rc, boff[j], d, nsc);
+#pragma unroll
+  for (int j = 1; j < DA; ++j) {
+    const uint32_t kb = j < nchunks ? (uint32_t)j * (kKC * 2) : kFar;
+    a_fetch<NV>(ah[j], rh, aoff, kb);
+    a_fetch<NV>(al[j], rh, aoff, lo_off + kb);
   }
-  a_put<NV>(h0, lds);
-  a_put<NV>(l0, lds + kTile);
+  scales_put<kDnScaleU>(sp, tab, nbk, ttotal);
+  a_put<NV>(ah[0], lds);
+  a_put<NV>(al[0], lds + kTile);
   __syncthreads();
+#pragma unroll
+  for (int d = 0; d < DB - 1; ++d)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_bscales(rb[d][j], trow[j], d, nsc);
 
   f32x4 acc[MT][2];
 #pragma unroll
@@ -424,25 +517,20 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = 2 * (sc0 + d) + h;
-        if (S::A2) {
-          const uint32_t kb = c + 2 < nchunks ? (uint32_t)(c + 2) * (kKC * 2) : kFar;
-          if (h == 0) {
-            a_fetch<NV>(h0, rh, aoff, kb);
-            a_fetch<NV>(l0, rh, aoff, lo_off + kb);
-          } else {
-            a_fetch<NV>(h1, rh, aoff, kb);
-            a_fetch<NV>(l1, rh, aoff, lo_off + kb);
-          }
-        } else {
-          const uint32_t kb = c + 1 < nchunks ? (uint32_t)(c + 1) * (kKC * 2) : kFar;
-          a_fetch<NV>(h0, rh, aoff, kb);
-          a_fetch<NV>(l0, rh, aoff, lo_off + kb);
+        const int cc = 2 * d + h, c = 2 * sc0 + cc;
+        {
+          const int cn = c + DA;
+          const uint32_t kb = cn < nchunks ? (uint32_t)cn * (kKC * 2) : kFar;
+          a_fetch<NV>(ah[cc % DA], rh, aoff, kb);
+          a_fetch<NV>(al[cc % DA], rh, aoff, lo_off + kb);
         }
         if (h == 0) {
           const int sn = sc0 + d + DB - 1;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) load_bsuper(rb[(d + DB - 1) % DB][j], rc, rs, boff[j], soff[j], sn, nsc);
+          for (int j = 0; j < 2; ++j) {
+            load_bcodes(rb[(d + DB - 1) % DB][j], rc, boff[j], sn, nsc);
+            load_bscales(rb[(d + DB - 1) % DB][j], trow[j], sn, nsc);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint16_t* Ah = lds + h * 2 * kTile;
@@ -463,18 +551,8 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
           }
         }
         uint16_t* nxt = lds + (h ^ 1) * 2 * kTile;
-        if (S::A2) {
-          if (h == 0) {
-            a_put<NV>(h1, nxt);
-            a_put<NV>(l1, nxt + kTile);
-          } else {
-            a_put<NV>(h0, nxt);
-            a_put<NV>(l0, nxt + kTile);
-          }
-        } else {
-          a_put<NV>(h0, nxt);
-          a_put<NV>(l0, nxt + kTile);
-        }
+        a_put<NV>(ah[(cc + 1) % DA], nxt);
+        a_put<NV>(al[(cc + 1) % DA], nxt + kTile);
         __syncthreads();
       }
     }
@@ -516,14 +594,14 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   __syncthreads();
   const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
   switch ((cnt + 15) / 16) {
-    case 1: down_block<1, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 2: down_block<2, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 3: down_block<3, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 4: down_block<4, 3>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 5: down_block<5, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 6: down_block<6, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 7: down_block<7, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    default: down_block<8, 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 1: down_block<1, dn_db(1), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 2: down_block<2, dn_db(2), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 3: down_block<3, dn_db(3), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 4: down_block<4, dn_db(4), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 5: down_block<5, dn_db(5), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 6: down_block<6, dn_db(6), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 7: down_block<7, dn_db(7), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    default: down_block<8, dn_db(8), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
   }
 }
 
@@ -646,11 +724,23 @@ static unsigned items_grid(int max_blocks, int ntiles) {
   return (unsigned)rounds * 8u * (unsigned)ntiles;
 }
 
+// LDS per workgroup on gfx950, and the kernels' static LDS (pid, row_base).
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kStaticLds = 2 * kMB * 4;
+static size_t gateup_lds(int H) { return (size_t)2 * kTile * 2 + (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
+static size_t down_lds(int I) { return (size_t)4 * kTile * 2 + (size_t)kDN_NT * scale_row_pitch(I / 32); }
+
+bool grouped_shape_ok(int64_t H, int64_t I) {
+  if (H <= 0 || I <= 0 || H % 256 != 0 || I % 256 != 0) return false;
+  if (H / 32 > 64 * kGuScaleU || I / 32 > 32 * kDnScaleU) return false;
+  return gateup_lds((int)H) + kStaticLds <= kLdsBytes && down_lds((int)I) + kStaticLds <= kLdsBytes;
+}
+
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
                               const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
                               int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s) {
   const int ntiles = (I + kGU_NT - 1) / kGU_NT;
-  const size_t lds = (size_t)2 * kTile * 2;
+  const size_t lds = gateup_lds(H);
   k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(
       x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, hterm);
   return hipGetLastError();
@@ -660,7 +750,7 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s) {
   const int ntiles = (H + kDN_NT - 1) / kDN_NT;
-  const size_t lds = (size_t)4 * kTile * 2;
+  const size_t lds = down_lds(I);
   k_down_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
                                                                        scales, H, I, E, P, max_blocks, ntiles, ybuf);
   return hipGetLastError();
