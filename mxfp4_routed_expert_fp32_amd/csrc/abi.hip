@@ -65,8 +65,9 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, total;
+  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, rpart, total;
   int max_blocks;
+  bool has_rpart;
 };
 
 int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
@@ -89,6 +90,11 @@ int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) 
   L->max_blocks = moe::max_expert_blocks((int)Tk, d->n_experts);
   L->blocks = c.take((size_t)L->max_blocks * 16);
   L->nblocks = c.take(4);
+  // partial router sums for few tokens on the MFMA router
+  L->has_rpart = d->hidden % 128 == 0 && moe::router_mfma_splits(T, d->hidden) > 1;
+  size_t rp = 0;
+  if (L->has_rpart && !mul_ok(TE, (size_t)moe::router_mfma_splits(T, d->hidden) * 4, &rp)) return MOE_ERR_OVERFLOW;
+  L->rpart = c.take(rp);
   L->total = c.take(0);
   if (c.overflow) return MOE_ERR_OVERFLOW;
   // pair indices are int32 on the device; MFMA-path byte offsets are 32-bit
@@ -121,10 +127,12 @@ bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
 
 // Router logits: many bf16 tokens go to the MFMA kernel (fp32 weights split
 // into three exact bf16 terms), a few tokens or fp32 tokens to the GEMV.
+// `part` (optional) is room for the MFMA router's partial sums.
 hipError_t router(const moe_layer_desc* d, const void* x, bool x_f32, const float* wr, const float* bias,
-                  int32_t T, float* logits, hipStream_t s) {
+                  int32_t T, float* logits, float* part, hipStream_t s) {
   if (T > 8 && !x_f32 && d->hidden % 128 == 0)
-    return moe::launch_router_mfma(static_cast<const uint16_t*>(x), wr, bias, T, d->hidden, d->n_experts, logits, s);
+    return moe::launch_router_mfma(static_cast<const uint16_t*>(x), wr, bias, T, d->hidden, d->n_experts, logits,
+                                   part, s);
   return moe::launch_router_logits(x, x_f32, wr, bias, T, d->hidden, d->n_experts, logits, s);
 }
 
@@ -184,7 +192,8 @@ int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   float* w = w_out ? w_out : reinterpret_cast<float*>(ws + L.w);
   const bool xf = x_dtype == MOE_DTYPE_F32;
-  MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, s)));
+  float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
+  MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
   if (T > 1 && !xf && grouped_fits(d, T, (int64_t)T * k)) {
     // prefill form: top-k, then sort + grouped GEMMs
     MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
@@ -339,7 +348,8 @@ int moe_router_logits(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (n_tokens < 1 || n_tokens > kMaxTokens) return MOE_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_ALIGN;
-  return dev(router(d, x, x_dtype == MOE_DTYPE_F32, router_w, router_bias, n_tokens, logits, as_stream(stream)));
+  return dev(router(d, x, x_dtype == MOE_DTYPE_F32, router_w, router_bias, n_tokens, logits, nullptr,
+                    as_stream(stream)));
 }
 
 int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* idx,

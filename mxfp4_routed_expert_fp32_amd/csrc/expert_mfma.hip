@@ -21,6 +21,9 @@
 // K chunk, lane group g = l/16 supplies K = chunk + 32*g + 8*s .. +8, so each
 // lane reads one whole 16-byte code block (32 codes) per chunk and uses a
 // quarter of it per step.
+#include <algorithm>
+#include <cstdint>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -71,37 +74,6 @@ __device__ __forceinline__ void decode_item(int ntiles, int* eb, int* nt) {
   const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
   *eb = (r / ntiles) * 8 + xcd;
   *nt = r % ntiles;
-}
-
-// Stage rows [0, kMB) x K [k0, k0+kKC) of a bf16 source through registers:
-// thread t of the 512 moves 16-byte pieces q = t + 512*v (row q/16, piece
-// q%16).  Rows past `cnt` (or with a negative source row) are zero.
-constexpr int kThreads = 512;
-struct AStage {
-  uint4 v[4];
-};
-
-__device__ __forceinline__ void stage_load(AStage& a, const uint16_t* __restrict__ src, size_t row_stride,
-                                           const int32_t* rows_lds, int cnt, int k0) {
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int q = threadIdx.x + kThreads * v;
-    const int row = q / 16, piece = q % 16;
-    const int sr = row < cnt ? rows_lds[row] : -1;
-    if (sr >= 0)
-      a.v[v] = *reinterpret_cast<const uint4*>(src + (size_t)sr * row_stride + k0 + piece * 8);
-    else
-      a.v[v] = make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-__device__ __forceinline__ void stage_store(const AStage& a, uint16_t* lds) {
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int q = threadIdx.x + kThreads * v;
-    const int row = q / 16, piece = q % 16;
-    *reinterpret_cast<uint4*>(lds + row * kLdsRow + piece * 8) = a.v[v];
-  }
 }
 
 constexpr int kTile = kMB * kLdsRow;  // bf16 elements of one LDS activation tile
@@ -606,107 +578,173 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
 }
 
 // ---------------------------------------------------------------- router logits (many tokens)
-// logits[t][e] = x[t] . Wr[e] (+ b[e]) for bf16 activations, on MFMA: each
-// fp32 router weight w is split into three bf16 terms w = w0 + w1 + w2
-// (w0 = bf16(w), w1 = bf16(w - w0), w2 = w - w0 - w1; exact for every normal
-// fp32 whose low terms stay above the bf16 subnormal range), so every
-// product is exact and the sum is fp32.  Tile: 128 tokens x 128 experts;
-// wave w (of 8) owns experts 16w .. 16w+15, all token m-tiles.
+// logits[t][e] = x[t] . Wr[e] (+ b[e]) for bf16 activations, on MFMA.  Each
+// fp32 router weight w is split into three bf16 terms w0 = bf16(w),
+// w1 = bf16(w - w0), w2 = bf16(w - w0 - w1), rounding to nearest even; the
+// split is exact for every normal fp32 whose low terms stay above the bf16
+// subnormal range, so every product is exact and only fp32 sums round.
+// Tile: up to 128 tokens (MT m-tiles) x 128 experts; wave w owns experts
+// 16w .. 16w+15 and all m-tiles.  K runs in slices of two 128-wide chunks;
+// each slice is accumulated from zero and added to the running sum in slice
+// order, so the result does not depend on how slices are spread over
+// workgroups: a workgroup runs all slices of its tile, or (few tokens, where
+// tiles alone cannot fill the chip) each slice runs in a workgroup of its own
+// and writes a partial sum that k_router_reduce adds up in the same order.
 constexpr int kRT_NT = 128;
+constexpr int kRtSlice = 2;          // chunks per slice
+constexpr int kRtSplitTokens = 256;  // slices run in workgroups of their own up to this many tokens
 
-// Split two fp32 weights into three packed bf16 pairs (term 0, 1, 2).
-__device__ __forceinline__ void split3_pair(uint32_t a, uint32_t b, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
-  const float wa = __uint_as_float(a), wb = __uint_as_float(b);
-  const uint32_t a0 = f32_to_bf16_rne(wa), b0 = f32_to_bf16_rne(wb);
-  const float ra = wa - __uint_as_float(a0 << 16), rb = wb - __uint_as_float(b0 << 16);
-  const uint32_t a1 = f32_to_bf16_rne(ra), b1 = f32_to_bf16_rne(rb);
-  const uint32_t a2 = f32_to_bf16_rne(ra - __uint_as_float(a1 << 16));
-  const uint32_t b2 = f32_to_bf16_rne(rb - __uint_as_float(b1 << 16));
-  p0 = a0 | (b0 << 16);
-  p1 = a1 | (b1 << 16);
-  p2 = a2 | (b2 << 16);
-}
+// This lane's 32 weights of one chunk: K = 32g .. 32g+31 of the chunk.
+struct WChunk {
+  u32x4 q[8];
+};
 
-__device__ __forceinline__ void split3(const u32x4& q0, const u32x4& q1, bf16x8& t0, bf16x8& t1, bf16x8& t2) {
-  uint32_t u0[4], u1[4], u2[4];
-  split3_pair(q0.x, q0.y, u0[0], u1[0], u2[0]);
-  split3_pair(q0.z, q0.w, u0[1], u1[1], u2[1]);
-  split3_pair(q1.x, q1.y, u0[2], u1[2], u2[2]);
-  split3_pair(q1.z, q1.w, u0[3], u1[3], u2[3]);
-  __builtin_memcpy(&t0, &u0, 16);
-  __builtin_memcpy(&t1, &u1, 16);
-  __builtin_memcpy(&t2, &u2, 16);
-}
-
-__global__ __launch_bounds__(kThreads, 1) void k_router_mfma(const uint16_t* __restrict__ x,
-                                                             const float* __restrict__ wr,
-                                                             const float* __restrict__ bias, int T, int H, int E,
-                                                             int ntiles, float* __restrict__ logits) {
-  extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
-  __shared__ int32_t tok[kMB];
-  const int mt = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
-  const int t0 = mt * kMB;
-  const int cnt = min(kMB, T - t0);
-  for (int i = threadIdx.x; i < kMB; i += kThreads) tok[i] = i < cnt ? t0 + i : -1;
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const int nl = lane % 16, g = lane / 16;
-  const int mtiles = (cnt + 15) / 16;
-  const int ex = nt * kRT_NT + wid * 16 + nl;
-  const bool eok = ex < E;
-  const rsrc_t rw = mk_rsrc(wr, (uint32_t)((size_t)E * H * 4));
-  const uint32_t woff = (uint32_t)ex * (uint32_t)(H * 4) + 128u * g;  // 32 floats of the lane's K slice
-  const int nchunks = H / kKC;
-  __syncthreads();
-  AStage st;
-  stage_load(st, x, (size_t)H, tok, cnt, 0);
-  stage_store(st, a_lds);
-  u32x4 wq[8];
+__device__ __forceinline__ void load_wchunk(WChunk& w, rsrc_t rw, uint32_t woff, int c, int c_end) {
+  const bool ok = c < c_end;
 #pragma unroll
   for (int v = 0; v < 8; ++v)
-    wq[v] = __builtin_amdgcn_raw_buffer_load_b128(rw, eok ? woff + 16u * v : 0x80000000u, 0, 0);
+    w.q[v] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? woff + (uint32_t)c * 512u + 16u * v : kOOB, 0, 0);
+}
+
+// Three bf16 terms of 8 fp32 weights (two packed quads), hardware round to
+// nearest even.
+__device__ __forceinline__ void split3(const u32x4& q0, const u32x4& q1, bf16x8& t0, bf16x8& t1, bf16x8& t2) {
+  const uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 w = {__uint_as_float(in[2 * j]), __uint_as_float(in[2 * j + 1])};
+    const bf16x2 a = __builtin_convertvector(w, bf16x2);
+    const f32x2 r = w - __builtin_convertvector(a, f32x2);
+    const bf16x2 b = __builtin_convertvector(r, bf16x2);
+    const bf16x2 c = __builtin_convertvector(r - __builtin_convertvector(b, f32x2), bf16x2);
+    t0[2 * j] = a[0]; t0[2 * j + 1] = a[1];
+    t1[2 * j] = b[0]; t1[2 * j + 1] = b[1];
+    t2[2 * j] = c[0]; t2[2 * j + 1] = c[1];
+  }
+}
+
+// Chunks [c_begin, c_end) of one tile; c_begin is a slice start.  Writes the
+// tile's sums to out[t][e] (row stride E) plus bias when `bias_add`.
+template <int MT, int DW>
+__device__ __forceinline__ void router_block(rsrc_t rx, rsrc_t rw, const float* __restrict__ bias, bool bias_add,
+                                             int H, int E, int nt, int c_begin, int c_end, int t0, int cnt,
+                                             const uint32_t* row_base, uint16_t* lds, float* __restrict__ out) {
+  using S = Shape<MT>;
+  constexpr int NV = S::NV;
+  static_assert(DW % kRtSlice == 0, "the weight ring holds whole slices");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int ex = nt * kRT_NT + wid * 16 + nl;
+  const uint32_t woff = ex < E ? (uint32_t)ex * (uint32_t)(H * 4) + 128u * g : kOOB;
+  const int last_slice = (c_end + kRtSlice - 1) / kRtSlice;  // slices below this index are real
+  uint16_t* buf0 = lds;
+  uint16_t* buf1 = lds + kTile;
+
+  uint32_t aoff[NV];
+  a_offsets<NV>(aoff, row_base);
+  ARegs<NV> ar[2];  // chunk c's rows in slot c % 2 (c_begin is even)
+  a_fetch<NV>(ar[0], rx, aoff, (uint32_t)c_begin * (kKC * 2));
+  WChunk wq[DW];
+#pragma unroll
+  for (int d = 0; d < DW - 1; ++d) load_wchunk(wq[d], rw, woff, c_begin + d, c_end);
+  a_fetch<NV>(ar[1], rx, aoff, c_begin + 1 < c_end ? (uint32_t)(c_begin + 1) * (kKC * 2) : kFar);
+  a_put<NV>(ar[0], buf0);
   __syncthreads();
-  f32x4 acc[8];
+
+  f32x4 acc[MT], tot[MT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    bf16x8 bt[4][3];
+  for (int m = 0; m < MT; ++m) acc[m] = tot[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = c_begin; c0 < c_end; c0 += DW) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) split3(wq[2 * s], wq[2 * s + 1], bt[s][0], bt[s][1], bt[s][2]);
-    if (more) {
+    for (int d = 0; d < DW; ++d) {
+      const int c = c0 + d;  // c % 2 == d % 2
+      a_fetch<NV>(ar[d & 1], rx, aoff, c + 2 < c_end ? (uint32_t)(c + 2) * (kKC * 2) : kFar);
+      load_wchunk(wq[(d + DW - 1) % DW], rw, woff, c + DW - 1, c_end);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+      const uint16_t* A = (d & 1) ? buf1 : buf0;
 #pragma unroll
-      for (int v = 0; v < 8; ++v)
-        wq[v] = __builtin_amdgcn_raw_buffer_load_b128(rw, eok ? woff + (uint32_t)(c + 1) * 512u + 16u * v : 0x80000000u,
-                                                       0, 0);
-      stage_load(st, x, (size_t)H, tok, cnt, (c + 1) * kKC);
-    }
-    const uint16_t* A = a_lds + (c % 2) * kTile;
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 b0, b1, b2;
+        split3(wq[d].q[2 * st], wq[d].q[2 * st + 1], b0, b1, b2);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (m < mtiles) {
-          const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(A + (m * 16 + nl) * kLdsRow + 32 * g + 8 * s));
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bt[s][0], acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bt[s][1], acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bt[s][2], acc[m], 0, 0, 0);
+        for (int m = 0; m < MT; ++m) {
+          const bf16x8 af = lds_frag(A, m * 16 + nl, 32 * g + 8 * st);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b2, acc[m], 0, 0, 0);
         }
       }
-    }
-    if (more) stage_store(st, a_lds + ((c + 1) % 2) * kTile);
-    __syncthreads();
-  }
-  const float b = (bias && eok) ? bias[ex] : 0.0f;
+      if (d % kRtSlice == kRtSlice - 1) {  // end of a slice: fold it into the running sum
+        if (c / kRtSlice < last_slice) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m < mtiles) {
+          for (int m = 0; m < MT; ++m) tot[m] += acc[m];
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      a_put<NV>(ar[(d + 1) & 1], (d & 1) ? buf0 : buf1);
+      __syncthreads();
+    }
+  }
+  if (ex < E) {
+    const float b = (bias_add && bias) ? bias[ex] : 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int slot = m * 16 + 4 * g + r;
-        if (slot < cnt && eok) logits[(size_t)(t0 + slot) * E + ex] = acc[m][r] + b;
+        if (slot < cnt) out[(size_t)(t0 + slot) * E + ex] = bias_add ? tot[m][r] + b : tot[m][r];
       }
     }
   }
+}
+
+// Workgroup b: split = b % nsplit, expert tile (b / nsplit) % ntiles, token
+// tile b / (nsplit * ntiles).  nsplit == 1: every slice, logits out (with
+// bias); otherwise slice `split` only, its partial sums to part[split][t][e].
+__global__ __launch_bounds__(kThr, 1) void k_router_mfma(const uint16_t* __restrict__ x,
+                                                        const float* __restrict__ wr,
+                                                        const float* __restrict__ bias, int T, int H, int E,
+                                                        int ntiles, int nsplit, float* __restrict__ part,
+                                                        float* __restrict__ logits) {
+  extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
+  __shared__ uint32_t row_base[kMB];
+  const int split = blockIdx.x % nsplit, r = blockIdx.x / nsplit;
+  const int nt = r % ntiles, mt = r / ntiles;
+  const int t0 = mt * kMB;
+  const int cnt = min(kMB, T - t0);
+  for (int i = threadIdx.x; i < kMB; i += kThr) row_base[i] = i < cnt ? (uint32_t)(t0 + i) * (uint32_t)(H * 2) : kFar;
+  __syncthreads();
+  const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
+  const rsrc_t rw = mk_rsrc(wr, (uint32_t)((size_t)E * H * 4));
+  const int nchunks = H / kKC;
+  const bool whole = nsplit == 1;
+  const int c_begin = whole ? 0 : split * kRtSlice;
+  const int c_end = whole ? nchunks : min(nchunks, c_begin + kRtSlice);
+  float* out = whole ? logits : part + (size_t)split * T * E;
+  switch ((cnt + 15) / 16) {
+    case 1: router_block<1, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 2: router_block<2, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 3: router_block<3, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 4: router_block<4, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 5: router_block<5, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 6: router_block<6, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 7: router_block<7, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    default: router_block<8, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+  }
+}
+
+// logits[i] = (sum over splits s in order of part[s][i]) + bias: the same
+// additions, in the same order, as a workgroup that runs every slice.
+__global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int nsplit, int T, int E,
+                                                       const float* __restrict__ bias, float* __restrict__ logits) {
+  const size_t n = (size_t)T * E;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.0f;
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) v += part[(size_t)sp * n + i];
+  logits[i] = v + (bias ? bias[i % E] : 0.0f);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -756,12 +794,28 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
   return hipGetLastError();
 }
 
+int router_mfma_splits(int T, int H) {
+  return T <= kRtSplitTokens ? (H / kKC + kRtSlice - 1) / kRtSlice : 1;
+}
+
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, hipStream_t s) {
+                              float* logits, float* part, hipStream_t s) {
   const int ntiles = (E + kRT_NT - 1) / kRT_NT;
-  const int mtiles = (T + kMB - 1) / kMB;
   const size_t lds = (size_t)2 * kTile * 2;
-  k_router_mfma<<<dim3((unsigned)(mtiles * ntiles)), kThreads, lds, s>>>(x, wr, bias, T, H, E, ntiles, logits);
+  const int nsplit = part ? router_mfma_splits(T, H) : 1;
+  // token batches keep x's 32-bit buffer offsets (and the kFar sentinel) in range
+  const int tb = (int)std::min<int64_t>(T, ((int64_t{1} << 29) / ((int64_t)H * 2)) / kMB * kMB);
+  for (int t0 = 0; t0 < T; t0 += tb) {
+    const int n = std::min(tb, T - t0);
+    const int mtiles = (n + kMB - 1) / kMB;
+    k_router_mfma<<<dim3((unsigned)(mtiles * ntiles * nsplit)), kThr, lds, s>>>(
+        x + (size_t)t0 * H, wr, bias, n, H, E, ntiles, nsplit, part, logits + (size_t)t0 * E);
+    if (nsplit > 1) {
+      const size_t cells = (size_t)n * E;
+      k_router_reduce<<<dim3((unsigned)((cells + 255) / 256)), 256, 0, s>>>(part, nsplit, n, E, bias,
+                                                                          logits + (size_t)t0 * E);
+    }
+  }
   return hipGetLastError();
 }
 

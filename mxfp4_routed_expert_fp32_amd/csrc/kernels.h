@@ -33,7 +33,7 @@ hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H
 // gate/up + SwiGLU and down grouped GEMMs on MFMA.  hterm holds h as two bf16
 // terms, [2][P][I].  grouped_shape_ok: H and I multiples of 256 whose
 // per-workgroup scale tables fit LDS beside the activation tiles
-// (H <= 11264, I <= 2560).
+// (H <= 11264, I <= 2560; layers have H <= 8192).
 bool grouped_shape_ok(int64_t H, int64_t I);
 int max_expert_blocks(int P, int E);
 hipError_t launch_expert_blocks(const int32_t* offsets, int E, int max_blocks, int4* blocks, int32_t* nblocks,
@@ -45,9 +45,14 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s);
 
-// Router logits for many bf16 tokens on MFMA (H a multiple of 128).
+// Router logits for many bf16 tokens on MFMA (H a multiple of 128).  With
+// `part` (router_mfma_splits(T, H) * T * E floats) and few tokens, K slices
+// run in workgroups of their own and a second kernel adds their partial sums
+// in order; without it one workgroup runs all slices of its tile.  Both give
+// the same bits.
+int router_mfma_splits(int T, int H);
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, hipStream_t s);
+                              float* logits, float* part, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,

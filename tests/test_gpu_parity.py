@@ -159,6 +159,31 @@ def test_router_mfma_logits_within_bound(T, H, E):
     P.assert_logits_close(got, oracle.router_logits(xf, wr_h, bias=b), xf, wr_h, bias=b)
 
 
+@pytest.mark.parametrize("T,H,E", [(64, 1024, 130), (200, 7168, 96), (37, 640, 40), (256, 512, 8)])
+def test_router_split_k_matches_whole_tiles(T, H, E):
+    """Up to 256 tokens, the forward runs the MFMA router's K slices in
+    workgroups of their own and adds their partial sums in a second kernel;
+    the router stage entry (no workspace) runs every slice of a tile in one
+    workgroup.  Both add the same slice sums in the same order, so the logits
+    are the same bits; H = 640 has an odd number of 128-wide chunks."""
+    w = synth.Workload("rs", 66, T, H, 256, E, 2, "bf16", weight_seed=7800 + T + H)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    b = np.random.default_rng(T + 1).standard_normal(E).astype(np.float32)
+    bias = torch.from_numpy(b).to(DEV)
+    _, lf, _, _ = run_forward(desc, w, x, wr, bias, codes, scales, 2)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    moe.moe_router_logits(desc, x, wr, bias, logits)
+    torch.cuda.synchronize()
+    ls = logits.cpu().numpy()
+    assert np.array_equal(lf.view(np.uint32), ls.view(np.uint32))
+    xf = synth.tokens_f32(w, range(T))
+    wr_h = wr.cpu().numpy()
+    P.assert_logits_close(lf, oracle.router_logits(xf, wr_h, bias=b), xf, wr_h, bias=b)
+
+
 def test_sort_by_expert_matches_stable_sort():
     rng = np.random.default_rng(9)
     for T, E, k in [(1, 8, 2), (64, 896, 16), (4096, 896, 16), (130, 50, 5)]:
@@ -280,11 +305,16 @@ def test_rmsnorm_and_residual():
 
 @pytest.mark.parametrize("H,I,E,k,T,hot", [(256, 256, 8, 2, 37, False), (512, 256, 16, 4, 65, False),
                                            (256, 512, 4, 2, 300, True), (1024, 768, 12, 3, 130, True),
-                                           (768, 1280, 6, 2, 45, False)])
+                                           (768, 1280, 6, 2, 45, False),
+                                           (8192, 256, 2, 1, 20, False), (256, 2560, 4, 2, 37, False),
+                                           (256, 2816, 4, 2, 9, False)])
 def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     """T > 1 with bf16 activations runs the sort + MFMA grouped GEMMs (H, I
     multiples of 256; an odd count of 256-wide K superchunks included); expert
-    blocks are ragged, and `hot` makes one expert take more than 128 tokens."""
+    blocks are ragged, and `hot` makes one expert take more than 128 tokens.
+    H = 8192 is the largest hidden size a layer may have; I = 2560 is the
+    largest scale table the grouped down kernel keeps in LDS, and I = 2816 is
+    past that and takes the decode-form kernels."""
     w = synth.Workload("g", 63, T, H, I, E, k, "bf16", weight_seed=7500 + H + E + T)
     c, s, ex = experts_host(w)
     desc, codes, scales = pack_whole(w, c, s)
