@@ -198,10 +198,10 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
 
 /*
  * Prefill form, stage by stage: the kernels moe_mxfp4_forward runs for more
- * than one bf16 token when H and I are multiples of 256 with I <= 2560 (the
- * grouped GEMMs on bf16 MFMA; each workgroup keeps its weight rows' scales in
- * LDS, which bounds the down projection's K), for stage-level checks and timing.
- * Other shapes take the decode-form kernels.  After moe_sort_by_expert:
+ * than one bf16 token when H and I are multiples of 256 (the grouped GEMMs on
+ * bf16 MFMA), for stage-level checks and timing; the forward runs them over
+ * batches of tokens small enough for the limits below.  Other shapes take the
+ * decode-form kernels.  After moe_sort_by_expert:
  *  - moe_max_expert_blocks: capacity of the block list for n_pairs pairs,
  *    ceil(n_pairs / 128) + min(n_pairs, n_experts).
  *  - moe_expert_blocks: cut each expert's sorted pairs into blocks of at most
@@ -216,7 +216,7 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
  *    hterm[1][p]), for every pair named by a block.
  * Blocks that do not name a valid expert and pair range, and pair ids outside
  * [0, n_pairs), are skipped on the device.  MOE_ERR_UNSUPPORTED if H or I is
- * not a multiple of 256, I > 2560, or x or hterm reaches 1 GiB.
+ * not a multiple of 256, x or hterm reaches 1 GiB, or y reaches 2 GiB.
  */
 int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks);
 int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,

@@ -11,6 +11,8 @@
 #include <new>
 
 #include "moe_mxfp4.h"
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -116,13 +118,25 @@ int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
   return MOE_OK;
 }
 
-// The grouped GEMMs tile K by 256 (weights) and 128 (activations), keep each
-// row tile's scales in LDS (which caps H and I), and address activations with
-// 32-bit buffer offsets and an out-of-range sentinel at 1 GiB: x (bf16) and
-// the two bf16 terms of h must each stay below that.
+// The grouped GEMMs tile K by 256 (weights) and 128 (activations), keep the
+// gate/up row tile's scales in LDS (which caps H), and address activations
+// with 32-bit buffer offsets and an out-of-range sentinel at 1 GiB: x (bf16)
+// and the two bf16 terms of h must each stay below that; y (fp32) is stored
+// through 32-bit offsets below 2 GiB.
 bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
   return moe::grouped_shape_ok(d->hidden, d->inter) && T * d->hidden * 2 < (int64_t{1} << 30) &&
-         P * d->inter * 4 < (int64_t{1} << 30);
+         P * d->inter * 4 < (int64_t{1} << 30) && P * d->hidden * 4 < (int64_t{1} << 31);
+}
+
+// Tokens per batch of the prefill form (larger T runs in batches of this
+// many tokens, which are independent); 0 if the shape has no prefill form.
+int64_t grouped_batch(const moe_layer_desc* d, int32_t k) {
+  if (!moe::grouped_shape_ok(d->hidden, d->inter)) return 0;
+  const int64_t H = d->hidden, I = d->inter;
+  int64_t tb = ((int64_t{1} << 30) - 1) / (H * 2);
+  tb = std::min(tb, ((int64_t{1} << 30) - 1) / (k * I * 4));
+  tb = std::min(tb, ((int64_t{1} << 31) - 1) / (k * H * 4));
+  return tb >= 2 ? tb : 0;
 }
 
 // Router logits: many bf16 tokens go to the MFMA kernel (fp32 weights split
@@ -147,19 +161,25 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  if (T > 1 && !x_f32 && grouped_fits(d, T, P)) {
-    // prefill form: sort pairs by expert, grouped GEMMs on MFMA, combine
+  const int64_t tb = grouped_batch(d, k);
+  if (T > 1 && !x_f32 && tb > 0) {
+    // prefill form, per batch of tokens: sort pairs by expert, grouped GEMMs on MFMA, combine
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
     int4* blocks = reinterpret_cast<int4*>(ws + L.blocks);
     int32_t* nblocks = reinterpret_cast<int32_t*>(ws + L.nblocks);
-    uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][P][I] bf16, same bytes as h
-    MOE_TRY(dev(moe::launch_sort_by_expert(idx, T, E, k, offsets, pairs, s)));
-    MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
-    MOE_TRY(dev(moe::launch_gateup_mfma(static_cast<const uint16_t*>(x), T, pairs, blocks, nblocks, L.max_blocks, c,
-                                        sc, H, I, E, k, P, hterm, s)));
-    MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, P, y, s)));
-    MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
+    uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][n*k][I] bf16, same bytes as h
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    for (int64_t t0 = 0; t0 < T; t0 += tb) {
+      const int n = (int)std::min<int64_t>(tb, T - t0);
+      const int Pn = n * k;
+      MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, s)));
+      MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
+      MOE_TRY(dev(moe::launch_gateup_mfma(xb + t0 * H, n, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, k,
+                                          Pn, hterm, s)));
+      MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, Pn, y, s)));
+      MOE_TRY(dev(moe::launch_combine(y, w + t0 * k, n, k, H, resid ? resid + t0 * H : nullptr, out + t0 * H, s)));
+    }
     return MOE_OK;
   }
   MOE_TRY(dev(moe::launch_gateup_gemv(x, x_f32, idx, P, k, c, sc, H, I, E, h, s)));
@@ -194,7 +214,7 @@ int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const 
   const bool xf = x_dtype == MOE_DTYPE_F32;
   float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
   MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
-  if (T > 1 && !xf && grouped_fits(d, T, (int64_t)T * k)) {
+  if (T > 1 && !xf && grouped_batch(d, k) > 0) {
     // prefill form: top-k, then sort + grouped GEMMs
     MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
     return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);

@@ -414,16 +414,39 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
 // 32w + 16..31.  The activations are the two bf16 terms of h for the block's
 // pairs, both staged in LDS; each MFMA step runs once per term into the same
 // accumulator.  Output y[p][n] (fp32).
+// K = I is short (1536: 12 chunks), so a workgroup runs kDnTiles row tiles
+// of its expert block back to back: the weight and activation rings run on
+// across tile boundaries (the next tile's first weights are in flight while
+// this tile finishes), and only the first tile waits for a cold pipeline.
+// Scales come straight from memory here: a row's I/32 scale bytes are few
+// (48), so 16 rows share a handful of lines that stay in L2.
 constexpr int kDN_NT = 256;
+constexpr int kDnTiles = 4;
 // Weight ring: 3 superchunks up to 64 rows of a block, 2 above (register
-// budget); K = 1536 gives 6 superchunks.  Activation ring: 2 chunks.
+// budget).  Activation ring: 2 chunks.
 constexpr int dn_db(int mt) { return mt <= 4 ? 3 : 2; }
-// Scale-table pieces per thread: 256 rows x nb bytes in 16-byte pieces over
-// 512 threads covers nb <= 32 * kDnScaleU, i.e. K <= 3072 (LDS caps it lower).
-constexpr int kDnScaleU = 3;
 
+// Codes and scales of one superchunk from memory.  The lane's part of the
+// offsets (its row in the first tile, its code block) is a vector offset; the
+// workgroup-uniform part (tile and superchunk) is a scalar offset, used only
+// when the superchunk is real (ok, uniform): otherwise the vector offset is
+// out of range and the scalar offset 0.
+__device__ __forceinline__ void load_bsuper_direct(BSuper& b, rsrc_t rc, rsrc_t rs, uint32_t vcode, uint32_t vscale,
+                                                   uint32_t scode, uint32_t sscale, bool ok) {
+  const uint32_t vc = ok ? vcode : kOOB, vs = ok ? vscale : kOOB;
+  const uint32_t sc_ = ok ? scode : 0u, ss_ = ok ? sscale : 0u;
+  b.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc, sc_, 0);
+  b.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 64u, sc_, 0);
+  const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(rs, vs, ss_, 0);
+  b.s[0] = sv[0];
+  b.s[1] = sv[1];
+}
+
+// Tiles nt0 .. nt0 + kDnTiles - 1 (those below ntiles) of one expert block.
+// Superchunk index G runs over the tiles, nscp (the per-tile superchunk
+// count rounded up to the ring) per tile; superchunks past K read zeros.
 template <int MT, int DB, int DA>
-__device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, rsrc_t rh,
+__device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, int I, int P, rsrc_t rh,
                                            const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                            const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
                                            float* __restrict__ ybuf) {
@@ -436,25 +459,37 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
   const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
   const rsrc_t rc = mk_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
   const rsrc_t rs = mk_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
+  const rsrc_t ry = mk_rsrc(ybuf, (uint32_t)((size_t)P * H * 4));
   const int nbk = I / 32;
-  int row[2];
-  uint32_t boff[2];
+  const int nchunks = I / kKC, nsc = nchunks / 2;
+  const int nscp = (nsc + DB - 1) / DB * DB;
+  const int ntw = min(kDnTiles, ntiles - nt0);
+  const int gend = ntw * nscp;
+  const uint32_t lo_off = (uint32_t)((size_t)P * I * 2);  // byte offset of the lo term
+  // this lane's two rows of tile t: t * 256 + rbase + 16 j
+  const int rbase = nt0 * kDN_NT + wid * 32 + nl;
+  // weights of global superchunk G (tile G / nscp, superchunk G % nscp);
+  // every row of a real tile is below H (H is a multiple of 256)
+  uint32_t vcode[2], vscale[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    row[j] = nt * kDN_NT + wid * 32 + 16 * j + nl;
-    const bool ok = row[j] < H;
-    boff[j] = ok ? (uint32_t)row[j] * (uint32_t)(nbk * 16) + 16u * g : kOOB;
+    vcode[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)(nbk * 16) + 16u * g;
+    vscale[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)nbk;
   }
-  const int nchunks = I / kKC, nsc = nchunks / 2;
-  const uint32_t lo_off = (uint32_t)((size_t)P * I * 2);  // byte offset of the lo term
-  // LDS: buffer b, term t at lds + (2b + t) * kTile; then the row tile's scale table
-  uint8_t* tab = reinterpret_cast<uint8_t*>(lds + 4 * kTile);
-  const int pitch = scale_row_pitch(nbk);
-  const uint8_t* trow[2] = {tab + (wid * 32 + nl) * pitch, tab + (wid * 32 + 16 + nl) * pitch};
-  const uint32_t ttotal = (uint32_t)kDN_NT * (uint32_t)nbk;
-  SPieces<kDnScaleU> sp;
-  scales_fetch<kDnScaleU>(sp, rs, (uint32_t)nt * ttotal, ttotal);
-  // activation ring (both terms), as in the gate/up kernel
+  auto load_b = [&](BSuper (&b)[2], int G) {
+    const int t = G / nscp, sc = G - t * nscp;
+    const bool ok = G < gend && sc < nsc;
+    const uint32_t scode = (uint32_t)t * (uint32_t)(kDN_NT * nbk * 16) + (uint32_t)sc * 128u;
+    const uint32_t sscale = (uint32_t)t * (uint32_t)(kDN_NT * nbk) + (uint32_t)sc * 8u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_bsuper_direct(b[j], rc, rs, vcode[j], vscale[j], scode, sscale, ok);
+  };
+  // activations of global chunk q (chunk q % (2 nscp) of its tile; past K or past the last tile: zeros)
+  auto a_kbyte = [&](int q) -> uint32_t {
+    const int cin = q % (2 * nscp);
+    return (q < 2 * gend && cin < nchunks) ? (uint32_t)cin * (kKC * 2) : kFar;
+  };
+
   uint32_t aoff[NV];
   a_offsets<NV>(aoff, row_base);
   ARegs<NV> ah[DA], al[DA];
@@ -462,48 +497,33 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
   a_fetch<NV>(al[0], rh, aoff, lo_off);
   BSuper rb[DB][2];
 #pragma unroll
-  for (int d = 0; d < DB - 1; ++d)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_bcodes(rb[d][j], rc, boff[j], d, nsc);
+  for (int d = 0; d < DB - 1; ++d) load_b(rb[d], d);
 #pragma unroll
   for (int j = 1; j < DA; ++j) {
-    const uint32_t kb = j < nchunks ? (uint32_t)j * (kKC * 2) : kFar;
+    const uint32_t kb = a_kbyte(j);
     a_fetch<NV>(ah[j], rh, aoff, kb);
     a_fetch<NV>(al[j], rh, aoff, lo_off + kb);
   }
-  scales_put<kDnScaleU>(sp, tab, nbk, ttotal);
   a_put<NV>(ah[0], lds);
   a_put<NV>(al[0], lds + kTile);
   __syncthreads();
-#pragma unroll
-  for (int d = 0; d < DB - 1; ++d)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_bscales(rb[d][j], trow[j], d, nsc);
 
   f32x4 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int sc0 = 0; sc0 < nsc; sc0 += DB) {
+  for (int G0 = 0; G0 < gend; G0 += DB) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int cc = 2 * d + h, c = 2 * sc0 + cc;
+        const int cc = 2 * d + h, q = 2 * G0 + cc;  // global chunk; q % DA == cc % DA
         {
-          const int cn = c + DA;
-          const uint32_t kb = cn < nchunks ? (uint32_t)cn * (kKC * 2) : kFar;
+          const uint32_t kb = a_kbyte(q + DA);
           a_fetch<NV>(ah[cc % DA], rh, aoff, kb);
           a_fetch<NV>(al[cc % DA], rh, aoff, lo_off + kb);
         }
-        if (h == 0) {
-          const int sn = sc0 + d + DB - 1;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            load_bcodes(rb[(d + DB - 1) % DB][j], rc, boff[j], sn, nsc);
-            load_bscales(rb[(d + DB - 1) % DB][j], trow[j], sn, nsc);
-          }
-        }
+        if (h == 0) load_b(rb[(d + DB - 1) % DB], G0 + d + DB - 1);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint16_t* Ah = lds + h * 2 * kTile;
         const uint16_t* Al = Ah + kTile;
@@ -528,16 +548,21 @@ __device__ __forceinline__ void down_block(int e, int nt, int H, int I, int P, r
         __syncthreads();
       }
     }
-  }
+    if ((G0 + DB) % nscp == 0) {  // a tile ends with this round: store its rows, start the next
+      const int t = G0 / nscp;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+      for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = pid[m * 16 + 4 * g + r];
-      if (p >= 0) {
+        for (int r = 0; r < 4; ++r) {
+          const int p = pid[m * 16 + 4 * g + r];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (row[j] < H) ybuf[(size_t)p * H + row[j]] = acc[m][j][r];
+          for (int j = 0; j < 2; ++j) {
+            const int row = rbase + t * kDN_NT + 16 * j;
+            const uint32_t off = (p >= 0 && row < H) ? ((uint32_t)p * (uint32_t)H + (uint32_t)row) * 4u : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][j][r]), ry, off, 0, 0);
+          }
+        }
+        acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
@@ -551,8 +576,9 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   extern __shared__ uint16_t a_lds[];  // [2 buffers][2 terms][kMB][kLdsRow]
   __shared__ int32_t pid[kMB];
   __shared__ uint32_t row_base[kMB];
-  int eb, nt;
-  decode_item(ntiles, &eb, &nt);
+  const int ngroups = (ntiles + kDnTiles - 1) / kDnTiles;
+  int eb, ng;
+  decode_item(ngroups, &eb, &ng);
   if (eb >= min(*nblocks, max_blocks)) return;
   const int4 blk = blocks[eb];
   const int e = blk.x, cnt = blk.z;
@@ -565,15 +591,16 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   }
   __syncthreads();
   const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
+  const int nt0 = ng * kDnTiles;
   switch ((cnt + 15) / 16) {
-    case 1: down_block<1, dn_db(1), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 2: down_block<2, dn_db(2), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 3: down_block<3, dn_db(3), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 4: down_block<4, dn_db(4), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 5: down_block<5, dn_db(5), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 6: down_block<6, dn_db(6), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 7: down_block<7, dn_db(7), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    default: down_block<8, dn_db(8), 2>(e, nt, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 1: down_block<1, dn_db(1), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 2: down_block<2, dn_db(2), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 3: down_block<3, dn_db(3), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 4: down_block<4, dn_db(4), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 5: down_block<5, dn_db(5), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 6: down_block<6, dn_db(6), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 7: down_block<7, dn_db(7), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    default: down_block<8, dn_db(8), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
   }
 }
 
@@ -766,12 +793,12 @@ static unsigned items_grid(int max_blocks, int ntiles) {
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kStaticLds = 2 * kMB * 4;
 static size_t gateup_lds(int H) { return (size_t)2 * kTile * 2 + (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
-static size_t down_lds(int I) { return (size_t)4 * kTile * 2 + (size_t)kDN_NT * scale_row_pitch(I / 32); }
+static size_t down_lds() { return (size_t)4 * kTile * 2; }
 
 bool grouped_shape_ok(int64_t H, int64_t I) {
   if (H <= 0 || I <= 0 || H % 256 != 0 || I % 256 != 0) return false;
-  if (H / 32 > 64 * kGuScaleU || I / 32 > 32 * kDnScaleU) return false;
-  return gateup_lds((int)H) + kStaticLds <= kLdsBytes && down_lds((int)I) + kStaticLds <= kLdsBytes;
+  if (H / 32 > 64 * kGuScaleU) return false;
+  return gateup_lds((int)H) + kStaticLds <= kLdsBytes && down_lds() + kStaticLds <= kLdsBytes;
 }
 
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
@@ -788,9 +815,10 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s) {
   const int ntiles = (H + kDN_NT - 1) / kDN_NT;
-  const size_t lds = down_lds(I);
-  k_down_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
-                                                                       scales, H, I, E, P, max_blocks, ntiles, ybuf);
+  const int ngroups = (ntiles + kDnTiles - 1) / kDnTiles;
+  const size_t lds = down_lds();
+  k_down_mfma<<<dim3(items_grid(max_blocks, ngroups)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
+                                                                        scales, H, I, E, P, max_blocks, ntiles, ybuf);
   return hipGetLastError();
 }
 

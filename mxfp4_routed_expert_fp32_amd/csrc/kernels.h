@@ -31,9 +31,9 @@ hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H
 
 // Prefill form (bf16 activations): expert blocks of at most 128 sorted pairs,
 // gate/up + SwiGLU and down grouped GEMMs on MFMA.  hterm holds h as two bf16
-// terms, [2][P][I].  grouped_shape_ok: H and I multiples of 256 whose
-// per-workgroup scale tables fit LDS beside the activation tiles
-// (H <= 11264, I <= 2560; layers have H <= 8192).
+// terms, [2][P][I].  grouped_shape_ok: H and I multiples of 256, with the
+// gate/up workgroup's scale table fitting LDS beside the activation tiles
+// (H <= 11264; layers have H <= 8192).
 bool grouped_shape_ok(int64_t H, int64_t I);
 int max_expert_blocks(int P, int E);
 hipError_t launch_expert_blocks(const int32_t* offsets, int E, int max_blocks, int4* blocks, int32_t* nblocks,

@@ -147,8 +147,8 @@ def test_grouped_stage_entry_points_reject_before_launch():
     assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 4096, 17, *args[3:]) == -2
     odd = D(hidden=7168 + 32)
     assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(odd), *args) == -7
-    # the down kernel's scale table must fit LDS: I <= 2560
-    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(D(inter=2560 + 256)), *args) == -7
+    # y of 4096 x 16 pairs x 8192 fp32 reaches 2 GiB
+    assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(D(hidden=8192)), *args) == -7
     # x of 40000 x 7168 bf16 tokens reaches 1 GiB
     assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 40000, 16, *args[3:]) == -7
     assert L.moe_mxfp4_grouped_gate_up(ctypes.byref(d), 16, 4096, 16, 16, 8, 16, 1408, 16, 16, 16, None) == -4

@@ -306,15 +306,14 @@ def test_rmsnorm_and_residual():
 @pytest.mark.parametrize("H,I,E,k,T,hot", [(256, 256, 8, 2, 37, False), (512, 256, 16, 4, 65, False),
                                            (256, 512, 4, 2, 300, True), (1024, 768, 12, 3, 130, True),
                                            (768, 1280, 6, 2, 45, False),
-                                           (8192, 256, 2, 1, 20, False), (256, 2560, 4, 2, 37, False),
-                                           (256, 2816, 4, 2, 9, False)])
+                                           (8192, 256, 2, 1, 20, False), (256, 2816, 4, 2, 37, False)])
 def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     """T > 1 with bf16 activations runs the sort + MFMA grouped GEMMs (H, I
     multiples of 256; an odd count of 256-wide K superchunks included); expert
     blocks are ragged, and `hot` makes one expert take more than 128 tokens.
-    H = 8192 is the largest hidden size a layer may have; I = 2560 is the
-    largest scale table the grouped down kernel keeps in LDS, and I = 2816 is
-    past that and takes the decode-form kernels."""
+    H = 8192 is the largest hidden size a layer may have (and the largest
+    gate/up scale table in LDS); H = 256 has a single row tile, fewer than a
+    down workgroup's run of tiles."""
     w = synth.Workload("g", 63, T, H, I, E, k, "bf16", weight_seed=7500 + H + E + T)
     c, s, ex = experts_host(w)
     desc, codes, scales = pack_whole(w, c, s)
@@ -334,6 +333,36 @@ def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     P.assert_weights_close(wt, r_w, k)
     err = P.assert_out_close(out, r_out)
     assert err < 1e-5, err
+
+
+def test_prefill_token_batches_equal_separate_calls():
+    """Past the grouped GEMMs' 32-bit offset limits the forward runs the
+    prefill form over batches of tokens.  At H = I = 256, k = 8 a batch holds
+    131071 tokens (k * I * 4 bytes of h terms per token below 1 GiB); 131071 +
+    900 tokens take two batches.  Tokens are independent and each token's
+    sums do not depend on which tokens share its expert blocks, so the output
+    equals two separate calls bit for bit; sampled tokens of both batches are
+    checked against the oracle."""
+    H, I, E, k = 256, 256, 8, 8
+    T1, T2 = 131071, 900
+    T = T1 + T2
+    w = synth.Workload("tb", 67, T, H, I, E, k, "bf16", weight_seed=7900)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    out, logits, idx, wt = run_forward(desc, w, x, wr, None, codes, scales, k)
+    o1, l1, i1, w1 = run_forward(desc, w, x[:T1].contiguous(), wr, None, codes, scales, k)
+    o2, l2, i2, w2 = run_forward(desc, w, x[T1:].contiguous(), wr, None, codes, scales, k)
+    assert np.array_equal(logits.view(np.uint32), np.concatenate([l1, l2]).view(np.uint32))
+    assert np.array_equal(idx, np.concatenate([i1, i2]))
+    assert np.array_equal(out.view(np.uint32), np.concatenate([o1, o2]).view(np.uint32))
+    rows = np.r_[0, 1, T1 - 1, T1, T1 + 1, T - 1, np.random.default_rng(3).integers(0, T, 12)]
+    xf = synth.tokens_f32(w, rows)
+    r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, None, logits[rows])
+    assert np.array_equal(idx[rows], r_idx)
+    P.assert_weights_close(wt[rows], r_w, k)
+    P.assert_out_close(out[rows], r_out)
 
 
 def test_grouped_stages_equal_forward_and_skip_malformed_blocks():
