@@ -231,30 +231,104 @@ struct Shape {
   static constexpr bool FD = MT <= 4;
 };
 
+// ---------------------------------------------------------------- activation tiles by DMA
+// An activation chunk (rows x 128 bf16, 256 bytes per row) goes from memory
+// straight into LDS: buffer_load ... lds writes lane i's 16 bytes at the
+// wave's LDS base + 16 i, so no registers or LDS store instructions are
+// involved.  LDS rows are 256 bytes with the 16-byte pieces swizzled by row
+// (piece p of row r sits in slot p ^ (r % 16)), so a fragment read of 16 rows
+// at one K offset touches 16 different slots and no bank twice.  Wave w moves
+// blocks b = w + 8 i (i < MS/2) of 4 rows; lane j loads row 4b + j/16, the
+// piece that belongs in slot j % 16.  Rows past the block read out of range
+// and land as zeros.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kDmaRow = kKC * 2;  // bytes per LDS activation row
+
+template <int MS>
+__device__ __forceinline__ void dma_offsets(uint32_t* doff, const uint32_t* row_base) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < MS / 2; ++i) {
+    const int row = 4 * (wid + 8 * i) + lane / 16;
+    doff[i] = row_base[row] + (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
+  }
+}
+
+// Requests chunk bytes [kbyte, kbyte + 256) of every staged row into `buf`.
+template <int MS>
+__device__ __forceinline__ void dma_chunk(rsrc_t r, const uint32_t* doff, uint32_t kbyte, uint8_t* buf) {
+  const int wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < MS / 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + (wid + 8 * i) * (4 * kDmaRow)), 16,
+                                             doff[i] + kbyte, 0, 0, 0);
+}
+
+// Fragment of row m*16 + nl (this lane's), K piece p (0..15) of a swizzled tile.
+__device__ __forceinline__ bf16x8 lds_frag_sw(const uint8_t* buf, int m, int nl, int p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(buf + (m * 16 + nl) * kDmaRow + ((p ^ nl) << 4)));
+}
+
+// Waits until at most n vector memory operations of this wave are in flight,
+// and for its LDS operations, then joins the workgroup barrier.  The barrier
+// carries no memory fence (a fence would wait for every load in flight); the
+// empty asm keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // Row tile = 128 rows of gate and the same 128 rows of up; wave w: n-tile 0
 // = gate rows 16w + 0..15, n-tile 1 = the same up rows.  Output: h as two
 // bf16 terms, hterm[0][p][i] = hi and hterm[1][p][i] = lo.
 constexpr int kGU_NT = 128;
-// Weight ring: 4 superchunks (K = 7168 gives 28, whole rounds).  Activation
-// ring: 4 chunks up to 64 rows of a block (the weight loads then get their
-// full ring distance, since a wait for an activation load also waits for
-// every older weight load), 2 above, where the accumulators need the
-// registers (measured: a longer activation ring does not help there).
+// Weight ring: 4 superchunks (K = 7168 gives 28, whole rounds).
 constexpr int kGuDB = 4;
-constexpr int gu_da(int mt) { return mt <= 4 ? 4 : 2; }
 // Scale-table pieces per thread and matrix: 128 rows x nb bytes in 16-byte
 // pieces over 512 threads covers nb <= 64 * kGuScaleU, i.e. K <= 12288.
 constexpr int kGuScaleU = 6;
 
-template <int MT, int DB, int DA>
+// Activation buffers (DMA ring of NB buffers of MS*16 rows, chunks requested
+// NB - 1 ahead; a wait for a chunk's DMA also waits for every older weight
+// load, so the ring should reach about as far ahead as the weight ring
+// allows): 5 up to 2 m-tiles, 4 up to 4, 3 up to 6; 3 above when they fit
+// LDS beside the scale table (K up to 7424), else 2.  The scale table follows
+// the buffers.
+constexpr int gu_nbuf_small(int mt) { return mt <= 2 ? 5 : (mt <= 4 ? 4 : (mt <= 6 ? 3 : 2)); }
+constexpr int kGuActSmall = 3 * 96 * kDmaRow;  // holds every small-LDS ring (5x32, 4x64, 3x96, 2x128 rows)
+constexpr int kGuActLarge = 3 * 128 * kDmaRow;
+
+// Vector memory operations a wave issues after the DMA of chunk c + 1 (issued
+// in chunk c + 2 - NB, first thing) until the end of chunk c: the DMAs of the
+// NB - 2 chunks after it (MS/2 each) and the weight codes (4 loads) of every
+// even chunk among the NB - 1 chunks from c + 2 - NB to c.
+constexpr int gu_wait_ops(int nb, int ms, int h) {
+  const int da = nb - 1;
+  const int p0 = ((h + 1 - da) % 2 + 2) % 2;  // parity of chunk c + 1 - da
+  const int evens = p0 == 0 ? (da + 1) / 2 : da / 2;
+  return (da - 1) * (ms / 2) + 4 * evens;
+}
+static_assert(gu_wait_ops(3, 8, 0) == 8 && gu_wait_ops(3, 8, 1) == 8, "two ahead");
+static_assert(gu_wait_ops(2, 8, 0) == 4 && gu_wait_ops(2, 8, 1) == 0, "one ahead");
+
+template <int MT, int DB, int NB>
 __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
                                              const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                             const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
-                                             uint16_t* __restrict__ hterm) {
+                                             const int32_t* pid, const uint32_t* row_base, uint8_t* lds,
+                                             int act_bytes, uint16_t* __restrict__ hterm) {
   using S = Shape<MT>;
-  constexpr int NV = S::NV;
-  static_assert((2 * DB) % DA == 0, "activation ring must divide the unrolled chunks");
+  constexpr int MS = S::MS;
+  constexpr int DA = NB - 1;
+  static_assert(NB >= 2 && NB <= 5, "activation buffers");
+  constexpr uint32_t kBuf = (uint32_t)MS * 16 * kDmaRow;
+  static_assert(NB * MS * 16 * kDmaRow <= kGuActLarge, "ring fits the activation region");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
@@ -266,10 +340,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   const bool rok = row < I;
   const uint32_t boff = rok ? (uint32_t)row * (uint32_t)(nb * 16) + 16u * g : kOOB;
   const int nchunks = H / kKC, nsc = nchunks / 2;
-  uint16_t* buf0 = lds;
-  uint16_t* buf1 = lds + kTile;
   // scale table: gate rows, then up rows, of this row tile
-  uint8_t* tab = reinterpret_cast<uint8_t*>(lds + 2 * kTile);
+  uint8_t* tab = lds + act_bytes;
   const int pitch = scale_row_pitch(nb);
   const uint8_t* tg = tab + (wid * 16 + nl) * pitch;
   const uint8_t* tu = tg + kGU_NT * pitch;
@@ -278,24 +350,27 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   scales_fetch<kGuScaleU>(spg, rsg, tfirst, ttotal);
   scales_fetch<kGuScaleU>(spu, rsu, tfirst, ttotal);
 
-  // activation ring: slot j holds chunk c (c % DA == j) from its request
-  // until it is written to LDS at the end of chunk c - 1
-  uint32_t aoff[NV];
-  a_offsets<NV>(aoff, row_base);
-  ARegs<NV> ar[DA];
-  a_fetch<NV>(ar[0], rx, aoff, 0);
+  uint32_t doff[MS / 2];
+  dma_offsets<MS>(doff, row_base);
+  auto kb_of = [&](int c) -> uint32_t { return c < nchunks ? (uint32_t)c * kDmaRow : kFar; };
+  // The prologue issues what the loop would have issued in the chunks before
+  // chunk 0, in the loop's order (chunk v: DMA of chunk v + DA, then in even
+  // chunks the weight codes of superchunk v/2 + DB - 1), so the loop's wait
+  // counts hold from its first chunk on.
   BSuper rg[DB], ru[DB];
+  constexpr int V = 2 * (DB - 1) > DA ? 2 * (DB - 1) : DA;
 #pragma unroll
-  for (int d = 0; d < DB - 1; ++d) {
-    load_bcodes(rg[d], rcg, boff, d, nsc);
-    load_bcodes(ru[d], rcu, boff, d, nsc);
+  for (int v = -V; v < 0; ++v) {
+    if (v + DA >= 0) dma_chunk<MS>(rx, doff, kb_of(v + DA), lds + (v + DA) * kBuf);
+    if (v % 2 == 0 && v / 2 + DB - 1 >= 0) {
+      const int sn = v / 2 + DB - 1;
+      load_bcodes(rg[sn], rcg, boff, sn, nsc);
+      load_bcodes(ru[sn], rcu, boff, sn, nsc);
+    }
   }
-#pragma unroll
-  for (int j = 1; j < DA; ++j) a_fetch<NV>(ar[j], rx, aoff, j < nchunks ? (uint32_t)j * (kKC * 2) : kFar);
   scales_put<kGuScaleU>(spg, tab, nb, ttotal);
   scales_put<kGuScaleU>(spu, tab + kGU_NT * pitch, nb, ttotal);
-  a_put<NV>(ar[0], buf0);
-  __syncthreads();
+  wait_vm_barrier<gu_wait_ops(NB, MS, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d) {
     load_bscales(rg[d], tg, d, nsc);
@@ -306,17 +381,20 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the ring holds whole superchunks; a phantom superchunk past K (odd nsc
-  // with DB = 2) reads zeros on both operands and adds nothing
+  // the ring holds whole superchunks; a phantom superchunk past K reads zeros
+  // on both operands and adds nothing
+  int slot = 0;  // LDS buffer of the current chunk, c % NB
   for (int sc0 = 0; sc0 < nsc; sc0 += DB) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int cc = 2 * d + h, c = 2 * sc0 + cc;  // chunk; c % 2 == h, c % DA == cc % DA
+        const int c = 2 * sc0 + 2 * d + h;  // chunk; c % 2 == h
         {
-          const int cn = c + DA;  // refills the slot chunk c left (written to LDS before the last barrier)
-          a_fetch<NV>(ar[cc % DA], rx, aoff, cn < nchunks ? (uint32_t)cn * (kKC * 2) : kFar);
+          // chunk c + DA into the buffer chunk c - 1 used (every wave passed the last barrier after reading it)
+          int nslot = slot + DA;
+          nslot -= nslot >= NB ? NB : 0;
+          dma_chunk<MS>(rx, doff, kb_of(c + DA), lds + nslot * kBuf);
         }
         if (h == 0) {
           const int sn = sc0 + d + DB - 1;
@@ -326,24 +404,24 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           load_bscales(ru[(d + DB - 1) % DB], tu, sn, nsc);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
-        const uint16_t* A = h == 0 ? buf0 : buf1;
+        const uint8_t* A = lds + slot * kBuf;
         const float sgv = e8m0_operand((rg[d].s[h] >> (8 * g)) & 0xFFu);
         const float suv = e8m0_operand((ru[d].s[h] >> (8 * g)) & 0xFFu);
         bf16x8 fa[2][MT];
         if (S::FD) {
 #pragma unroll
-          for (int m = 0; m < MT; ++m) fa[0][m] = lds_frag(A, m * 16 + nl, 32 * g);
+          for (int m = 0; m < MT; ++m) fa[0][m] = lds_frag_sw(A, m, nl, 4 * g);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if (S::FD) {
             if (s < 3) {
 #pragma unroll
-              for (int m = 0; m < MT; ++m) fa[(s + 1) & 1][m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * (s + 1));
+              for (int m = 0; m < MT; ++m) fa[(s + 1) & 1][m] = lds_frag_sw(A, m, nl, 4 * g + s + 1);
             }
           } else {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) fa[s & 1][m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * s);
+            for (int m = 0; m < MT; ++m) fa[s & 1][m] = lds_frag_sw(A, m, nl, 4 * g + s);
           }
           const bf16x8 bg = decode8(rg[d].q[h][s], sgv), bu = decode8(ru[d].q[h][s], suv);
 #pragma unroll
@@ -352,12 +430,14 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
             acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bu, acc[m][1], 0, 0, 0);
           }
         }
-        // activations of chunk c+1 (requested DA - 1 chunks ago) into the other buffer
-        a_put<NV>(ar[(cc + 1) % DA], h == 0 ? buf1 : buf0);
-        __syncthreads();
+        // chunk c + 1 must be in LDS for every wave before anyone reads it
+        if (h == 0) wait_vm_barrier<gu_wait_ops(NB, MS, 0)>();
+        else wait_vm_barrier<gu_wait_ops(NB, MS, 1)>();
+        slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no LDS transfer outlives the loop
   // lane holds row `row` for slots m*16 + 4g + r
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -379,8 +459,10 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int T, int H, int I, int E, int k, int P, int max_blocks, int ntiles,
-    uint16_t* __restrict__ hterm) {
-  extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
+    int large, uint16_t* __restrict__ hterm) {
+  extern __shared__ uint4 lds_dyn[];  // activation buffers, then the scale table
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds_dyn);
+  const int act = large ? kGuActLarge : kGuActSmall;
   __shared__ int32_t pid[kMB];
   __shared__ uint32_t row_base[kMB];
   int eb, nt;
@@ -398,14 +480,16 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
   __syncthreads();
   const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
   switch ((cnt + 15) / 16) {
-    case 1: gateup_block<1, kGuDB, gu_da(1)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 2: gateup_block<2, kGuDB, gu_da(2)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 3: gateup_block<3, kGuDB, gu_da(3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 4: gateup_block<4, kGuDB, gu_da(4)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 5: gateup_block<5, kGuDB, gu_da(5)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 6: gateup_block<6, kGuDB, gu_da(6)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    case 7: gateup_block<7, kGuDB, gu_da(7)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
-    default: gateup_block<8, kGuDB, gu_da(8)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, a_lds, hterm); break;
+    case 1: gateup_block<1, kGuDB, gu_nbuf_small(1)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 2: gateup_block<2, kGuDB, gu_nbuf_small(2)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 3: gateup_block<3, kGuDB, gu_nbuf_small(3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 4: gateup_block<4, kGuDB, gu_nbuf_small(4)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 5: gateup_block<5, kGuDB, gu_nbuf_small(5)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 6: gateup_block<6, kGuDB, gu_nbuf_small(6)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 7: (large ? gateup_block<7, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<7, kGuDB, 2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    default: (large ? gateup_block<8, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<8, kGuDB, 2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
   }
 }
 
@@ -792,7 +876,9 @@ static unsigned items_grid(int max_blocks, int ntiles) {
 // LDS per workgroup on gfx950, and the kernels' static LDS (pid, row_base).
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kStaticLds = 2 * kMB * 4;
-static size_t gateup_lds(int H) { return (size_t)2 * kTile * 2 + (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
+static size_t gu_table_bytes(int H) { return (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
+static bool gu_large(int H) { return kGuActLarge + gu_table_bytes(H) + kStaticLds <= kLdsBytes; }
+static size_t gateup_lds(int H) { return (size_t)(gu_large(H) ? kGuActLarge : kGuActSmall) + gu_table_bytes(H); }
 static size_t down_lds() { return (size_t)4 * kTile * 2; }
 
 bool grouped_shape_ok(int64_t H, int64_t I) {
@@ -807,7 +893,7 @@ hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, co
   const int ntiles = (I + kGU_NT - 1) / kGU_NT;
   const size_t lds = gateup_lds(H);
   k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(
-      x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, hterm);
+      x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, gu_large(H) ? 1 : 0, hterm);
   return hipGetLastError();
 }
 
