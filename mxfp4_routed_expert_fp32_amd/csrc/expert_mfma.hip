@@ -298,25 +298,56 @@ constexpr int kGuScaleU = 6;
 // Activation buffers (DMA ring of NB buffers of MS*16 rows, chunks requested
 // NB - 1 ahead; a wait for a chunk's DMA also waits for every older weight
 // load, so the ring should reach about as far ahead as the weight ring
-// allows): 5 up to 2 m-tiles, 4 up to 4, 3 up to 6; 3 above when they fit
-// LDS beside the scale table (K up to 7424), else 2.  The scale table follows
-// the buffers.
+// allows): 5 up to 2 m-tiles, 4 up to 4; above, 4 (up to 6 m-tiles) or 3
+// when they fit LDS beside the scale table (K up to 7424), else 3 or 2.  The
+// scale table follows the buffers.
 constexpr int gu_nbuf_small(int mt) { return mt <= 2 ? 5 : (mt <= 4 ? 4 : (mt <= 6 ? 3 : 2)); }
 constexpr int kGuActSmall = 3 * 96 * kDmaRow;  // holds every small-LDS ring (5x32, 4x64, 3x96, 2x128 rows)
 constexpr int kGuActLarge = 3 * 128 * kDmaRow;
 
 // Vector memory operations a wave issues after the DMA of chunk c + 1 (issued
 // in chunk c + 2 - NB, first thing) until the end of chunk c: the DMAs of the
-// NB - 2 chunks after it (MS/2 each) and the weight codes (4 loads) of every
+// NB - 2 chunks after it (dmaops each) and the weight loads (codeops) of every
 // even chunk among the NB - 1 chunks from c + 2 - NB to c.
-constexpr int gu_wait_ops(int nb, int ms, int h) {
+constexpr int dma_wait_ops(int nb, int dmaops, int codeops, int h) {
   const int da = nb - 1;
   const int p0 = ((h + 1 - da) % 2 + 2) % 2;  // parity of chunk c + 1 - da
   const int evens = p0 == 0 ? (da + 1) / 2 : da / 2;
-  return (da - 1) * (ms / 2) + 4 * evens;
+  return (da - 1) * dmaops + codeops * evens;
 }
-static_assert(gu_wait_ops(3, 8, 0) == 8 && gu_wait_ops(3, 8, 1) == 8, "two ahead");
-static_assert(gu_wait_ops(2, 8, 0) == 4 && gu_wait_ops(2, 8, 1) == 0, "one ahead");
+
+// Replays the issue order of the prologue and the loop (nchunks chunks, weight
+// ring db) and checks that every wait count equals the operations issued after
+// the DMA it waits for: fewer would wait longer than needed, more would let a
+// chunk be read before it is in LDS.  (Stores issued between, at the down
+// kernel's tile ends, only lengthen a wait.)
+constexpr bool dma_waits_exact(int nb, int dmaops, int codeops, int db, int nchunks) {
+  const int da = nb - 1;
+  int last[160] = {};  // op count when the DMA of a chunk was issued
+  int n = 0;
+  const int v0 = 2 * (db - 1) > da ? 2 * (db - 1) : da;
+  for (int v = -v0; v < 0; ++v) {
+    if (v + da >= 0) { n += dmaops; last[v + da] = n; }
+    if (v % 2 == 0 && v / 2 + db - 1 >= 0) n += codeops;
+  }
+  if (n - last[0] != dma_wait_ops(nb, dmaops, codeops, 1)) return false;
+  for (int sc0 = 0; sc0 < nchunks / 2; sc0 += db)
+    for (int d = 0; d < db; ++d)
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * sc0 + 2 * d + h;
+        n += dmaops;
+        last[c + da] = n;
+        if (h == 0) n += codeops;
+        if (n - last[c + 1] != dma_wait_ops(nb, dmaops, codeops, h)) return false;
+      }
+  return true;
+}
+// gate/up: MS/2 DMA instructions and 4 code loads per chunk; the ring sizes used
+static_assert(dma_waits_exact(5, 1, 4, 4, 56) && dma_waits_exact(4, 2, 4, 4, 56) && dma_waits_exact(3, 3, 4, 4, 56) &&
+                  dma_waits_exact(3, 4, 4, 4, 56) && dma_waits_exact(2, 4, 4, 4, 56) && dma_waits_exact(5, 1, 4, 4, 2) &&
+                  dma_waits_exact(2, 4, 4, 4, 2) && dma_waits_exact(3, 3, 4, 4, 64) && dma_waits_exact(4, 2, 4, 4, 18) &&
+                  dma_waits_exact(4, 3, 4, 4, 56) && dma_waits_exact(3, 4, 4, 4, 2),
+              "gate/up DMA wait counts");
 
 template <int MT, int DB, int NB>
 __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
@@ -370,7 +401,7 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   }
   scales_put<kGuScaleU>(spg, tab, nb, ttotal);
   scales_put<kGuScaleU>(spu, tab + kGU_NT * pitch, nb, ttotal);
-  wait_vm_barrier<gu_wait_ops(NB, MS, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
+  wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d) {
     load_bscales(rg[d], tg, d, nsc);
@@ -431,8 +462,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           }
         }
         // chunk c + 1 must be in LDS for every wave before anyone reads it
-        if (h == 0) wait_vm_barrier<gu_wait_ops(NB, MS, 0)>();
-        else wait_vm_barrier<gu_wait_ops(NB, MS, 1)>();
+        if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 0)>();
+        else wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 1)>();
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
@@ -484,8 +515,10 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
     case 2: gateup_block<2, kGuDB, gu_nbuf_small(2)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
     case 3: gateup_block<3, kGuDB, gu_nbuf_small(3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
     case 4: gateup_block<4, kGuDB, gu_nbuf_small(4)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 5: gateup_block<5, kGuDB, gu_nbuf_small(5)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 6: gateup_block<6, kGuDB, gu_nbuf_small(6)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 5: (large ? gateup_block<5, kGuDB, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<5, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 6: (large ? gateup_block<6, kGuDB, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<6, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
     case 7: (large ? gateup_block<7, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
                    : gateup_block<7, kGuDB, 2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
     default: (large ? gateup_block<8, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
@@ -506,9 +539,8 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
 // (48), so 16 rows share a handful of lines that stay in L2.
 constexpr int kDN_NT = 256;
 constexpr int kDnTiles = 4;
-// Weight ring: 3 superchunks up to 64 rows of a block, 2 above (register
-// budget).  Activation ring: 2 chunks.
-constexpr int dn_db(int mt) { return mt <= 4 ? 3 : 2; }
+// Weight ring: 3 superchunks (K = 1536 gives 6 per tile).
+constexpr int dn_db(int) { return 3; }
 
 // Codes and scales of one superchunk from memory.  The lane's part of the
 // offsets (its row in the first tile, its code block) is a vector offset; the
@@ -526,17 +558,30 @@ __device__ __forceinline__ void load_bsuper_direct(BSuper& b, rsrc_t rc, rsrc_t 
   b.s[1] = sv[1];
 }
 
+// Activation ring (DMA, both terms of a chunk per buffer): 5 buffers up to 2
+// m-tiles, 4 up to 4, 3 up to 6, 2 above.
+constexpr int dn_nbuf(int mt) { return mt <= 2 ? 5 : (mt <= 4 ? 4 : (mt <= 6 ? 3 : 2)); }
+constexpr int kDnActBytes = 3 * 2 * 96 * kDmaRow;  // holds every ring: 5x2x32, 4x2x64, 3x2x96, 2x2x128 rows
+// per chunk: MS DMA instructions (two terms), and 6 weight loads (two n-tiles:
+// two code blocks and the scales each) in even chunks
+static_assert(dma_waits_exact(5, 2, 6, 3, 48) && dma_waits_exact(4, 4, 6, 3, 48) && dma_waits_exact(3, 6, 6, 2, 48) &&
+                  dma_waits_exact(2, 8, 6, 2, 48) && dma_waits_exact(5, 2, 6, 3, 24) && dma_waits_exact(2, 8, 6, 3, 12) &&
+                  dma_waits_exact(4, 4, 6, 3, 6),
+              "down DMA wait counts");
+
 // Tiles nt0 .. nt0 + kDnTiles - 1 (those below ntiles) of one expert block.
 // Superchunk index G runs over the tiles, nscp (the per-tile superchunk
 // count rounded up to the ring) per tile; superchunks past K read zeros.
-template <int MT, int DB, int DA>
+template <int MT, int DB, int NB>
 __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, int I, int P, rsrc_t rh,
                                            const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                           const int32_t* pid, const uint32_t* row_base, uint16_t* lds,
+                                           const int32_t* pid, const uint32_t* row_base, uint8_t* lds,
                                            float* __restrict__ ybuf) {
   using S = Shape<MT>;
-  constexpr int NV = S::NV;
-  static_assert((2 * DB) % DA == 0, "activation ring must divide the unrolled chunks");
+  constexpr int MS = S::MS;
+  constexpr int DA = NB - 1;
+  constexpr uint32_t kTerm = (uint32_t)MS * 16 * kDmaRow, kBuf = 2 * kTerm;
+  static_assert(NB * kBuf <= kDnActBytes, "ring fits the activation region");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
@@ -568,49 +613,47 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
 #pragma unroll
     for (int j = 0; j < 2; ++j) load_bsuper_direct(b[j], rc, rs, vcode[j], vscale[j], scode, sscale, ok);
   };
-  // activations of global chunk q (chunk q % (2 nscp) of its tile; past K or past the last tile: zeros)
-  auto a_kbyte = [&](int q) -> uint32_t {
+  // activations of global chunk q (chunk q % (2 nscp) of its tile; past K or
+  // past the last tile: zeros), both terms, into buffer `buf`
+  uint32_t doff[MS / 2];
+  dma_offsets<MS>(doff, row_base);
+  auto dma_q = [&](int q, uint8_t* buf) {
     const int cin = q % (2 * nscp);
-    return (q < 2 * gend && cin < nchunks) ? (uint32_t)cin * (kKC * 2) : kFar;
+    const uint32_t kb = (q < 2 * gend && cin < nchunks) ? (uint32_t)cin * kDmaRow : kFar;
+    dma_chunk<MS>(rh, doff, kb, buf);
+    dma_chunk<MS>(rh, doff, lo_off + kb, buf + kTerm);
   };
 
-  uint32_t aoff[NV];
-  a_offsets<NV>(aoff, row_base);
-  ARegs<NV> ah[DA], al[DA];
-  a_fetch<NV>(ah[0], rh, aoff, 0);
-  a_fetch<NV>(al[0], rh, aoff, lo_off);
+  // prologue: the loop's own issue order for the chunks before chunk 0
   BSuper rb[DB][2];
+  constexpr int V = 2 * (DB - 1) > DA ? 2 * (DB - 1) : DA;
 #pragma unroll
-  for (int d = 0; d < DB - 1; ++d) load_b(rb[d], d);
-#pragma unroll
-  for (int j = 1; j < DA; ++j) {
-    const uint32_t kb = a_kbyte(j);
-    a_fetch<NV>(ah[j], rh, aoff, kb);
-    a_fetch<NV>(al[j], rh, aoff, lo_off + kb);
+  for (int v = -V; v < 0; ++v) {
+    if (v + DA >= 0) dma_q(v + DA, lds + (v + DA) * kBuf);
+    if (v % 2 == 0 && v / 2 + DB - 1 >= 0) load_b(rb[v / 2 + DB - 1], v / 2 + DB - 1);
   }
-  a_put<NV>(ah[0], lds);
-  a_put<NV>(al[0], lds + kTile);
-  __syncthreads();
+  wait_vm_barrier<dma_wait_ops(NB, MS, 6, 1)>();
 
   f32x4 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  int slot = 0;  // LDS buffer of the current chunk
   for (int G0 = 0; G0 < gend; G0 += DB) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int cc = 2 * d + h, q = 2 * G0 + cc;  // global chunk; q % DA == cc % DA
+        const int q = 2 * G0 + 2 * d + h;  // global chunk
         {
-          const uint32_t kb = a_kbyte(q + DA);
-          a_fetch<NV>(ah[cc % DA], rh, aoff, kb);
-          a_fetch<NV>(al[cc % DA], rh, aoff, lo_off + kb);
+          int nslot = slot + DA;
+          nslot -= nslot >= NB ? NB : 0;
+          dma_q(q + DA, lds + nslot * kBuf);
         }
         if (h == 0) load_b(rb[(d + DB - 1) % DB], G0 + d + DB - 1);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
-        const uint16_t* Ah = lds + h * 2 * kTile;
-        const uint16_t* Al = Ah + kTile;
+        const uint8_t* Ah = lds + slot * kBuf;
+        const uint8_t* Al = Ah + kTerm;
         const float s0v = e8m0_operand((rb[d][0].s[h] >> (8 * g)) & 0xFFu);
         const float s1v = e8m0_operand((rb[d][1].s[h] >> (8 * g)) & 0xFFu);
 #pragma unroll
@@ -618,18 +661,17 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           const bf16x8 b0 = decode8(rb[d][0].q[h][s], s0v), b1 = decode8(rb[d][1].q[h][s], s1v);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const bf16x8 fh = lds_frag(Ah, m * 16 + nl, 32 * g + 8 * s);
-            const bf16x8 fl = lds_frag(Al, m * 16 + nl, 32 * g + 8 * s);
+            const bf16x8 fh = lds_frag_sw(Ah, m, nl, 4 * g + s);
+            const bf16x8 fl = lds_frag_sw(Al, m, nl, 4 * g + s);
             acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b0, acc[m][0], 0, 0, 0);
             acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b1, acc[m][1], 0, 0, 0);
             acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b0, acc[m][0], 0, 0, 0);
             acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b1, acc[m][1], 0, 0, 0);
           }
         }
-        uint16_t* nxt = lds + (h ^ 1) * 2 * kTile;
-        a_put<NV>(ah[(cc + 1) % DA], nxt);
-        a_put<NV>(al[(cc + 1) % DA], nxt + kTile);
-        __syncthreads();
+        if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS, 6, 0)>();
+        else wait_vm_barrier<dma_wait_ops(NB, MS, 6, 1)>();
+        slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
     if ((G0 + DB) % nscp == 0) {  // a tile ends with this round: store its rows, start the next
@@ -650,6 +692,7 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no LDS transfer outlives the loop
 }
 
 __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
@@ -657,7 +700,8 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int H, int I, int E, int P, int max_blocks, int ntiles,
     float* __restrict__ ybuf) {
-  extern __shared__ uint16_t a_lds[];  // [2 buffers][2 terms][kMB][kLdsRow]
+  extern __shared__ uint4 lds_dyn[];  // activation ring
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds_dyn);
   __shared__ int32_t pid[kMB];
   __shared__ uint32_t row_base[kMB];
   const int ngroups = (ntiles + kDnTiles - 1) / kDnTiles;
@@ -677,14 +721,14 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
   const int nt0 = ng * kDnTiles;
   switch ((cnt + 15) / 16) {
-    case 1: down_block<1, dn_db(1), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 2: down_block<2, dn_db(2), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 3: down_block<3, dn_db(3), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 4: down_block<4, dn_db(4), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 5: down_block<5, dn_db(5), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 6: down_block<6, dn_db(6), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    case 7: down_block<7, dn_db(7), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
-    default: down_block<8, dn_db(8), 2>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, a_lds, ybuf); break;
+    case 1: down_block<1, dn_db(1), dn_nbuf(1)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 2: down_block<2, dn_db(2), dn_nbuf(2)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 3: down_block<3, dn_db(3), dn_nbuf(3)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 4: down_block<4, dn_db(4), dn_nbuf(4)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 5: down_block<5, dn_db(5), dn_nbuf(5)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 6: down_block<6, dn_db(6), dn_nbuf(6)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 7: down_block<7, dn_db(7), dn_nbuf(7)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    default: down_block<8, dn_db(8), dn_nbuf(8)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
   }
 }
 
@@ -879,7 +923,7 @@ constexpr size_t kStaticLds = 2 * kMB * 4;
 static size_t gu_table_bytes(int H) { return (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
 static bool gu_large(int H) { return kGuActLarge + gu_table_bytes(H) + kStaticLds <= kLdsBytes; }
 static size_t gateup_lds(int H) { return (size_t)(gu_large(H) ? kGuActLarge : kGuActSmall) + gu_table_bytes(H); }
-static size_t down_lds() { return (size_t)4 * kTile * 2; }
+static size_t down_lds() { return (size_t)kDnActBytes; }
 
 bool grouped_shape_ok(int64_t H, int64_t I) {
   if (H <= 0 || I <= 0 || H % 256 != 0 || I % 256 != 0) return false;
