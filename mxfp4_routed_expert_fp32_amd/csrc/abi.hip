@@ -206,14 +206,23 @@ int check_forward_args(const moe_layer_desc* d, const void* x, int32_t x_dtype, 
 int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
                  const float* router_bias, const void* codes, const void* scales, int32_t T, int32_t k,
                  float* out, float* logits_out, int32_t* idx_out, float* w_out, void* workspace,
-                 const FwdLayout& L, const float* resid, hipStream_t s) {
+                 const FwdLayout& L, const float* resid, hipStream_t s, const float* norm_gamma = nullptr,
+                 float norm_eps = 0.0f, float* norm_out = nullptr) {
   char* ws = static_cast<char*>(workspace);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.logits);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   float* w = w_out ? w_out : reinterpret_cast<float*>(ws + L.w);
   const bool xf = x_dtype == MOE_DTYPE_F32;
-  float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
-  MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
+  if (norm_gamma) {
+    // x is an fp32 residual: the router kernel also applies the RMSNorm and
+    // writes the normalised rows to norm_out, which the expert kernels read
+    MOE_TRY(dev(moe::launch_norm_router_logits(static_cast<const float*>(x), norm_gamma, norm_eps, router_w,
+                                               router_bias, T, d->hidden, d->n_experts, logits, norm_out, s)));
+    x = norm_out;
+  } else {
+    float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
+    MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
+  }
   if (T > 1 && !xf && grouped_batch(d, k) > 0) {
     // prefill form: top-k, then sort + grouped GEMMs
     MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
@@ -548,10 +557,11 @@ static int stack_enqueue(const moe_layer_desc* d, int32_t n_layers, const void* 
   float* nbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + nb_off);
   MOE_TRY(dev(moe::launch_widen(x, x_dtype == MOE_DTYPE_F32, n, residual, s)));
   for (int l = 0; l < n_layers; ++l) {
-    MOE_TRY(dev(moe::launch_rmsnorm(residual, gamma[l], eps, T, d->hidden, nbuf, s)));
+    // RMSNorm runs inside the layer's router kernel (same bits as a separate pass), which leaves the
+    // normalised rows in nbuf for the expert kernels
     const float* b = router_bias ? router_bias[l] : nullptr;
-    MOE_TRY(forward_impl(d, nbuf, MOE_DTYPE_F32, router_w[l], b, codes[l], scales[l], T, k, residual,
-                         nullptr, nullptr, nullptr, ws, L, residual, s));
+    MOE_TRY(forward_impl(d, residual, MOE_DTYPE_F32, router_w[l], b, codes[l], scales[l], T, k, residual,
+                         nullptr, nullptr, nullptr, ws, L, residual, s, gamma[l], eps, nbuf));
   }
   return MOE_OK;
 }

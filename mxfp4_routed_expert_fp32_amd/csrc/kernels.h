@@ -10,6 +10,11 @@ namespace moe {
 
 hipError_t launch_router_logits(const void* x, bool x_f32, const float* wr, const float* bias, int T,
                                 int H, int E, float* logits, hipStream_t s);
+// RMSNorm folded into the fp32 router: logits of n = RMSNorm(r) * gamma, and
+// n itself written to nout (bit-identical to k_rmsnorm + k_router_logits).
+hipError_t launch_norm_router_logits(const float* r, const float* gamma, float eps, const float* wr,
+                                     const float* bias, int T, int H, int E, float* logits, float* nout,
+                                     hipStream_t s);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                hipStream_t s);
 hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets,

@@ -82,6 +82,126 @@ __global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- RMSNorm + router logits
+// k_router_logits on n = (r * inv) * gamma, inv = 1 / sqrt(mean(r^2) + eps),
+// for fp32 rows r: every workgroup reduces its tokens' r^2 itself, with the
+// element order and reduction tree of k_rmsnorm, so n, and the logits, are
+// the bits the two separate kernels give.  Workgroup e also writes its slice
+// of n, float4 columns [e S4, e S4 + S4) with S4 = ceil(H/4 / E), for the
+// expert kernels that follow; the slices cover every column.
+template <int TT, int NW>
+__global__ __launch_bounds__(256) void k_norm_router_logits(const float* __restrict__ r,
+                                                            const float* __restrict__ gamma, float eps,
+                                                            const float* __restrict__ wr,
+                                                            const float* __restrict__ bias, int T, int H,
+                                                            int E, float* __restrict__ logits,
+                                                            float* __restrict__ nout) {
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * TT;
+  const int n4 = H / 4;
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const float4* wrow = reinterpret_cast<const float4*>(wr + (size_t)e * H);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  float4 w[NW], gv[NW], v[TT][NW];
+#pragma unroll
+  for (int c = 0; c < NW; ++c) {
+    const int q = threadIdx.x + 256 * c;
+    if (q < n4) {
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wrow + q));
+      w[c] = make_float4(a.x, a.y, a.z, a.w);
+      gv[c] = g4[q];
+    } else {
+      w[c] = gv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __shared__ float red_ss[TT][4], red_dot[TT][4];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float ss = 0.0f;
+    if (t0 + t < T) {
+      const float4* rt = reinterpret_cast<const float4*>(r + (size_t)(t0 + t) * H);
+#pragma unroll
+      for (int c = 0; c < NW; ++c) {
+        const int q = threadIdx.x + 256 * c;
+        v[t][c] = q < n4 ? rt[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q < n4) {
+          ss = fmaf(v[t][c].x, v[t][c].x, ss);
+          ss = fmaf(v[t][c].y, v[t][c].y, ss);
+          ss = fmaf(v[t][c].z, v[t][c].z, ss);
+          ss = fmaf(v[t][c].w, v[t][c].w, ss);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NW; ++c) v[t][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ss = group_sum<kWave>(ss);
+    if (lane == 0) red_ss[t][wid] = ss;
+  }
+  __syncthreads();
+  const int s4 = (n4 + E - 1) / E;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float acc = 0.0f;
+    if (t0 + t < T) {
+      const float tot = (red_ss[t][0] + red_ss[t][1]) + (red_ss[t][2] + red_ss[t][3]);
+      const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+      float4* nt = reinterpret_cast<float4*>(nout + (size_t)(t0 + t) * H);
+#pragma unroll
+      for (int c = 0; c < NW; ++c) {
+        const int q = threadIdx.x + 256 * c;
+        const float4 x = v[t][c], gg = gv[c];
+        const float4 nv = make_float4((x.x * inv) * gg.x, (x.y * inv) * gg.y, (x.z * inv) * gg.z,
+                                      (x.w * inv) * gg.w);
+        acc = fmaf(w[c].x, nv.x, acc);
+        acc = fmaf(w[c].y, nv.y, acc);
+        acc = fmaf(w[c].z, nv.z, acc);
+        acc = fmaf(w[c].w, nv.w, acc);
+        if (q < n4 && q >= e * s4 && q < e * s4 + s4) nt[q] = nv;
+      }
+    }
+    const float sv = wave_sum(acc);
+    if (lane == 0) red_dot[t][wid] = sv;
+  }
+  __syncthreads();
+  if (threadIdx.x < TT && t0 + (int)threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float o = (red_dot[t][0] + red_dot[t][1]) + (red_dot[t][2] + red_dot[t][3]);
+    if (bias) o += bias[e];
+    logits[(size_t)(t0 + t) * E + e] = o;
+  }
+}
+
+template <int TT>
+static hipError_t norm_router_dispatch(dim3 grid, hipStream_t s, const float* r, const float* gamma, float eps,
+                                       const float* wr, const float* bias, int T, int H, int E, float* logits,
+                                       float* nout) {
+  const int nw = (H / 4 + 255) / 256;
+#define MOE_NRT(N) \
+  k_norm_router_logits<TT, N><<<grid, 256, 0, s>>>(r, gamma, eps, wr, bias, T, H, E, logits, nout)
+  switch (nw) {
+    case 1: MOE_NRT(1); break;
+    case 2: MOE_NRT(2); break;
+    case 3: MOE_NRT(3); break;
+    case 4: MOE_NRT(4); break;
+    case 5: MOE_NRT(5); break;
+    case 6: MOE_NRT(6); break;
+    case 7: MOE_NRT(7); break;
+    case 8: MOE_NRT(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_NRT
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_router_logits(const float* r, const float* gamma, float eps, const float* wr,
+                                     const float* bias, int T, int H, int E, float* logits, float* nout,
+                                     hipStream_t s) {
+  if (T == 1) return norm_router_dispatch<1>(dim3(E, 1), s, r, gamma, eps, wr, bias, T, H, E, logits, nout);
+  constexpr int TT = 4;
+  return norm_router_dispatch<TT>(dim3(E, (T + TT - 1) / TT), s, r, gamma, eps, wr, bias, T, H, E, logits, nout);
+}
+
 // ---------------------------------------------------------------- top-k + softmax
 // (selection in topk.h)
 template <int MAXV>

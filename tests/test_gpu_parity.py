@@ -365,6 +365,39 @@ def test_prefill_token_batches_equal_separate_calls():
     P.assert_out_close(out[rows], r_out)
 
 
+@pytest.mark.parametrize("H,I,E,k,T", [(512, 256, 16, 4, 3), (256, 128, 100, 3, 5), (1024, 256, 8, 2, 1)])
+def test_stack_small_matches_oracle_layer_by_layer(H, I, E, k, T):
+    """The layer stack (RMSNorm inside each layer's router kernel, fp32
+    residual stream) on small shapes: two layers against the oracle layer by
+    layer on the GPU's logits.  E > H/4 leaves some router workgroups without
+    a slice of the normalised rows to write; T > 1 runs the 4-token tiles."""
+    w = synth.Workload("st", 68, T, H, I, E, k, "bf16", weight_seed=8000 + H + E)
+    desc = sd.desc_for(w)
+    packed, exs = [], []
+    for l in range(2):
+        c, s, ex = experts_host(w, l)
+        packed.append(pack_whole(w, c, s)[1:])
+        exs.append(ex)
+    wrs = [sd.router_w(w, l) for l in range(2)]
+    gam = [sd.gamma(w, l) for l in range(2)]
+    x = sd.tokens(w, range(T))
+    resid = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe.stack_workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
+    moe.moe_mxfp4_stack_forward(desc, [p[0] for p in packed], [p[1] for p in packed], wrs, None, gam, w.eps, x, k,
+                                resid, ws)
+    torch.cuda.synchronize()
+    got = resid.cpu().numpy()
+    r = synth.tokens_f32(w, range(T))
+    for l in range(2):
+        n = oracle.rmsnorm(r, gam[l].cpu().numpy(), w.eps)
+        lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+        moe.moe_router_logits(desc, torch.from_numpy(n).to(DEV), wrs[l], None, lg)
+        torch.cuda.synchronize()
+        o, *_ = oracle.moe_forward(n, wrs[l].cpu().numpy(), exs[l], H, I, k, logits_override=lg.cpu().numpy())
+        r = oracle.residual_add(r, o)
+    P.assert_out_close(got, r)
+
+
 def test_grouped_stages_equal_forward_and_skip_malformed_blocks():
     """The prefill form run stage by stage through its own entry points (sort,
     expert blocks, grouped gate/up, grouped down, combine) gives the forward's
