@@ -222,13 +222,11 @@ __device__ __forceinline__ void scales_put(const SPieces<U>& sp, uint8_t* tab, i
 }
 
 // Per-MT shape: MS m-tiles staged (even; rows past the block read 0), NV
-// 16-byte pieces per thread per chunk and activation term, FD = activation
-// fragments fetched one MFMA step ahead.
+// 16-byte pieces per thread per chunk and activation term.
 template <int MT>
 struct Shape {
   static constexpr int MS = (MT + 1) / 2 * 2;
   static constexpr int NV = MS * 16 * 16 / kThr;
-  static constexpr bool FD = MT <= 4;
 };
 
 // ---------------------------------------------------------------- activation tiles by DMA
@@ -295,6 +293,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 constexpr int kGU_NT = 128;
 // Weight ring: 4 superchunks (K = 7168 gives 28, whole rounds).
 constexpr int kGuDB = 4;
+constexpr int kGuPF = 4;  // activation fragments requested ahead of use (2 MFMAs each)
 // Scale-table pieces per thread and matrix: 128 rows x nb bytes in 16-byte
 // pieces over 512 threads covers nb <= 64 * kGuScaleU, i.e. K <= 12288.
 constexpr int kGuScaleU = 6;
@@ -442,28 +441,26 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
         const uint8_t* A = lds + slot * kBuf;
         const float sgv = e8m0_operand((rg[d].s[h] >> (8 * g)) & 0xFFu);
         const float suv = e8m0_operand((ru[d].s[h] >> (8 * g)) & 0xFFu);
-        bf16x8 fa[2][MT];
-        if (S::FD) {
+        // fragment (step s, m-tile m) = pair i = s*MT + m; the fragment of pair
+        // i + kGuPF is requested before the multiplies of pair i (scheduling
+        // barriers keep that order), so LDS latency hides behind 2 kGuPF MFMAs
+        constexpr int NQ = 4 * MT, RF = kGuPF + 1;
+        bf16x8 fa[RF];
 #pragma unroll
-          for (int m = 0; m < MT; ++m) fa[0][m] = lds_frag_sw(A, m, nl, 4 * g);
-        }
+        for (int i = 0; i < kGuPF && i < NQ; ++i) fa[i % RF] = lds_frag_sw(A, i % MT, nl, 4 * g + i / MT);
+        bf16x8 bg = decode8(rg[d].q[h][0], sgv), bu = decode8(ru[d].q[h][0], suv);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (S::FD) {
-            if (s < 3) {
-#pragma unroll
-              for (int m = 0; m < MT; ++m) fa[(s + 1) & 1][m] = lds_frag_sw(A, m, nl, 4 * g + s + 1);
-            }
-          } else {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) fa[s & 1][m] = lds_frag_sw(A, m, nl, 4 * g + s);
+        for (int i = 0; i < NQ; ++i) {
+          const int st = i / MT, m = i % MT;
+          if (i + kGuPF < NQ) fa[(i + kGuPF) % RF] = lds_frag_sw(A, (i + kGuPF) % MT, nl, 4 * g + (i + kGuPF) / MT);
+          if (m == 0 && st > 0) {
+            bg = decode8(rg[d].q[h][st], sgv);
+            bu = decode8(ru[d].q[h][st], suv);
           }
-          const bf16x8 bg = decode8(rg[d].q[h][s], sgv), bu = decode8(ru[d].q[h][s], suv);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bg, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][m], bu, acc[m][1], 0, 0, 0);
-          }
+          __builtin_amdgcn_sched_barrier(0);
+          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i % RF], bg, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i % RF], bu, acc[m][1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // chunk c + 1 must be in LDS for every wave before anyone reads it
         if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 0)>();
@@ -544,7 +541,10 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
 constexpr int kDN_NT = 256;
 constexpr int kDnTiles = 4;
 // Weight ring: 3 superchunks (K = 1536 gives 6 per tile).
-constexpr int dn_db(int) { return 3; }
+constexpr int dn_db(int mt) { return mt >= 5 ? 2 : 3; }
+// fragment pairs (both terms) requested ahead of use (4 MFMAs each); 1 for
+// blocks of 7-8 m-tiles, whose accumulators leave no room for more
+constexpr int dn_pf(int mt) { return mt >= 7 ? 1 : 2; }
 
 // Codes and scales of one superchunk from memory.  The lane's part of the
 // offsets (its row in the first tile, its code block) is a vector offset; the
@@ -569,7 +569,7 @@ constexpr int kDnActBytes = 3 * 2 * 96 * kDmaRow;  // holds every ring: 5x2x32, 
 // per chunk: MS DMA instructions (two terms), and 6 weight loads (two n-tiles:
 // two code blocks and the scales each) in even chunks
 static_assert(dma_waits_exact(5, 2, 6, 3, 48) && dma_waits_exact(4, 4, 6, 3, 48) && dma_waits_exact(3, 6, 6, 2, 48) &&
-                  dma_waits_exact(2, 8, 6, 2, 48) && dma_waits_exact(5, 2, 6, 3, 24) && dma_waits_exact(2, 8, 6, 3, 12) &&
+                  dma_waits_exact(2, 8, 6, 2, 48) && dma_waits_exact(5, 2, 6, 3, 24) && dma_waits_exact(2, 8, 6, 2, 8) &&
                   dma_waits_exact(4, 4, 6, 3, 6),
               "down DMA wait counts");
 
@@ -660,18 +660,35 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
         const uint8_t* Al = Ah + kTerm;
         const float s0v = e8m0_operand((rb[d][0].s[h] >> (8 * g)) & 0xFFu);
         const float s1v = e8m0_operand((rb[d][1].s[h] >> (8 * g)) & 0xFFu);
+        // pair i = s*MT + m (step s, m-tile m); both terms' fragments of pair
+        // i + kDnPF are requested before the four multiplies of pair i
+        constexpr int kDnPF = dn_pf(MT);
+        constexpr int NQ = 4 * MT, RF = kDnPF + 1;
+        bf16x8 fh[RF], fl[RF];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 b0 = decode8(rb[d][0].q[h][s], s0v), b1 = decode8(rb[d][1].q[h][s], s1v);
+        for (int i = 0; i < kDnPF && i < NQ; ++i) {
+          fh[i % RF] = lds_frag_sw(Ah, i % MT, nl, 4 * g + i / MT);
+          fl[i % RF] = lds_frag_sw(Al, i % MT, nl, 4 * g + i / MT);
+        }
+        bf16x8 b0 = decode8(rb[d][0].q[h][0], s0v), b1 = decode8(rb[d][1].q[h][0], s1v);
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const bf16x8 fh = lds_frag_sw(Ah, m, nl, 4 * g + s);
-            const bf16x8 fl = lds_frag_sw(Al, m, nl, 4 * g + s);
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b0, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, b1, acc[m][1], 0, 0, 0);
-            acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b0, acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, b1, acc[m][1], 0, 0, 0);
+        for (int i = 0; i < NQ; ++i) {
+          const int st = i / MT, m = i % MT;
+          if (i + kDnPF < NQ) {
+            const int j = i + kDnPF;
+            fh[j % RF] = lds_frag_sw(Ah, j % MT, nl, 4 * g + j / MT);
+            fl[j % RF] = lds_frag_sw(Al, j % MT, nl, 4 * g + j / MT);
           }
+          if (m == 0 && st > 0) {
+            b0 = decode8(rb[d][0].q[h][st], s0v);
+            b1 = decode8(rb[d][1].q[h][st], s1v);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh[i % RF], b0, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh[i % RF], b1, acc[m][1], 0, 0, 0);
+          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[i % RF], b0, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[i % RF], b1, acc[m][1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS, 6, 0)>();
         else wait_vm_barrier<dma_wait_ops(NB, MS, 6, 1)>();
