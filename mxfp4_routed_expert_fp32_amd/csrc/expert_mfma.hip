@@ -309,11 +309,11 @@ constexpr int kGuActSmall = 3 * 96 * kDmaRow;  // holds every small-LDS ring (5x
 constexpr int kGuActLarge = 3 * 128 * kDmaRow;
 
 // Vector memory operations a wave issues after the DMA of chunk c + 1 (issued
-// in chunk c + 2 - NB, first thing) until the end of chunk c: the DMAs of the
-// NB - 2 chunks after it (dmaops each) and the weight loads (codeops) of every
-// even chunk among the NB - 1 chunks from c + 2 - NB to c.
-constexpr int dma_wait_ops(int nb, int dmaops, int codeops, int h) {
-  const int da = nb - 1;
+// in chunk c + 1 - da, first thing, da = chunks requested ahead) until its
+// wait in chunk c (after the chunk's own loads): the DMAs of the da - 1
+// chunks after it (dmaops each) and the weight loads (codeops) of every even
+// chunk among the da chunks from c + 1 - da to c.
+constexpr int dma_wait_ops(int da, int dmaops, int codeops, int h) {
   const int p0 = ((h + 1 - da) % 2 + 2) % 2;  // parity of chunk c + 1 - da
   const int evens = p0 == 0 ? (da + 1) / 2 : da / 2;
   return (da - 1) * dmaops + codeops * evens;
@@ -324,8 +324,7 @@ constexpr int dma_wait_ops(int nb, int dmaops, int codeops, int h) {
 // the DMA it waits for: fewer would wait longer than needed, more would let a
 // chunk be read before it is in LDS.  (Stores issued between, at the down
 // kernel's tile ends, only lengthen a wait.)
-constexpr bool dma_waits_exact(int nb, int dmaops, int codeops, int db, int nchunks) {
-  const int da = nb - 1;
+constexpr bool dma_waits_exact(int da, int dmaops, int codeops, int db, int nchunks) {
   int last[160] = {};  // op count when the DMA of a chunk was issued
   int n = 0;
   const int v0 = 2 * (db - 1) > da ? 2 * (db - 1) : da;
@@ -333,7 +332,7 @@ constexpr bool dma_waits_exact(int nb, int dmaops, int codeops, int db, int nchu
     if (v + da >= 0) { n += dmaops; last[v + da] = n; }
     if (v % 2 == 0 && v / 2 + db - 1 >= 0) n += codeops;
   }
-  if (n - last[0] != dma_wait_ops(nb, dmaops, codeops, 1)) return false;
+  if (n - last[0] != dma_wait_ops(da, dmaops, codeops, 1)) return false;
   for (int sc0 = 0; sc0 < nchunks / 2; sc0 += db)
     for (int d = 0; d < db; ++d)
       for (int h = 0; h < 2; ++h) {
@@ -341,26 +340,27 @@ constexpr bool dma_waits_exact(int nb, int dmaops, int codeops, int db, int nchu
         n += dmaops;
         last[c + da] = n;
         if (h == 0) n += codeops;
-        if (n - last[c + 1] != dma_wait_ops(nb, dmaops, codeops, h)) return false;
+        if (n - last[c + 1] != dma_wait_ops(da, dmaops, codeops, h)) return false;
       }
   return true;
 }
-// gate/up: MS/2 DMA instructions and 4 code loads per chunk; the ring sizes used
-static_assert(dma_waits_exact(5, 1, 4, 4, 56) && dma_waits_exact(4, 2, 4, 4, 56) && dma_waits_exact(3, 3, 4, 4, 56) &&
-                  dma_waits_exact(3, 4, 4, 4, 56) && dma_waits_exact(2, 4, 4, 4, 56) && dma_waits_exact(5, 1, 4, 4, 2) &&
-                  dma_waits_exact(2, 4, 4, 4, 2) && dma_waits_exact(3, 3, 4, 4, 64) && dma_waits_exact(4, 2, 4, 4, 18) &&
-                  dma_waits_exact(4, 3, 4, 4, 56) && dma_waits_exact(3, 4, 4, 4, 2),
+// gate/up: MS/2 DMA instructions and 4 code loads per chunk; (da, MS) as used
+static_assert(dma_waits_exact(3, 1, 4, 4, 56) && dma_waits_exact(2, 2, 4, 4, 56) && dma_waits_exact(2, 3, 4, 4, 56) &&
+                  dma_waits_exact(1, 3, 4, 4, 56) && dma_waits_exact(1, 4, 4, 4, 56) && dma_waits_exact(3, 1, 4, 4, 2) &&
+                  dma_waits_exact(1, 4, 4, 4, 2) && dma_waits_exact(2, 3, 4, 4, 64) && dma_waits_exact(2, 2, 4, 4, 18),
               "gate/up DMA wait counts");
 
-template <int MT, int DB, int NB>
+template <int MT, int DB, int NB, bool MID>
 __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
                                              const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                              const int32_t* pid, const uint32_t* row_base, uint8_t* lds,
                                              int act_bytes, uint16_t* __restrict__ hterm) {
   using S = Shape<MT>;
   constexpr int MS = S::MS;
-  constexpr int DA = NB - 1;
-  static_assert(NB >= 2 && NB <= 5, "activation buffers");
+  // chunks requested ahead: NB - 2 when the barrier sits mid-chunk (a buffer
+  // is then still read after the barrier that follows its use), else NB - 1
+  constexpr int DA = MID ? NB - 2 : NB - 1;
+  static_assert(NB >= 2 && NB <= 5 && DA >= 1, "activation buffers");
   constexpr uint32_t kBuf = (uint32_t)MS * 16 * kDmaRow;
   static_assert(NB * MS * 16 * kDmaRow <= kGuActLarge, "ring fits the activation region");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -404,7 +404,7 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   }
   scales_put<kGuScaleU>(spg, tab, nb, ttotal);
   scales_put<kGuScaleU>(spu, tab + kGU_NT * pitch, nb, ttotal);
-  wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
+  wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d) {
     load_bscales(rg[d], tg, d, nsc);
@@ -414,6 +414,21 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   f32x4 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Activation fragments: pair i = s*MT + m (step s, m-tile m) of a chunk;
+  // the fragment of pair i + kGuPF is requested before the multiplies of pair
+  // i (scheduling barriers keep that order), so LDS latency hides behind
+  // 2 kGuPF MFMAs.  With MID the barrier for chunk c + 1 sits kGuPF pairs
+  // before the end of chunk c and the requests run on into chunk c + 1, so no
+  // chunk starts by waiting for its first fragment.  The ring of RF
+  // fragments divides the pairs of one unrolled round.
+  constexpr int NQ = 4 * MT, RF = 8;
+  static_assert(kGuPF < RF && kGuPF <= NQ && (2 * DB * NQ) % RF == 0, "fragment ring");
+  bf16x8 fa[RF];
+  if (MID) {
+#pragma unroll
+    for (int i = 0; i < kGuPF; ++i) fa[i % RF] = lds_frag_sw(lds, i % MT, nl, 4 * g + i / MT);
+  }
 
   // the ring holds whole superchunks; a phantom superchunk past K reads zeros
   // on both operands and adds nothing
@@ -439,32 +454,40 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint8_t* A = lds + slot * kBuf;
+        const uint8_t* An = lds + (slot + 1 == NB ? 0 : slot + 1) * kBuf;  // next chunk's buffer
         const float sgv = e8m0_operand((rg[d].s[h] >> (8 * g)) & 0xFFu);
         const float suv = e8m0_operand((ru[d].s[h] >> (8 * g)) & 0xFFu);
-        // fragment (step s, m-tile m) = pair i = s*MT + m; the fragment of pair
-        // i + kGuPF is requested before the multiplies of pair i (scheduling
-        // barriers keep that order), so LDS latency hides behind 2 kGuPF MFMAs
-        constexpr int NQ = 4 * MT, RF = kGuPF + 1;
-        bf16x8 fa[RF];
+        const int q0 = (2 * d + h) * NQ;  // ring position of this chunk's first pair
+        if (!MID) {
 #pragma unroll
-        for (int i = 0; i < kGuPF && i < NQ; ++i) fa[i % RF] = lds_frag_sw(A, i % MT, nl, 4 * g + i / MT);
+          for (int i = 0; i < kGuPF; ++i) fa[(q0 + i) % RF] = lds_frag_sw(A, i % MT, nl, 4 * g + i / MT);
+        }
         bf16x8 bg = decode8(rg[d].q[h][0], sgv), bu = decode8(ru[d].q[h][0], suv);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
           const int st = i / MT, m = i % MT;
-          if (i + kGuPF < NQ) fa[(i + kGuPF) % RF] = lds_frag_sw(A, (i + kGuPF) % MT, nl, 4 * g + (i + kGuPF) / MT);
+          const int j = i + kGuPF;
+          if (MID && j == NQ) {
+            // chunk c + 1 must be in LDS for every wave before its first read
+            if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0)>();
+            else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();
+          }
+          if (j < NQ) fa[(q0 + j) % RF] = lds_frag_sw(A, j % MT, nl, 4 * g + j / MT);
+          else if (MID) fa[(q0 + j) % RF] = lds_frag_sw(An, (j - NQ) % MT, nl, 4 * g + (j - NQ) / MT);
           if (m == 0 && st > 0) {
             bg = decode8(rg[d].q[h][st], sgv);
             bu = decode8(ru[d].q[h][st], suv);
           }
           __builtin_amdgcn_sched_barrier(0);
-          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i % RF], bg, acc[m][0], 0, 0, 0);
-          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i % RF], bu, acc[m][1], 0, 0, 0);
+          acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[(q0 + i) % RF], bg, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[(q0 + i) % RF], bu, acc[m][1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // chunk c + 1 must be in LDS for every wave before anyone reads it
-        if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 0)>();
-        else wait_vm_barrier<dma_wait_ops(NB, MS / 2, 4, 1)>();
+        if (!MID) {
+          // chunk c + 1 must be in LDS for every wave before anyone reads it
+          if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0)>();
+          else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();
+        }
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
@@ -512,18 +535,18 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
   __syncthreads();
   const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
   switch ((cnt + 15) / 16) {
-    case 1: gateup_block<1, kGuDB, gu_nbuf_small(1)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 2: gateup_block<2, kGuDB, gu_nbuf_small(2)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 3: gateup_block<3, kGuDB, gu_nbuf_small(3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 4: gateup_block<4, kGuDB, gu_nbuf_small(4)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 5: (large ? gateup_block<5, kGuDB, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<5, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    case 6: (large ? gateup_block<6, kGuDB, 4>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<6, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    case 7: (large ? gateup_block<7, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<7, kGuDB, 2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    default: (large ? gateup_block<8, kGuDB, 3>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<8, kGuDB, 2>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 1: gateup_block<1, kGuDB, gu_nbuf_small(1), (gu_nbuf_small(1) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 2: gateup_block<2, kGuDB, gu_nbuf_small(2), (gu_nbuf_small(2) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 3: gateup_block<3, kGuDB, gu_nbuf_small(3), (gu_nbuf_small(3) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 4: gateup_block<4, kGuDB, gu_nbuf_small(4), (gu_nbuf_small(4) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 5: (large ? gateup_block<5, kGuDB, 4, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<5, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 6: (large ? gateup_block<6, kGuDB, 4, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<6, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 7: (large ? gateup_block<7, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<7, kGuDB, 2, false>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    default: (large ? gateup_block<8, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<8, kGuDB, 2, false>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
   }
 }
 
@@ -568,9 +591,9 @@ constexpr int dn_nbuf(int mt) { return mt <= 2 ? 5 : (mt <= 4 ? 4 : (mt <= 6 ? 3
 constexpr int kDnActBytes = 3 * 2 * 96 * kDmaRow;  // holds every ring: 5x2x32, 4x2x64, 3x2x96, 2x2x128 rows
 // per chunk: MS DMA instructions (two terms), and 6 weight loads (two n-tiles:
 // two code blocks and the scales each) in even chunks
-static_assert(dma_waits_exact(5, 2, 6, 3, 48) && dma_waits_exact(4, 4, 6, 3, 48) && dma_waits_exact(3, 6, 6, 2, 48) &&
-                  dma_waits_exact(2, 8, 6, 2, 48) && dma_waits_exact(5, 2, 6, 3, 24) && dma_waits_exact(2, 8, 6, 2, 8) &&
-                  dma_waits_exact(4, 4, 6, 3, 6),
+static_assert(dma_waits_exact(4, 2, 6, 3, 48) && dma_waits_exact(3, 4, 6, 3, 48) && dma_waits_exact(2, 6, 6, 2, 48) &&
+                  dma_waits_exact(1, 8, 6, 2, 48) && dma_waits_exact(4, 2, 6, 3, 24) && dma_waits_exact(1, 8, 6, 2, 8) &&
+                  dma_waits_exact(3, 4, 6, 3, 6),
               "down DMA wait counts");
 
 // Tiles nt0 .. nt0 + kDnTiles - 1 (those below ntiles) of one expert block.
@@ -636,7 +659,7 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
     if (v + DA >= 0) dma_q(v + DA, lds + (v + DA) * kBuf);
     if (v % 2 == 0 && v / 2 + DB - 1 >= 0) load_b(rb[v / 2 + DB - 1], v / 2 + DB - 1);
   }
-  wait_vm_barrier<dma_wait_ops(NB, MS, 6, 1)>();
+  wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1)>();
 
   f32x4 acc[MT][2];
 #pragma unroll
@@ -690,8 +713,8 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[i % RF], b1, acc[m][1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == 0) wait_vm_barrier<dma_wait_ops(NB, MS, 6, 0)>();
-        else wait_vm_barrier<dma_wait_ops(NB, MS, 6, 1)>();
+        if (h == 0) wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 0)>();
+        else wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1)>();
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
