@@ -217,6 +217,13 @@ def moe_topk_softmax(logits, k, idx, w, stream=None):
         _ptr(logits), logits.shape[0], logits.shape[1], k, _ptr(idx), _ptr(w), _stream(stream)))
 
 
+def sort_workspace_bytes(n_experts: int, n_tokens: int, k: int) -> int:
+    b = ctypes.c_size_t()
+    _check("moe_sort_workspace_bytes",
+           lib().moe_sort_workspace_bytes(n_experts, n_tokens, k, ctypes.byref(b)))
+    return b.value
+
+
 def moe_sort_by_expert(topk_idx, n_experts, expert_offsets, pair_list, workspace=None, stream=None):
     nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("moe_sort_by_expert", lib().moe_sort_by_expert(

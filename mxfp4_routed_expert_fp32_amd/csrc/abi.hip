@@ -67,7 +67,7 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, rpart, total;
+  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, rpart, sortws, total;
   int max_blocks;
   bool has_rpart;
 };
@@ -97,6 +97,7 @@ int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) 
   size_t rp = 0;
   if (L->has_rpart && !mul_ok(TE, (size_t)moe::router_mfma_splits(T, d->hidden) * 4, &rp)) return MOE_ERR_OVERFLOW;
   L->rpart = c.take(rp);
+  L->sortws = c.take(moe::sort_workspace_bytes(T, d->n_experts));
   L->total = c.take(0);
   if (c.overflow) return MOE_ERR_OVERFLOW;
   // pair indices are int32 on the device; MFMA-path byte offsets are 32-bit
@@ -173,7 +174,7 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
     for (int64_t t0 = 0; t0 < T; t0 += tb) {
       const int n = (int)std::min<int64_t>(tb, T - t0);
       const int Pn = n * k;
-      MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, s)));
+      MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s)));
       MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
       MOE_TRY(dev(moe::launch_gateup_mfma(xb + t0 * H, n, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, k,
                                           Pn, hterm, s)));
@@ -395,22 +396,23 @@ int moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, siz
   if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
     return MOE_ERR_SHAPE;
   if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
-  *bytes = 0;  // the sort keeps its scratch in LDS
+  *bytes = moe::sort_workspace_bytes(n_tokens, n_experts);  // per-block counts for many tokens
   return MOE_OK;
 }
 
 int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_experts, int32_t k,
                        int32_t* expert_offsets, int32_t* pair_list, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!topk_idx || !expert_offsets || !pair_list) return MOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
     return MOE_ERR_SHAPE;
   if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)n_tokens * k > INT32_MAX) return MOE_ERR_OVERFLOW;
+  const size_t need = moe::sort_workspace_bytes(n_tokens, n_experts);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return MOE_ERR_ALIGN;
   return dev(moe::launch_sort_by_expert(topk_idx, n_tokens, n_experts, k, expert_offsets, pair_list,
-                                        as_stream(stream)));
+                                        need > 0 ? workspace : nullptr, as_stream(stream)));
 }
 
 int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks) {

@@ -17,8 +17,11 @@ hipError_t launch_norm_router_logits(const float* r, const float* gamma, float e
                                      hipStream_t s);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                hipStream_t s);
-hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets,
-                                 int32_t* pairs, hipStream_t s);
+// Stable sort of the (token, rank) pairs by expert.  ws: sort_workspace_bytes(T, E)
+// bytes (may be null when that is 0; with null the one-workgroup sort runs).
+size_t sort_workspace_bytes(int T, int E);
+hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* pairs,
+                                 void* ws, hipStream_t s);
 
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
                               const uint8_t* codes, const uint8_t* scales, int H, int I, int E,

@@ -224,15 +224,82 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- counting sort
-// Stable sort of the T*k (token, rank) pairs by expert, in one workgroup:
-// histogram -> exclusive scan -> scatter.  Within an expert the pairs are in
-// token order: each token selects an expert at most once, so a pair's place
-// is the number of earlier tokens that selected the same expert.  Tokens are
-// taken 64 at a time; a 64-bit mask per expert records which tokens of the
-// chunk selected it, and a popcount below the token's bit gives its place.
+// Stable sort of the T*k (token, rank) pairs by expert: histogram ->
+// exclusive scan -> scatter.  Within an expert the pairs are in token order:
+// each token selects an expert at most once, so a pair's place is the number
+// of earlier tokens that selected the same expert.  Tokens are taken 64 at a
+// time; a 64-bit mask per expert records which tokens of the chunk selected
+// it, and a popcount below the token's bit gives its place.
+//
+// Up to kSortMultiMinTokens tokens one workgroup does everything.  Above, the
+// tokens are cut into blocks of kSortBlockTokens: each block's histogram, a
+// prefix over blocks per expert, a scan over experts, and a scatter in which
+// every block starts from its own cursors -- the same order as one workgroup.
 constexpr int kSortThreads = 1024;
+constexpr int kSortBlockTokens = 256;
+constexpr int kSortMultiMinTokens = 1024;
 
-// running[E] and mask[E] live in LDS (E <= 4096: 48 KB).
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Scatter of tokens [t0, t1) with cursors running[E] (LDS, advanced) and
+// mask[E] (LDS, zero on entry and exit); NT threads.
+template <int NT>
+__device__ void scatter_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
+                               unsigned long long* mask, int32_t* running, int32_t* __restrict__ pairs) {
+  const int tid = threadIdx.x;
+  for (int c0 = t0; c0 < t1; c0 += 64) {
+    const int np = min(64, t1 - c0) * k;
+    const int32_t* ic = idx + (size_t)c0 * k;
+    for (int p = tid; p < np; p += NT) atomicOr(&mask[clamp_expert(ic[p], E)], 1ull << (p / k));
+    __syncthreads();
+    for (int p = tid; p < np; p += NT) {
+      const int e = clamp_expert(ic[p], E);
+      const unsigned long long below = mask[e] & ((1ull << (p / k)) - 1ull);
+      pairs[running[e] + __popcll(below)] = c0 * k + p;
+    }
+    __syncthreads();
+    // the pair of the lowest token of each expert advances that expert's cursor
+    for (int p = tid; p < np; p += NT) {
+      const int e = clamp_expert(ic[p], E);
+      const unsigned long long m = mask[e];
+      if ((m & ((1ull << (p / k)) - 1ull)) == 0ull) running[e] += __popcll(m);
+    }
+    __syncthreads();
+    for (int p = tid; p < np; p += NT) mask[clamp_expert(ic[p], E)] = 0ull;
+    __syncthreads();
+  }
+}
+
+// Exclusive scan of counts[E] into offsets[E] (offsets[E] = total) by one
+// workgroup of kSortThreads; each thread owns `per` consecutive experts.
+// Also writes the scanned values to base_out when it is not null (it may be
+// counts itself: a thread reads each of its counts before overwriting it).
+__device__ void scan_experts(const int32_t* counts, int E, int32_t* __restrict__ offsets, int32_t* base_out,
+                             int32_t* part) {
+  const int tid = threadIdx.x;
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  const int e0 = tid * per;
+  int32_t local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) local += counts[e];
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kSortThreads; off <<= 1) {
+    const int32_t v = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t base = part[tid] - local;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    const int32_t c = counts[e];
+    offsets[e] = base;
+    if (base_out) base_out[e] = base;
+    base += c;
+  }
+  if (tid == kSortThreads - 1) offsets[E] = part[tid];
+}
+
+// One workgroup: running[E] and mask[E] live in LDS (E <= 4096: 48 KB).
 __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* __restrict__ idx,
                                                                  int T, int E, int k,
                                                                  int32_t* __restrict__ offsets,
@@ -245,68 +312,69 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* 
   for (int e = tid; e < E; e += kSortThreads) { running[e] = 0; mask[e] = 0ull; }
   __syncthreads();
   const int P = T * k;
-  for (int p = tid; p < P; p += kSortThreads) {
-    int e = idx[p];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    atomicAdd(&running[e], 1);
+  for (int p = tid; p < P; p += kSortThreads) atomicAdd(&running[clamp_expert(idx[p], E)], 1);
+  __syncthreads();
+  scan_experts(running, E, offsets, running, part);  // cursors start at the offsets
+  __syncthreads();
+  scatter_tokens<kSortThreads>(idx, 0, T, E, k, mask, running, pairs);
+}
+
+// Many tokens, step 1: counts[b][e] = pairs of token block b that chose e.
+__global__ __launch_bounds__(256) void k_sort_count(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                    int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];  // [E]
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int p0 = b * kSortBlockTokens * k, p1 = min(T, (b + 1) * kSortBlockTokens) * k;
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) atomicAdd(&hist[clamp_expert(idx[p], E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)b * E + e] = hist[e];
+}
+
+// Step 2: per expert, counts[b][e] becomes the pairs of blocks before b
+// (exclusive prefix over blocks), totals[e] the expert's pair count.
+__global__ __launch_bounds__(256) void k_sort_prefix(int32_t* __restrict__ counts, int nblk, int E,
+                                                     int32_t* __restrict__ totals) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  int32_t run = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const int32_t c = counts[(size_t)b * E + e];
+    counts[(size_t)b * E + e] = run;
+    run += c;
+  }
+  totals[e] = run;
+}
+
+// Step 3: offsets = exclusive scan of totals (one workgroup).
+__global__ __launch_bounds__(kSortThreads) void k_sort_offsets(const int32_t* __restrict__ totals, int E,
+                                                               int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[kSortThreads];
+  scan_experts(totals, E, offsets, nullptr, part);
+}
+
+// Step 4: block b scatters its tokens from cursors offsets[e] + counts[b][e].
+__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ pairs) {
+  extern __shared__ unsigned long long sort_lds[];
+  unsigned long long* mask = sort_lds;                          // [E]
+  int32_t* running = reinterpret_cast<int32_t*>(sort_lds + E);  // [E]
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    running[e] = offsets[e] + counts[(size_t)b * E + e];
+    mask[e] = 0ull;
   }
   __syncthreads();
-  // exclusive scan of the counts: each thread owns `per` consecutive experts
-  const int per = (E + kSortThreads - 1) / kSortThreads;
-  const int e0 = tid * per;
-  int32_t local = 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) local += running[e];
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kSortThreads; off <<= 1) {
-    int32_t v = (tid >= off) ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t base = part[tid] - local;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    int32_t c = running[e];
-    offsets[e] = base;
-    running[e] = base;
-    base += c;
-  }
-  if (tid == 0) offsets[E] = P;
-  __syncthreads();
-  for (int c0 = 0; c0 < T; c0 += 64) {
-    const int np = min(64, T - c0) * k;
-    const int32_t* ic = idx + (size_t)c0 * k;
-    for (int p = tid; p < np; p += kSortThreads) {
-      int e = ic[p];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-      atomicOr(&mask[e], 1ull << (p / k));
-    }
-    __syncthreads();
-    for (int p = tid; p < np; p += kSortThreads) {
-      int e = ic[p];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-      const int tl = p / k;
-      const unsigned long long m = mask[e];
-      const unsigned long long below = m & ((1ull << tl) - 1ull);
-      pairs[running[e] + __popcll(below)] = c0 * k + p;
-    }
-    __syncthreads();
-    // the pair of the lowest token of each expert advances that expert's cursor
-    for (int p = tid; p < np; p += kSortThreads) {
-      int e = ic[p];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-      const int tl = p / k;
-      const unsigned long long m = mask[e];
-      if ((m & ((1ull << tl) - 1ull)) == 0ull) running[e] += __popcll(m);
-    }
-    __syncthreads();
-    for (int p = tid; p < np; p += kSortThreads) {
-      int e = ic[p];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-      mask[e] = 0ull;
-    }
-    __syncthreads();
-  }
+  scatter_tokens<256>(idx, b * kSortBlockTokens, min(T, (b + 1) * kSortBlockTokens), E, k, mask, running, pairs);
+}
+
+size_t sort_workspace_bytes(int T, int E) {
+  if (T < kSortMultiMinTokens) return 0;
+  const size_t nblk = (size_t)(T + kSortBlockTokens - 1) / kSortBlockTokens;
+  return (nblk + 1) * (size_t)E * sizeof(int32_t);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -356,10 +424,20 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets,
-                                 int32_t* pairs, hipStream_t s) {
-  size_t lds = (size_t)E * (sizeof(unsigned long long) + sizeof(int32_t));
-  k_sort_by_expert<<<1, kSortThreads, lds, s>>>(idx, T, E, k, offsets, pairs);
+hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* pairs,
+                                 void* ws, hipStream_t s) {
+  const size_t lds = (size_t)E * (sizeof(unsigned long long) + sizeof(int32_t));
+  if (T < kSortMultiMinTokens || ws == nullptr) {
+    k_sort_by_expert<<<1, kSortThreads, lds, s>>>(idx, T, E, k, offsets, pairs);
+    return hipGetLastError();
+  }
+  const int nblk = (T + kSortBlockTokens - 1) / kSortBlockTokens;
+  int32_t* counts = static_cast<int32_t*>(ws);  // [nblk][E]
+  int32_t* totals = counts + (size_t)nblk * E;  // [E]
+  k_sort_count<<<nblk, 256, (size_t)E * sizeof(int32_t), s>>>(idx, T, E, k, counts);
+  k_sort_prefix<<<(E + 255) / 256, 256, 0, s>>>(counts, nblk, E, totals);
+  k_sort_offsets<<<1, kSortThreads, 0, s>>>(totals, E, offsets);
+  k_sort_scatter<<<nblk, 256, lds, s>>>(idx, T, E, k, offsets, counts, pairs);
   return hipGetLastError();
 }
 

@@ -121,6 +121,13 @@ def test_other_entry_points_reject_before_launch():
     assert L.moe_topk_softmax(16, 1, 5000, 4, 16, 16, None) == -7
     assert L.moe_topk_softmax(None, 1, 8, 2, 16, 16, None) == -1
     assert L.moe_sort_by_expert(16, 0, 8, 2, 16, 16, None, 0, None) == -2
+    # from 1024 tokens the sort works in blocks of 256 tokens and needs per-block counts
+    assert moe.sort_workspace_bytes(896, 1023, 16) == 0
+    assert moe.sort_workspace_bytes(896, 1024, 16) == (4 + 1) * 896 * 4
+    assert moe.sort_workspace_bytes(896, 4097, 16) == (17 + 1) * 896 * 4
+    assert L.moe_sort_by_expert(16, 4096, 896, 16, 16, 16, None, 0, None) == -5
+    assert L.moe_sort_by_expert(16, 4096, 896, 16, 16, 16, 16, 17 * 896 * 4 - 1, None) == -5
+    assert L.moe_sort_by_expert(16, 4096, 896, 16, 16, 16, 8, 17 * 896 * 4, None) == -4
     assert L.moe_rmsnorm(16, 16, ctypes.c_float(1e-6), 1, 7, 16, None) == -2
     assert L.moe_residual_add(16, None, 4, None) == -1
     g = ctypes.c_void_p()

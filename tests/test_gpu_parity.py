@@ -185,12 +185,23 @@ def test_router_split_k_matches_whole_tiles(T, H, E):
 
 
 def test_sort_by_expert_matches_stable_sort():
+    """One workgroup up to 1023 tokens, token blocks of 256 above (ragged last
+    block, a skewed choice of experts, the largest E): both give numpy's
+    stable argsort by expert."""
     rng = np.random.default_rng(9)
-    for T, E, k in [(1, 8, 2), (64, 896, 16), (4096, 896, 16), (130, 50, 5)]:
-        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    for T, E, k, skew in [(1, 8, 2, False), (64, 896, 16, False), (4096, 896, 16, False), (130, 50, 5, False),
+                          (1023, 40, 4, False), (1025, 40, 4, True), (5000, 4096, 8, False), (4097, 896, 16, True)]:
+        if skew:  # most tokens pick the same few experts first
+            idx = np.stack([np.r_[np.arange(3), 3 + rng.permutation(E - 3)[:k - 3]] if t % 5 else rng.permutation(E)[:k]
+                            for t in range(T)]).astype(np.int32)
+        else:
+            idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
         offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
         pairs = torch.empty(T * k, dtype=torch.int32, device=DEV)
-        moe.moe_sort_by_expert(torch.from_numpy(idx).to(DEV), E, offs, pairs)
+        nws = moe.sort_workspace_bytes(E, T, k)
+        assert (nws > 0) == (T >= 1024)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+        moe.moe_sort_by_expert(torch.from_numpy(idx).to(DEV), E, offs, pairs, ws)
         torch.cuda.synchronize()
         flat = idx.reshape(-1)
         order = np.argsort(flat, kind="stable")  # by expert, then pair id (= token, rank)
