@@ -157,10 +157,14 @@ struct BSuper {
 };
 
 // Codes: boff = row * row_bytes + 16 g (or kOOB for a row past the matrix).
-__device__ __forceinline__ void load_bcodes(BSuper& b, rsrc_t rc, uint32_t boff, int sc, int nsc) {
+// Half hf of superchunk sc: code block g + 4 hf.
+__device__ __forceinline__ void load_bcode_half(BSuper& b, rsrc_t rc, uint32_t boff, int sc, int nsc, int hf) {
   const bool ok = sc < nsc;
-  b.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u : kOOB, 0, 0);
-  b.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u + 64u : kOOB, 0, 0);
+  b.q[hf] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? boff + (uint32_t)sc * 128u + 64u * (uint32_t)hf : kOOB, 0, 0);
+}
+__device__ __forceinline__ void load_bcodes(BSuper& b, rsrc_t rc, uint32_t boff, int sc, int nsc) {
+  load_bcode_half(b, rc, boff, sc, nsc, 0);
+  load_bcode_half(b, rc, boff, sc, nsc, 1);
 }
 
 // Scales from this row's line of the LDS scale table; a superchunk past K
@@ -271,15 +275,20 @@ __device__ __forceinline__ bf16x8 lds_frag_sw(const uint8_t* buf, int m, int nl,
   return as_bf16x8(*reinterpret_cast<const uint4*>(buf + (m * 16 + nl) * kDmaRow + ((p ^ swz_key(nl)) << 4)));
 }
 
-// Waits until at most n vector memory operations of this wave are in flight,
-// and for its LDS operations, then joins the workgroup barrier.  The barrier
-// carries no memory fence (a fence would wait for every load in flight); the
-// empty asm keeps the compiler from moving memory accesses across it.
-template <int N>
+// Waits until at most N vector memory operations of this wave are in flight
+// (and, with LDS_DRAIN, for its LDS operations), then joins the workgroup
+// barrier.  The barrier carries no memory fence (a fence would wait for every
+// load in flight); the empty asm keeps the compiler from moving memory
+// accesses across it.  The barriers inside the chunk loops skip the LDS
+// drain: the buffer the next DMA overwrites was last read in an earlier
+// chunk, and those reads were consumed (hence complete) before this barrier,
+// while fragment reads of later chunks may stay in flight across it.  The
+// prologue barriers drain, since LDS writes (the scale table) precede them.
+template <int N, bool LDS_DRAIN = true>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt field");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | ((LDS_DRAIN ? 0x0 : 0xF) << 8));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -424,6 +433,15 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   // fragments divides the pairs of one unrolled round.
   constexpr int NQ = 4 * MT, RF = 8;
   static_assert(kGuPF < RF && kGuPF <= NQ && (2 * DB * NQ) % RF == 0, "fragment ring");
+  // An even chunk's four weight loads (gate and up halves of one superchunk)
+  // go between its multiplies at pairs WP0 + k WS, all before the chunk's
+  // wait, so the address unit takes them one at a time instead of in one
+  // burst with every other wave's; chunks with few pairs issue them up front.
+  // Either way they follow the chunk's DMA, as the wait counts assume.
+  constexpr int WLAST = MID ? NQ - kGuPF : NQ;
+  constexpr bool kSpread = WLAST >= 5;
+  constexpr int WP0 = 1, WS = kSpread ? (WLAST - 2) / 4 : 0;
+  static_assert(!kSpread || WP0 + 3 * WS < WLAST, "weight loads before the chunk's wait");
   bf16x8 fa[RF];
   if (MID) {
 #pragma unroll
@@ -445,10 +463,12 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           nslot -= nslot >= NB ? NB : 0;
           dma_chunk<MS>(rx, doff, kb_of(c + DA), lds + nslot * kBuf);
         }
+        const int sn = sc0 + d + DB - 1;  // the superchunk an even chunk requests
         if (h == 0) {
-          const int sn = sc0 + d + DB - 1;
-          load_bcodes(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc);
-          load_bcodes(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc);
+          if constexpr (!kSpread) {
+            load_bcodes(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc);
+            load_bcodes(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc);
+          }
           load_bscales(rg[(d + DB - 1) % DB], tg, sn, nsc);
           load_bscales(ru[(d + DB - 1) % DB], tu, sn, nsc);
         }
@@ -469,11 +489,17 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           const int j = i + kGuPF;
           if (MID && j == NQ) {
             // chunk c + 1 must be in LDS for every wave before its first read
-            if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0)>();
-            else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();
+            if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0), false>();
+            else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1), false>();
           }
           if (j < NQ) fa[(q0 + j) % RF] = lds_frag_sw(A, j % MT, nl, 4 * g + j / MT);
           else if (MID) fa[(q0 + j) % RF] = lds_frag_sw(An, (j - NQ) % MT, nl, 4 * g + (j - NQ) / MT);
+          if (kSpread && h == 0) {
+            if (i == WP0) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc, 0);
+            if (i == WP0 + WS) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc, 1);
+            if (i == WP0 + 2 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc, 0);
+            if (i == WP0 + 3 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc, 1);
+          }
           if (m == 0 && st > 0) {
             bg = decode8(rg[d].q[h][st], sgv);
             bu = decode8(ru[d].q[h][st], suv);
@@ -485,8 +511,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
         }
         if (!MID) {
           // chunk c + 1 must be in LDS for every wave before anyone reads it
-          if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0)>();
-          else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();
+          if (h == 0) wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 0), false>();
+          else wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1), false>();
         }
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
@@ -713,8 +739,8 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[i % RF], b1, acc[m][1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == 0) wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 0)>();
-        else wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1)>();
+        if (h == 0) wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 0), false>();
+        else wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1), false>();
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
