@@ -600,15 +600,18 @@ constexpr int dn_pf(int mt) { return mt >= 7 ? 1 : 2; }
 // workgroup-uniform part (tile and superchunk) is a scalar offset, used only
 // when the superchunk is real (ok, uniform): otherwise the vector offset is
 // out of range and the scalar offset 0.
-__device__ __forceinline__ void load_bsuper_direct(BSuper& b, rsrc_t rc, rsrc_t rs, uint32_t vcode, uint32_t vscale,
-                                                   uint32_t scode, uint32_t sscale, bool ok) {
+// Part 0 and 1: code blocks g and g + 4; part 2: the 8 scale bytes.
+__device__ __forceinline__ void load_bsuper_part(BSuper& b, rsrc_t rc, rsrc_t rs, uint32_t vcode, uint32_t vscale,
+                                                 uint32_t scode, uint32_t sscale, bool ok, int part) {
   const uint32_t vc = ok ? vcode : kOOB, vs = ok ? vscale : kOOB;
   const uint32_t sc_ = ok ? scode : 0u, ss_ = ok ? sscale : 0u;
-  b.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc, sc_, 0);
-  b.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 64u, sc_, 0);
-  const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(rs, vs, ss_, 0);
-  b.s[0] = sv[0];
-  b.s[1] = sv[1];
+  if (part < 2) {
+    b.q[part] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 64u * (uint32_t)part, sc_, 0);
+  } else {
+    const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(rs, vs, ss_, 0);
+    b.s[0] = sv[0];
+    b.s[1] = sv[1];
+  }
 }
 
 // Activation ring (DMA, both terms of a chunk per buffer): 5 buffers up to 2
@@ -658,14 +661,25 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
     vcode[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)(nbk * 16) + 16u * g;
     vscale[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)nbk;
   }
-  auto load_b = [&](BSuper (&b)[2], int G) {
+  // load k (0..5) of superchunk G: n-tile k / 3, part k % 3
+  auto load_b_part = [&](BSuper (&b)[2], int G, int k) {
     const int t = G / nscp, sc = G - t * nscp;
     const bool ok = G < gend && sc < nsc;
     const uint32_t scode = (uint32_t)t * (uint32_t)(kDN_NT * nbk * 16) + (uint32_t)sc * 128u;
     const uint32_t sscale = (uint32_t)t * (uint32_t)(kDN_NT * nbk) + (uint32_t)sc * 8u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_bsuper_direct(b[j], rc, rs, vcode[j], vscale[j], scode, sscale, ok);
+    load_bsuper_part(b[k / 3], rc, rs, vcode[k / 3], vscale[k / 3], scode, sscale, ok, k % 3);
   };
+  auto load_b = [&](BSuper (&b)[2], int G) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) load_b_part(b, G, k);
+  };
+  // As in gate/up, an even chunk's six weight loads go one at a time between
+  // its multiplies (pairs 1 + k WS, all before the chunk's closing wait) when
+  // it has enough pairs, else up front; they always follow the chunk's DMA.
+  constexpr int kDnNQ = 4 * MT;
+  constexpr bool kDnSpread = kDnNQ >= 8;
+  constexpr int kDnWS = kDnSpread ? (kDnNQ - 2) / 6 : 0;
+  static_assert(!kDnSpread || 1 + 5 * kDnWS < kDnNQ, "weight loads before the chunk's wait");
   // activations of global chunk q (chunk q % (2 nscp) of its tile; past K or
   // past the last tile: zeros), both terms, into buffer `buf`
   uint32_t doff[MS / 2];
@@ -703,7 +717,7 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           nslot -= nslot >= NB ? NB : 0;
           dma_q(q + DA, lds + nslot * kBuf);
         }
-        if (h == 0) load_b(rb[(d + DB - 1) % DB], G0 + d + DB - 1);
+        if (!kDnSpread && h == 0) load_b(rb[(d + DB - 1) % DB], G0 + d + DB - 1);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint8_t* Ah = lds + slot * kBuf;
         const uint8_t* Al = Ah + kTerm;
@@ -727,6 +741,11 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
             const int j = i + kDnPF;
             fh[j % RF] = lds_frag_sw(Ah, j % MT, nl, 4 * g + j / MT);
             fl[j % RF] = lds_frag_sw(Al, j % MT, nl, 4 * g + j / MT);
+          }
+          if (kDnSpread && h == 0) {
+#pragma unroll
+            for (int k = 0; k < 6; ++k)
+              if (i == 1 + k * kDnWS) load_b_part(rb[(d + DB - 1) % DB], G0 + d + DB - 1, k);
           }
           if (m == 0 && st > 0) {
             b0 = decode8(rb[d][0].q[h][st], s0v);
