@@ -268,12 +268,14 @@ def bench_batch(a):
     # routes of each rotating batch
     P = T * k
     mb = moe.max_expert_blocks(E, P)
+    nsw = moe.sort_workspace_bytes(E, T, k)
+    sort_ws = torch.empty(nsw, dtype=torch.uint8, device=dev) if nsw else None
     stage = []
     for b in range(nbatch):
         step(b)
         offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
         pairs = torch.empty(P, dtype=torch.int32, device=dev)
-        moe.moe_sort_by_expert(idx, E, offs, pairs)
+        moe.moe_sort_by_expert(idx, E, offs, pairs, sort_ws)
         blocks = torch.empty(mb, 4, dtype=torch.int32, device=dev)
         nb = torch.empty(1, dtype=torch.int32, device=dev)
         moe.moe_expert_blocks(offs, P, blocks, nb)
