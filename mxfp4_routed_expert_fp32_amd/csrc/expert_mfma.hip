@@ -946,15 +946,20 @@ __device__ __forceinline__ void router_block(rsrc_t rx, rsrc_t rw, const float* 
 // Workgroup b: split = b % nsplit, expert tile (b / nsplit) % ntiles, token
 // tile b / (nsplit * ntiles).  nsplit == 1: every slice, logits out (with
 // bias); otherwise slice `split` only, its partial sums to part[split][t][e].
+// xcd_major (nsplit == 1, at most 8 expert tiles): workgroup b runs on XCD
+// b % 8 and takes expert tile b % 8 (none past the last) and token tile b / 8,
+// so the workgroups of one XCD stream the same router rows through its L2.
 __global__ __launch_bounds__(kThr, 1) void k_router_mfma(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ wr,
                                                         const float* __restrict__ bias, int T, int H, int E,
-                                                        int ntiles, int nsplit, float* __restrict__ part,
-                                                        float* __restrict__ logits) {
+                                                        int ntiles, int nsplit, int xcd_major,
+                                                        float* __restrict__ part, float* __restrict__ logits) {
   extern __shared__ uint16_t a_lds[];  // [2][kMB][kLdsRow]
   __shared__ uint32_t row_base[kMB];
-  const int split = blockIdx.x % nsplit, r = blockIdx.x / nsplit;
-  const int nt = r % ntiles, mt = r / ntiles;
+  const int split = xcd_major ? 0 : blockIdx.x % nsplit, r = blockIdx.x / nsplit;
+  const int nt = xcd_major ? (int)(blockIdx.x % 8) : r % ntiles;
+  const int mt = xcd_major ? (int)(blockIdx.x / 8) : r / ntiles;
+  if (nt >= ntiles) return;
   const int t0 = mt * kMB;
   const int cnt = min(kMB, T - t0);
   for (int i = threadIdx.x; i < kMB; i += kThr) row_base[i] = i < cnt ? (uint32_t)(t0 + i) * (uint32_t)(H * 2) : kFar;
@@ -1055,8 +1060,10 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* b
   for (int t0 = 0; t0 < T; t0 += tb) {
     const int n = std::min(tb, T - t0);
     const int mtiles = (n + kMB - 1) / kMB;
-    k_router_mfma<<<dim3((unsigned)(mtiles * ntiles * nsplit)), kThr, lds, s>>>(
-        x + (size_t)t0 * H, wr, bias, n, H, E, ntiles, nsplit, part, logits + (size_t)t0 * E);
+    const int xcd_major = nsplit == 1 && ntiles <= 8 ? 1 : 0;
+    const unsigned grid = xcd_major ? (unsigned)(8 * mtiles) : (unsigned)(mtiles * ntiles * nsplit);
+    k_router_mfma<<<dim3(grid), kThr, lds, s>>>(x + (size_t)t0 * H, wr, bias, n, H, E, ntiles, nsplit, xcd_major,
+                                                part, logits + (size_t)t0 * E);
     if (nsplit > 1) {
       const size_t cells = (size_t)n * E;
       k_router_reduce<<<dim3((unsigned)((cells + 255) / 256)), 256, 0, s>>>(part, nsplit, n, E, bias,
