@@ -241,7 +241,9 @@ def test_forward_tiny_matches_oracle(seed):
                                            (160, 1024, 5, 2, 1, "f32"), (96, 2048, 6, 3, 3, "f32"),
                                            (64, 3072, 4, 2, 2, "f32"), (1056, 1536, 9, 4, 1, "bf16"),
                                            # decode-form GEMVs at other widths (bf16 x, one token or I % 128 != 0)
-                                           (4096, 96, 5, 2, 3, "bf16"), (2048, 64, 4, 2, 1, "bf16")])
+                                           (4096, 96, 5, 2, 3, "bf16"), (2048, 64, 4, 2, 1, "bf16"),
+                                           # fp32 x: K halves across wave pairs, model width and an odd block count
+                                           (7168, 1536, 20, 16, 2, "f32"), (1056, 160, 9, 4, 3, "f32")])
 def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
     w = synth.Workload("s", 60, T, H, I, E, k, xd, weight_seed=7100 + H + E)
     c, s, ex = experts_host(w)
