@@ -187,10 +187,21 @@ int moe_router_logits(const moe_layer_desc* desc, const void* x, int32_t x_dtype
 int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                      int32_t* idx, float* w, void* stream);
 
-/* Token -> expert sort alone: stable counting sort of the (token, rank) pairs by expert.
- *   expert_offsets [E+1]: pairs of expert e are pair_list[offsets[e] .. offsets[e+1])
- *   pair_list [n_tokens*k]: pair id t*k + j, ordered by expert, then token
- * The workspace must hold moe_sort_workspace_bytes(E, n_tokens, k) bytes. */
+/* Token -> expert sort alone: stable counting sort of the (token, rank) pairs by expert
+ * (the grouping the grouped expert GEMMs need; the pages do not describe it).
+ *   topk_idx [n_tokens][k] int32: expert ids in [0, E) (an id outside is clamped into it)
+ *   expert_offsets [E+1] int32: pairs of expert e are pair_list[offsets[e] .. offsets[e+1])
+ *   pair_list [n_tokens*k] int32: pair id t*k + j, ordered by expert, then token, then rank
+ *   workspace: device scratch of at least moe_sort_workspace_bytes(E, n_tokens, k)
+ *     bytes, 16-byte aligned, owned by the caller and overwritten by the call.  The
+ *     size is 0 below 1024 tokens (one workgroup sorts everything; workspace may then
+ *     be NULL); from 1024 tokens the pairs are counted in blocks of 256 tokens and the
+ *     workspace holds (blocks + 1) * E int32 counts.
+ * Errors: MOE_ERR_NULL (idx, offsets or pair list NULL), MOE_ERR_SHAPE (n_tokens,
+ * E or k out of range), MOE_ERR_UNSUPPORTED (E above 4096), MOE_ERR_OVERFLOW
+ * (n_tokens * k above INT32_MAX), MOE_ERR_WORKSPACE (workspace NULL or too small
+ * when the size is not 0), MOE_ERR_ALIGN (workspace not 16-byte aligned),
+ * MOE_ERR_DEVICE. */
 int moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, size_t* bytes);
 int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_experts, int32_t k,
                        int32_t* expert_offsets, int32_t* pair_list, void* workspace,
