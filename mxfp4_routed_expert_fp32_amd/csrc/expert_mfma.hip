@@ -910,13 +910,18 @@ __device__ __forceinline__ void router_block(rsrc_t rx, rsrc_t rw, const float* 
       for (int st = 0; st < 4; ++st) {
         bf16x8 b0, b1, b2;
         split3(wq[d].q[2 * st], wq[d].q[2 * st + 1], b0, b1, b2);
+        // every m-tile's fragment is requested first, then the three terms go
+        // term by term over the m-tiles, so consecutive multiplies are
+        // independent; each accumulator still takes w0, w1, w2 in that order
+        bf16x8 af[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const bf16x8 af = lds_frag(A, m * 16 + nl, 32 * g + 8 * st);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b2, acc[m], 0, 0, 0);
-        }
+        for (int m = 0; m < MT; ++m) af[m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * st);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b0, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b1, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b2, acc[m], 0, 0, 0);
       }
       if (d % kRtSlice == kRtSlice - 1) {  // end of a slice: fold it into the running sum
         if (c / kRtSlice < last_slice) {
