@@ -119,6 +119,31 @@ def hold_queue(seconds):
     torch.cuda._sleep(int(seconds * 2.4e9))
 
 
+def hold_for(n, enqueue_s, kernel_s):
+    """Hold the queue just long enough that the host, enqueuing n launches at
+    enqueue_s each, stays ahead of the GPU running them at kernel_s each (both
+    measured on the warm-up launches), plus 0.5 ms.  A long hold is
+    measurably wrong: after a 40 ms spin of one wave, 32-us GEMV launches ran
+    about 7% slower than the same launches back to back (the clock ramps back
+    up), and a 6 ms spin still cost about 4%."""
+    hold_queue(min(1.5 * n * max(0.0, enqueue_s - kernel_s) + 0.5e-3, 0.02))
+
+
+def warm(launch, n):
+    """Runs n warm-up launches; returns (host seconds per enqueue, GPU seconds per launch)."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    t0 = time.perf_counter()
+    for i in range(n):
+        launch(i)
+    host = (time.perf_counter() - t0) / n
+    e1.record()
+    torch.cuda.synchronize()
+    return host, e0.elapsed_time(e1) * 1e-3 / n
+
+
 def timed(step, n, warmup):
     import torch
     for i in range(warmup):
@@ -177,11 +202,11 @@ def bench_decode(a):
     # dominant kernel: gate/up + SwiGLU GEMV, timed over back-to-back launches on the
     # stream it runs on, with the same routes and tokens as the steps above
     hbuf = torch.empty(k, I, dtype=torch.float32, device=dev)
-    for i in range(a.warmup):
-        moe.moe_mxfp4_gate_up(desc, pool[i % a.pool:i % a.pool + 1], routes[i % a.pool], k, codes, scales, hbuf)
-    torch.cuda.synchronize()
+    enqueue_s, kernel_s = warm(
+        lambda i: moe.moe_mxfp4_gate_up(desc, pool[i % a.pool:i % a.pool + 1], routes[i % a.pool], k, codes,
+                                        scales, hbuf), max(1, a.warmup))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_queue(a.steps * 100e-6)
+    hold_for(a.steps, enqueue_s, kernel_s)
     e0.record()
     for i in range(a.steps):
         j = (a.warmup + i) % a.pool
@@ -286,12 +311,10 @@ def bench_batch(a):
         j = i % nbatch
         moe.moe_mxfp4_grouped_gate_up(desc, xs[j], k, stage[j][0], stage[j][1], stage[j][2], codes, scales, hterm)
 
-    for i in range(max(2, a.warmup)):
-        gate_up(i)
-    torch.cuda.synchronize()
+    enqueue_s, kernel_s = warm(gate_up, max(2, a.warmup))
     nl = max(a.steps, 2 * nbatch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_queue(nl * 100e-6)
+    hold_for(nl, enqueue_s, kernel_s)
     e0.record()
     for i in range(nl):
         gate_up(i)
