@@ -218,20 +218,21 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   int e;
   if constexpr (SEL > 0) {
     __shared__ uint64_t cand[kWave];
-    __shared__ uint32_t ncand;
     __shared__ uint32_t sel_e[kWave];
     __shared__ int32_t chosen;
-    for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
+    // wave 0 selects at once; the other waves stage the activations meanwhile
     if (wid == 0) {
       const int t = p / k;
       int sel;
       float wv;
-      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &ncand, sel_e, &sel, &wv);
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, sel_e, &sel, &wv);
       if (lane == p % k) chosen = sel;
       if (part == 0 && p % k == 0 && lane < k) {
         route[(size_t)t * k + lane] = sel;
         wsel[(size_t)t * k + lane] = wv;
       }
+    } else {
+      for (int c = threadIdx.x - kWave; c < xbytes / 16; c += 256 - kWave) xs_lds[c] = xg[c];
     }
     __syncthreads();
     e = __builtin_amdgcn_readfirstlane(chosen);

@@ -209,14 +209,13 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
                                                       int k, int32_t* __restrict__ idx,
                                                       float* __restrict__ wout) {
   __shared__ uint64_t cand[4][kWave];
-  __shared__ uint32_t ncand[4];
   __shared__ uint32_t sel_e[4][kWave];
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   int sel;
   float wsel;
-  topk_wave<MAXV>(logits + (size_t)t * E, E, k, cand[wid], &ncand[wid], sel_e[wid], &sel, &wsel);
+  topk_wave<MAXV>(logits + (size_t)t * E, E, k, cand[wid], sel_e[wid], &sel, &wsel);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
     wout[(size_t)t * k + lane] = wsel;

@@ -73,12 +73,12 @@ __device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf) {
 // lane and each one's rank among them is its place in the route.  When more
 // than 64 keys are >= L (heavy skew inside a few lanes) the wave falls back to
 // k rounds of "take the largest remaining key".  Both give the unique order
-// defined by rank_key.  cand, ncand and sel_e are this wave's LDS scratch.
+// defined by rank_key.  cand and sel_e are this wave's LDS scratch.
 // On return lane j < k holds the expert of rank j in *sel and its softmax
 // weight in *wsel (lanes >= k: expert 0, weight 0).
 template <int MAXV>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, uint64_t* cand,
-                                          uint32_t* ncand, uint32_t* sel_e, int* sel_out, float* w_out) {
+                                          uint32_t* sel_e, int* sel_out, float* w_out) {
   const int lane = threadIdx.x % kWave;
   float lv[MAXV];
 #pragma unroll
@@ -104,31 +104,26 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(lmax >> 32), src);
     L = ((uint64_t)hi << 32) | lo;
   }
-  // candidates: keys >= L
-  int mine = 0;
+  // candidates: keys >= L, compacted into cand[] in (slot, lane) order: one
+  // ballot per slot gives each candidate its position (no atomics)
+  uint32_t total = 0;  // the same in every lane
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) mine += (key[v] != 0ull && key[v] >= L) ? 1 : 0;
-  int total = mine;
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) total += __shfl_xor(total, m, kWave);
+  for (int v = 0; v < MAXV; ++v) {
+    const bool c = key[v] != 0ull && key[v] >= L;
+    const uint64_t b = __builtin_amdgcn_ballot_w64(c);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+    if (c && total + below < (uint32_t)kWave) cand[total + below] = key[v];
+    total += (uint32_t)__builtin_popcountll(b);
+  }
 
   int my_rank = kWave;          // rank of this lane's entry (>= k: not selected)
   uint32_t my_e = 0;
-  if (total <= kWave) {
-    if (lane == 0) *ncand = 0;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-      if (key[v] != 0ull && key[v] >= L) {
-        const uint32_t pos = atomicAdd(ncand, 1u);
-        cand[pos] = key[v];
-      }
-    }
+  if (total <= (uint32_t)kWave) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const uint64_t c = (lane < total) ? cand[lane] : 0ull;
+    const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
     const int r = rank_in_wave_lds(c, cand);
-    if (lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
+    if ((uint32_t)lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
   } else {
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
