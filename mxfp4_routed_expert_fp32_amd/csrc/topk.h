@@ -47,16 +47,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // Number of lanes whose 64-bit key is larger than this lane's (keys unique),
 // through a 64-entry LDS buffer of the wave: every lane writes its key, then
-// reads all 64 back two at a time (the same address in every lane, a
-// broadcast).  The buffer is free again when the function returns.
-__device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf) {
+// reads the first n back two at a time (the same address in every lane, a
+// broadcast).  Keys of lanes n and above must be 0 (they never count).  The
+// buffer is free again when the function returns.
+__device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf, int n = kWave) {
   const int lane = threadIdx.x % kWave;
   buf[lane] = v;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   int r = 0;
-#pragma unroll
-  for (int j = 0; j < kWave; j += 2) {
+  for (int j = 0; j < n; j += 2) {
     const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
     r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
   }
@@ -122,7 +122,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
-    const int r = rank_in_wave_lds(c, cand);
+    const int r = rank_in_wave_lds(c, cand, (int)total);  // candidates only (usually about k)
     if ((uint32_t)lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
   } else {
     for (int j = 0; j < k; ++j) {
