@@ -378,7 +378,8 @@ def test_prefill_token_batches_equal_separate_calls():
     P.assert_out_close(out[rows], r_out)
 
 
-@pytest.mark.parametrize("H,I,E,k,T", [(512, 256, 16, 4, 3), (256, 128, 100, 3, 5), (1024, 256, 8, 2, 1)])
+@pytest.mark.parametrize("H,I,E,k,T", [(512, 256, 16, 4, 3), (256, 128, 100, 3, 5), (1024, 256, 8, 2, 1),
+                                       (512, 256, 33, 4, 2)])  # E not a multiple of the router's experts per workgroup
 def test_stack_small_matches_oracle_layer_by_layer(H, I, E, k, T):
     """The layer stack (RMSNorm inside each layer's router kernel, fp32
     residual stream) on small shapes: two layers against the oracle layer by
