@@ -435,12 +435,12 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
 // out[t][n] = (resid[t][n] +) sum_j w[t][j] * y[t*k+j][n], j ascending; resid
 // may alias out.  Loads are issued in groups of 16 ranks (one group for the
 // usual k <= 16), so a thread waits for memory once per group.
-__global__ __launch_bounds__(64) void k_combine(const float* __restrict__ ybuf,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ybuf,
                                                 const float* __restrict__ w, int T, int k, int H,
                                                 const float* resid, float* out) {
   constexpr int G = 16;
   const size_t n4 = (size_t)T * H / 4;
-  for (size_t q = (size_t)blockIdx.x * 64 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 64) {
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 256) {
     const size_t flat = 4 * q;
     const int t = (int)(flat / H);
     const int n = (int)(flat % H);
@@ -604,9 +604,11 @@ hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P
 hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,
                           float* out, hipStream_t s) {
   const size_t n4 = (size_t)T * H / 4;
-  size_t blocks = (n4 + 63) / 64;
-  if (blocks > 4096) blocks = 4096;
-  k_combine<<<dim3((unsigned)blocks), 64, 0, s>>>(ybuf, w, T, k, H, resid, out);
+  // one float4 column per thread (measured faster than capping the grid and
+  // striding); the cap only bounds the grid for very many tokens
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > (1u << 20)) blocks = 1u << 20;
+  k_combine<<<dim3((unsigned)blocks), 256, 0, s>>>(ybuf, w, T, k, H, resid, out);
   return hipGetLastError();
 }
 
