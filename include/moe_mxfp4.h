@@ -130,7 +130,7 @@ int moe_mxfp4_pack(const moe_layer_desc* desc, const void* logical_codes, const 
  *   router_w     [E][H] fp32 row-major
  *   router_bias  [E] fp32 or NULL; added to the logits (moves selection and weights)
  *   packed_codes / packed_scales: the layer's device weights (moe_mxfp4_packed_bytes)
- *   n_tokens >= 1; 1 <= k <= desc->top_k_max
+ *   1 <= n_tokens <= 2^20 (MOE_ERR_SHAPE otherwise); 1 <= k <= desc->top_k_max
  *   out          [n_tokens][H] fp32
  *   logits_out   [n_tokens][E] fp32, or NULL
  *   topk_idx_out [n_tokens][k] int32 in rank order (descending logit, ties to the

@@ -98,6 +98,7 @@ def test_forward_rejects_before_launch():
     assert call_forward(d, wr=None) == -1
     assert call_forward(d, dtype=5) == -3
     assert call_forward(d, T=0) == -2
+    assert call_forward(d, T=(1 << 20) + 1) == -2   # above the largest token count
     assert call_forward(d, k=0) == -2
     assert call_forward(d, k=17) == -2
     assert call_forward(d, x=8) == -4

@@ -243,7 +243,13 @@ def test_forward_tiny_matches_oracle(seed):
                                            # decode-form GEMVs at other widths (bf16 x, one token or I % 128 != 0)
                                            (4096, 96, 5, 2, 3, "bf16"), (2048, 64, 4, 2, 1, "bf16"),
                                            # fp32 x: K halves across wave pairs, model width and an odd block count
-                                           (7168, 1536, 20, 16, 2, "f32"), (1056, 160, 9, 4, 3, "f32")])
+                                           (7168, 1536, 20, 16, 2, "f32"), (1056, 160, 9, 4, 3, "f32"),
+                                           # descriptor limits on the decode form: H = I = 8192 (the
+                                           # widest gate/up and down GEMVs); E above 1024 with the largest
+                                           # k (the selection's 64-slot form inside the gate/up kernel,
+                                           # combine over four groups of 16 ranks)
+                                           (8192, 8192, 2, 2, 1, "bf16"), (256, 128, 4096, 64, 2, "bf16"),
+                                           (96, 64, 1500, 64, 1, "f32")])
 def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
     w = synth.Workload("s", 60, T, H, I, E, k, xd, weight_seed=7100 + H + E)
     c, s, ex = experts_host(w)
@@ -371,6 +377,27 @@ def test_prefill_token_batches_equal_separate_calls():
     assert np.array_equal(idx, np.concatenate([i1, i2]))
     assert np.array_equal(out.view(np.uint32), np.concatenate([o1, o2]).view(np.uint32))
     rows = np.r_[0, 1, T1 - 1, T1, T1 + 1, T - 1, np.random.default_rng(3).integers(0, T, 12)]
+    xf = synth.tokens_f32(w, rows)
+    r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, None, logits[rows])
+    assert np.array_equal(idx[rows], r_idx)
+    P.assert_weights_close(wt[rows], r_w, k)
+    P.assert_out_close(out[rows], r_out)
+
+
+def test_forward_max_tokens_sampled():
+    """The largest token count a call accepts (2^20) on the prefill form,
+    which runs it as several token batches; sampled tokens, including both
+    ends, are checked against the oracle."""
+    H, I, E, k = 256, 256, 16, 4
+    T = 1 << 20
+    w = synth.Workload("maxT", 68, T, H, I, E, k, "bf16", weight_seed=7950)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    wr = sd.router_w(w)
+    out, logits, idx, wt = run_forward(desc, w, x, wr, None, codes, scales, k)
+    del x
+    rows = np.r_[0, 1, T // 2, T - 2, T - 1, np.random.default_rng(5).integers(0, T, 11)]
     xf = synth.tokens_f32(w, rows)
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, None, logits[rows])
     assert np.array_equal(idx[rows], r_idx)
