@@ -406,7 +406,8 @@ def test_forward_max_tokens_sampled():
 
 
 @pytest.mark.parametrize("H,I,E,k,T", [(512, 256, 16, 4, 3), (256, 128, 100, 3, 5), (1024, 256, 8, 2, 1),
-                                       (512, 256, 33, 4, 2)])  # E not a multiple of the router's experts per workgroup
+                                       (512, 256, 33, 4, 2),  # E not a multiple of the router's experts per workgroup
+                                       (256, 128, 2048, 32, 2)])  # the 64-slot selection on fp32 activations
 def test_stack_small_matches_oracle_layer_by_layer(H, I, E, k, T):
     """The layer stack (RMSNorm inside each layer's router kernel, fp32
     residual stream) on small shapes: two layers against the oracle layer by
