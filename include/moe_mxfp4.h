@@ -166,6 +166,14 @@ int moe_mxfp4_experts(const moe_layer_desc* desc, const void* x, int32_t x_dtype
  * down:    y [n_pairs][H] fp32, y[p][n] = Wd[n] . h[p].
  * combine: out[t][n] = (resid[t][n] +) sum_{j<k} w[t][j] * y[t*k+j][n], j ascending;
  *     resid may be NULL or alias out.
+ * x has ceil(n_pairs / k) rows.  An expert id outside [0, E) is clamped into
+ * it on the device.  Errors, all found before anything is enqueued:
+ * MOE_ERR_NULL (a required pointer is NULL), MOE_ERR_DTYPE (x_dtype),
+ * MOE_ERR_SHAPE (n_pairs below 1 or above 2^26; n_tokens below 1 or above
+ * 2^20; k outside [1, top_k_max] for gate/up or [1, 64] for combine; hidden not
+ * a positive multiple of 4), MOE_ERR_ALIGN (x, h, y, out, resid or the packed
+ * buffers not 16-byte aligned; combine's w needs none), the descriptor's own
+ * errors (moe_layer_check), and MOE_ERR_DEVICE when a launch fails.
  */
 int moe_mxfp4_gate_up(const moe_layer_desc* desc, const void* x, int32_t x_dtype,
                       const int32_t* pair_expert, int32_t n_pairs, int32_t k, const void* packed_codes,
@@ -176,14 +184,19 @@ int moe_mxfp4_down(const moe_layer_desc* desc, const float* h, const int32_t* pa
 int moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden,
                 const float* resid, float* out, void* stream);
 
-/* Router logits alone: logits [n_tokens][E] = x . router_w^T (+ bias), fp32 accumulation. */
+/* Router logits alone: logits [n_tokens][E] = x . router_w^T (+ bias), fp32 accumulation.
+ * x [n_tokens][H] (x_dtype), router_w [E][H] fp32 row-major, router_bias [E] or NULL.
+ * Errors: MOE_ERR_NULL, MOE_ERR_DTYPE, MOE_ERR_SHAPE (n_tokens outside [1, 2^20]),
+ * MOE_ERR_ALIGN (x or router_w not 16-byte aligned), descriptor errors,
+ * MOE_ERR_DEVICE. */
 int moe_router_logits(const moe_layer_desc* desc, const void* x, int32_t x_dtype,
                       const float* router_w, const float* router_bias, int32_t n_tokens,
                       float* logits, void* stream);
 
 /* Top-k + softmax alone, from given logits [n_tokens][n_experts]: idx [n_tokens][k] in
  * rank order and softmax weights w [n_tokens][k].  1 <= k <= min(E, 64),
- * E <= 4096. */
+ * E <= 4096.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n_tokens outside [1, 2^20],
+ * E below 1, k out of range), MOE_ERR_UNSUPPORTED (E above 4096), MOE_ERR_DEVICE. */
 int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                      int32_t* idx, float* w, void* stream);
 
@@ -243,16 +256,21 @@ int moe_mxfp4_grouped_down(const moe_layer_desc* desc, const void* hterm, int32_
 /* Dequantisation alone: dequantise one matrix of one expert from the device layout to
  * fp32, exactly: out = E2M1(code) * 2^(scale - 127), subnormals kept, +-inf on
  * overflow, scale byte 0xFF -> NaN 0x7FC00000.  matrix 0 = gate [I][H],
- * 1 = up [I][H], 2 = down [H][I]. */
+ * 1 = up [I][H], 2 = down [H][I].  out holds rows x cols fp32.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_RANGE (expert outside [0, E) or matrix outside 0..2), MOE_ERR_ALIGN (a buffer
+ * not 16-byte aligned), descriptor errors, MOE_ERR_DEVICE. */
 int moe_mxfp4_dequant(const moe_layer_desc* desc, const void* packed_codes, const void* packed_scales,
                       int64_t expert, int32_t matrix, float* out, void* stream);
 
 /* RMSNorm with gain, n = r / sqrt(mean(r^2) + eps) * gamma, per token.
- * r, n: [n_tokens][hidden] fp32; gamma [hidden] fp32; hidden % 4 == 0. */
+ * r, n: [n_tokens][hidden] fp32; gamma [hidden] fp32; hidden % 4 == 0.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (n_tokens outside [1, 2^20], hidden not a positive
+ * multiple of 4), MOE_ERR_ALIGN (r, gamma or n_out not 16-byte aligned), MOE_ERR_DEVICE. */
 int moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden,
                 float* n_out, void* stream);
 
-/* Residual add: r[i] += d[i] for i < n (fp32). */
+/* Residual add: r[i] += d[i] for i < n (fp32); n = 0 enqueues nothing.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (n negative), MOE_ERR_DEVICE. */
 int moe_residual_add(float* r, const float* d, int64_t n, void* stream);
 
 /*
