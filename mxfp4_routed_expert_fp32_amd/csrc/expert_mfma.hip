@@ -838,7 +838,11 @@ constexpr int kRT_NT = 128;
 constexpr int kRtSlice = 2;          // chunks per slice
 constexpr int kRtSplitTokens = 256;  // slices run in workgroups of their own up to this many tokens
 
-// This lane's 32 weights of one chunk: K = 32g .. 32g+31 of the chunk.
+// This lane's 32 weights of one chunk: for each 32-wide step st, K = 32 st +
+// 8g .. 32 st + 8g + 7 (q[2 st], q[2 st + 1]).  One load instruction then
+// takes 16-byte pieces 32 bytes apart from each row, so the four lane groups
+// of a row fall in one 128-byte line (and the next instruction fills it)
+// instead of four lines; the A fragments are read at the same K.
 struct WChunk {
   u32x4 q[8];
 };
@@ -847,7 +851,8 @@ __device__ __forceinline__ void load_wchunk(WChunk& w, rsrc_t rw, uint32_t woff,
   const bool ok = c < c_end;
 #pragma unroll
   for (int v = 0; v < 8; ++v)
-    w.q[v] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? woff + (uint32_t)c * 512u + 16u * v : kOOB, 0, 0);
+    w.q[v] = __builtin_amdgcn_raw_buffer_load_b128(
+        rw, ok ? woff + (uint32_t)c * 512u + 128u * (uint32_t)(v >> 1) + 16u * (uint32_t)(v & 1) : kOOB, 0, 0);
 }
 
 // Three bf16 terms of 8 fp32 weights (two packed quads), hardware round to
@@ -879,7 +884,7 @@ __device__ __forceinline__ void router_block(rsrc_t rx, rsrc_t rw, const float* 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int ex = nt * kRT_NT + wid * 16 + nl;
-  const uint32_t woff = ex < E ? (uint32_t)ex * (uint32_t)(H * 4) + 128u * g : kOOB;
+  const uint32_t woff = ex < E ? (uint32_t)ex * (uint32_t)(H * 4) + 32u * g : kOOB;
   const int last_slice = (c_end + kRtSlice - 1) / kRtSlice;  // slices below this index are real
   uint16_t* buf0 = lds;
   uint16_t* buf1 = lds + kTile;
@@ -915,7 +920,7 @@ __device__ __forceinline__ void router_block(rsrc_t rx, rsrc_t rw, const float* 
         // independent; each accumulator still takes w0, w1, w2 in that order
         bf16x8 af[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) af[m] = lds_frag(A, m * 16 + nl, 32 * g + 8 * st);
+        for (int m = 0; m < MT; ++m) af[m] = lds_frag(A, m * 16 + nl, 32 * st + 8 * g);
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b0, acc[m], 0, 0, 0);
 #pragma unroll
