@@ -981,16 +981,24 @@ __global__ __launch_bounds__(kThr, 1) void k_router_mfma(const uint16_t* __restr
   const int c_begin = whole ? 0 : split * kRtSlice;
   const int c_end = whole ? nchunks : min(nchunks, c_begin + kRtSlice);
   float* out = whole ? logits : part + (size_t)split * T * E;
+  // a workgroup of one slice (two chunks) keeps a two-chunk weight ring, so
+  // it runs no chunk past its slice; the bits do not depend on the ring
+#define MOE_RB_SMALL(M)                                                                                    \
+  if (whole)                                                                                               \
+    router_block<M, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out);      \
+  else                                                                                                     \
+    router_block<M, kRtSlice>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out);
   switch ((cnt + 15) / 16) {
-    case 1: router_block<1, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
-    case 2: router_block<2, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
-    case 3: router_block<3, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
-    case 4: router_block<4, 4>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
+    case 1: MOE_RB_SMALL(1) break;
+    case 2: MOE_RB_SMALL(2) break;
+    case 3: MOE_RB_SMALL(3) break;
+    case 4: MOE_RB_SMALL(4) break;
     case 5: router_block<5, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
     case 6: router_block<6, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
     case 7: router_block<7, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
     default: router_block<8, 2>(rx, rw, bias, whole, H, E, nt, c_begin, c_end, t0, cnt, row_base, a_lds, out); break;
   }
+#undef MOE_RB_SMALL
 }
 
 // logits[i] = (sum over splits s in order of part[s][i]) + bias: the same
