@@ -174,8 +174,13 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
     for (int64_t t0 = 0; t0 < T; t0 += tb) {
       const int n = (int)std::min<int64_t>(tb, T - t0);
       const int Pn = n * k;
-      MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s)));
-      MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
+      if (moe::sort_is_one_workgroup(n, ws + L.sortws)) {  // the sort also cuts the blocks
+        MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s, blocks,
+                                               L.max_blocks, nblocks)));
+      } else {
+        MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s)));
+        MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
+      }
       MOE_TRY(dev(moe::launch_gateup_mfma(xb + t0 * H, n, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, k,
                                           Pn, hterm, s)));
       MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, Pn, y, s)));

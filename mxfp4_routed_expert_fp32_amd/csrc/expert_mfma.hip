@@ -29,7 +29,7 @@
 
 namespace moe {
 
-constexpr int kMB = 128;       // pairs per expert block (8 m-tiles of 16)
+constexpr int kMB = kExpertBlockPairs;  // pairs per expert block (8 m-tiles of 16)
 constexpr int kKC = 128;       // K per chunk (4 blocks of 32)
 constexpr int kLdsRow = kKC + 8;  // bf16 per LDS row (16-byte pad against bank conflicts)
 

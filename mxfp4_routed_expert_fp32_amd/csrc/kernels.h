@@ -20,8 +20,15 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
 // Stable sort of the (token, rank) pairs by expert.  ws: sort_workspace_bytes(T, E)
 // bytes (may be null when that is 0; with null the one-workgroup sort runs).
 size_t sort_workspace_bytes(int T, int E);
+// Pairs per expert block of the grouped GEMMs (8 m-tiles of 16).
+constexpr int kExpertBlockPairs = 128;
+// True when launch_sort_by_expert runs as one workgroup (fewer than 1024
+// tokens, or no workspace); it can then also write the expert blocks
+// (blocks != nullptr), as launch_expert_blocks would.
+bool sort_is_one_workgroup(int T, const void* ws);
 hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* pairs,
-                                 void* ws, hipStream_t s);
+                                 void* ws, hipStream_t s, int4* blocks = nullptr, int max_blocks = 0,
+                                 int32_t* nblocks = nullptr);
 
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
                               const uint8_t* codes, const uint8_t* scales, int H, int I, int E,

@@ -329,10 +329,15 @@ __device__ void scan_experts(const int32_t* counts, int E, int32_t* __restrict__
 }
 
 // One workgroup: running[E] and mask[E] live in LDS (E <= 4096: 48 KB).
+// With blocks set it also cuts each expert's pairs into blocks of at most
+// kExpertBlockPairs, in expert order: blocks[b] = {expert, first sorted
+// index, count, 0} and *nblocks = the count written (at most max_blocks).
 __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* __restrict__ idx,
                                                                  int T, int E, int k,
                                                                  int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ pairs) {
+                                                                 int32_t* __restrict__ pairs,
+                                                                 int4* __restrict__ blocks, int max_blocks,
+                                                                 int32_t* __restrict__ nblocks) {
   extern __shared__ unsigned long long sort_lds[];
   unsigned long long* mask = sort_lds;                               // [E]
   int32_t* running = reinterpret_cast<int32_t*>(sort_lds + E);       // [E]
@@ -345,6 +350,32 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* 
   __syncthreads();
   scan_experts(running, E, offsets, running, part);  // cursors start at the offsets
   __syncthreads();
+  if (blocks) {
+    // expert e holds pairs [running[e], running[e + 1]) (the last ends at P)
+    const int per = (E + kSortThreads - 1) / kSortThreads;
+    const int e0 = tid * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+      const int32_t cnt = (e + 1 < E ? running[e + 1] : P) - running[e];
+      local += (cnt + kExpertBlockPairs - 1) / kExpertBlockPairs;
+    }
+    part[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kSortThreads; off <<= 1) {
+      const int32_t v = (tid >= off) ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int32_t b = part[tid] - local;
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+      const int32_t beg = running[e], cnt = (e + 1 < E ? running[e + 1] : P) - beg;
+      for (int32_t m0 = 0; m0 < cnt; m0 += kExpertBlockPairs, ++b)
+        if (b < max_blocks) blocks[b] = make_int4(e, beg + m0, min(kExpertBlockPairs, cnt - m0), 0);
+    }
+    if (tid == kSortThreads - 1) *nblocks = min(part[kSortThreads - 1], max_blocks);
+    __syncthreads();  // the scatter below moves the cursors
+  }
   scatter_tokens<kSortThreads>(idx, 0, T, E, k, mask, running, pairs);
 }
 
@@ -453,13 +484,17 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
   return hipGetLastError();
 }
 
+bool sort_is_one_workgroup(int T, const void* ws) { return T < kSortMultiMinTokens || ws == nullptr; }
+
 hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* pairs,
-                                 void* ws, hipStream_t s) {
+                                 void* ws, hipStream_t s, int4* blocks, int max_blocks, int32_t* nblocks) {
   const size_t lds = (size_t)E * (sizeof(unsigned long long) + sizeof(int32_t));
-  if (T < kSortMultiMinTokens || ws == nullptr) {
-    k_sort_by_expert<<<1, kSortThreads, lds, s>>>(idx, T, E, k, offsets, pairs);
+  if (sort_is_one_workgroup(T, ws)) {
+    if (blocks && !nblocks) return hipErrorInvalidValue;
+    k_sort_by_expert<<<1, kSortThreads, lds, s>>>(idx, T, E, k, offsets, pairs, blocks, max_blocks, nblocks);
     return hipGetLastError();
   }
+  if (blocks) return hipErrorInvalidValue;  // the caller runs launch_expert_blocks
   const int nblk = (T + kSortBlockTokens - 1) / kSortBlockTokens;
   int32_t* counts = static_cast<int32_t*>(ws);  // [nblk][E]
   int32_t* totals = counts + (size_t)nblk * E;  // [E]
