@@ -225,13 +225,26 @@ int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const 
     MOE_TRY(dev(moe::launch_norm_router_logits(static_cast<const float*>(x), norm_gamma, norm_eps, router_w,
                                                router_bias, T, d->hidden, d->n_experts, logits, norm_out, s)));
     x = norm_out;
-  } else {
-    float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
-    MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
   }
-  if (T > 1 && !xf && grouped_batch(d, k) > 0) {
+  const bool prefill = T > 1 && !xf && grouped_batch(d, k) > 0;
+  bool selected = false;
+  if (!norm_gamma) {
+    float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
+    if (prefill && rpart && T > 8) {
+      // the MFMA router runs its K slices in workgroups of their own; their
+      // sum and the top-k run as one launch
+      MOE_TRY(dev(moe::launch_router_mfma(static_cast<const uint16_t*>(x), router_w, router_bias, T, d->hidden,
+                                          d->n_experts, logits, rpart, s, false)));
+      MOE_TRY(dev(moe::launch_router_reduce_topk(rpart, moe::router_mfma_splits(T, d->hidden), T, d->n_experts,
+                                                 router_bias, k, logits, idx, w, s)));
+      selected = true;
+    } else {
+      MOE_TRY(dev(router(d, x, xf, router_w, router_bias, T, logits, rpart, s)));
+    }
+  }
+  if (prefill) {
     // prefill form: top-k, then sort + grouped GEMMs
-    MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
+    if (!selected) MOE_TRY(dev(moe::launch_topk_softmax(logits, T, d->n_experts, k, idx, w, s)));
     return run_experts(d, x, xf, idx, w, codes, scales, T, k, out, resid, ws, L, s);
   }
   // decode form: the gate/up kernel selects the experts itself (and writes

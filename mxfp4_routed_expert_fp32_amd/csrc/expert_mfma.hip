@@ -1069,7 +1069,7 @@ int router_mfma_splits(int T, int H) {
 }
 
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, float* part, hipStream_t s) {
+                              float* logits, float* part, hipStream_t s, bool reduce) {
   const int ntiles = (E + kRT_NT - 1) / kRT_NT;
   const size_t lds = (size_t)2 * kTile * 2;
   const int nsplit = part ? router_mfma_splits(T, H) : 1;
@@ -1082,7 +1082,7 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* b
     const unsigned grid = xcd_major ? (unsigned)(8 * mtiles) : (unsigned)(mtiles * ntiles * nsplit);
     k_router_mfma<<<dim3(grid), kThr, lds, s>>>(x + (size_t)t0 * H, wr, bias, n, H, E, ntiles, nsplit, xcd_major,
                                                 part, logits + (size_t)t0 * E);
-    if (nsplit > 1) {
+    if (nsplit > 1 && reduce) {
       const size_t cells = (size_t)n * E;
       k_router_reduce<<<dim3((unsigned)((cells + 255) / 256)), 256, 0, s>>>(part, nsplit, n, E, bias,
                                                                           logits + (size_t)t0 * E);

@@ -66,8 +66,16 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
 // in order; without it one workgroup runs all slices of its tile.  Both give
 // the same bits.
 int router_mfma_splits(int T, int H);
+// reduce = false leaves the partial sums to launch_router_reduce_topk (only
+// when the launch splits, router_mfma_splits(T, H) > 1, and T <= 256).
 hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                              float* logits, float* part, hipStream_t s);
+                              float* logits, float* part, hipStream_t s, bool reduce = true);
+// The split router's last step and the top-k in one launch: logits[t][e] =
+// sum of part[0..nsplit)[t][e] in slice order (+ bias[e]), the bits the
+// router's own reduction gives, then the exact top-k + softmax of each token
+// as launch_topk_softmax.  One workgroup per token.
+hipError_t launch_router_reduce_topk(const float* part, int nsplit, int T, int E, const float* bias, int k,
+                                     float* logits, int32_t* idx, float* w, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,

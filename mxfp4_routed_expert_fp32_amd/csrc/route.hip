@@ -437,6 +437,49 @@ size_t sort_workspace_bytes(int T, int E) {
   return (nblk + 1) * (size_t)E * sizeof(int32_t);
 }
 
+// ---------------------------------------------------------------- split router's sum + top-k
+// One workgroup of 1024 threads per token, one logit per thread (up to 1024
+// experts; more loop): its E logits are summed from the router's K-slice
+// partials part[sp][t][e] in slice order, from 0, with the bias added last
+// (the order of the router's own reduction kernel), kept in LDS and written
+// out; wave 0 then selects from LDS.
+constexpr int kRedTopkThreads = 1024;
+template <int MAXV>
+__global__ __launch_bounds__(kRedTopkThreads) void k_router_reduce_topk(const float* __restrict__ part, int nsplit, int T,
+                                                            int E, const float* __restrict__ bias, int k,
+                                                            float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                            float* __restrict__ wout) {
+  constexpr int kMaxSplit = 32;  // K slices of 256 for H <= 8192
+  __shared__ float lg[kWave * MAXV];
+  __shared__ uint64_t cand[kWave];
+  __shared__ uint32_t sel_e[kWave];
+  const int t = blockIdx.x;
+  const size_t n = (size_t)T * E;
+  for (int e = threadIdx.x; e < E; e += kRedTopkThreads) {
+    const size_t i = (size_t)t * E + e;
+    float pv[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) pv[sp] = sp < nsplit ? part[(size_t)sp * n + i] : 0.0f;
+    float v = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp)
+      if (sp < nsplit) v += pv[sp];
+    v = v + (bias ? bias[e] : 0.0f);
+    lg[e] = v;
+    logits[i] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  int sel;
+  float wsel;
+  topk_wave<MAXV>(lg, E, k, cand, sel_e, &sel, &wsel);
+  const int lane = threadIdx.x;
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = sel;
+    wout[(size_t)t * k + lane] = wsel;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <bool XF32, int TT>
@@ -485,6 +528,19 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
 }
 
 bool sort_is_one_workgroup(int T, const void* ws) { return T < kSortMultiMinTokens || ws == nullptr; }
+
+hipError_t launch_router_reduce_topk(const float* part, int nsplit, int T, int E, const float* bias, int k,
+                                     float* logits, int32_t* idx, float* w, hipStream_t s) {
+  if (nsplit < 1 || nsplit > 32) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)T);
+  if (E <= 64 * 4)
+    k_router_reduce_topk<4><<<grid, kRedTopkThreads, 0, s>>>(part, nsplit, T, E, bias, k, logits, idx, w);
+  else if (E <= 64 * 16)
+    k_router_reduce_topk<16><<<grid, kRedTopkThreads, 0, s>>>(part, nsplit, T, E, bias, k, logits, idx, w);
+  else
+    k_router_reduce_topk<64><<<grid, kRedTopkThreads, 0, s>>>(part, nsplit, T, E, bias, k, logits, idx, w);
+  return hipGetLastError();
+}
 
 hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_t* offsets, int32_t* pairs,
                                  void* ws, hipStream_t s, int4* blocks, int max_blocks, int32_t* nblocks) {
