@@ -347,6 +347,12 @@ def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
         assert np.sum(idx == 1) > 128
     xf = synth.tokens_f32(w, range(T))
     P.assert_logits_close(logits, oracle.router_logits(xf, wr.cpu().numpy(), bias=b), xf, wr.cpu().numpy(), bias=b)
+    # the forward's router (K slices in workgroups of their own up to 256 tokens,
+    # summed in the top-k launch) gives the stage entry's whole-tile bits
+    lg_stage = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    moe.moe_router_logits(desc, x, wr, bias, lg_stage)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.bits(logits), P.bits(lg_stage.cpu().numpy()))
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, b, logits)
     assert np.array_equal(idx, r_idx)
     P.assert_weights_close(wt, r_w, k)
