@@ -454,7 +454,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ybuf,
       for (int u = 0; u < G; ++u) {
         const int j = j0 + u;
         if (j < k) {
-          y[u] = *reinterpret_cast<const float4*>(ybuf + ((size_t)t * k + j) * H + n);
+          // read once: a non-temporal load (4096 tokens: 374 -> 330 us)
+          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + ((size_t)t * k + j) * H + n));
+          y[u] = make_float4(v.x, v.y, v.z, v.w);
           wj[u] = w[(size_t)t * k + j];
         } else {
           y[u] = make_float4(0.f, 0.f, 0.f, 0.f);
