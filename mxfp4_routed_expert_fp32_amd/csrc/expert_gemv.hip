@@ -152,7 +152,7 @@ __device__ __forceinline__ void load_row(RowBlocks<NBL>& r, rsrc_t codes, rsrc_t
     const int b = c + LPR * m;
     const bool ok = row >= 0 && b < nb;
     r.q[m] = __builtin_amdgcn_raw_buffer_load_b128(codes, ok ? rc + 16u * b : kOOB, 0, 2 /* nt */);
-    r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(scales, ok ? rsc + b : kOOB, 0, 0);
+    r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(scales, ok ? rsc + b : kOOB, 0, 2 /* nt */);
   }
 }
 
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
     const int n = r0 + 4 * st + rsub;
     const bool ok = st < steps && n < H;
     r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(dcod, ok ? (uint32_t)n * (uint32_t)(I / 2) + 16u * b : kOOB, 0, 2);
-    r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 0);
+    r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 2 /* nt */);
   };
   RowBlocks<1> ring[D];
 #pragma unroll
