@@ -52,6 +52,10 @@ def lib():
             L.oracle_moe_forward.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, ctypes.c_int]
             L.oracle_moe_forward.restype = ctypes.c_int
+            L.oracle_moe_experts.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+            L.oracle_moe_experts.restype = ctypes.c_int
+            L.oracle_moe_abs_scale.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+            L.oracle_moe_abs_scale.restype = ctypes.c_int
             L.oracle_rmsnorm.argtypes = [vp, vp, f32, i64, i64, vp]
             L.oracle_residual_add.argtypes = [vp, vp, i64]
             _lib = L
@@ -158,6 +162,57 @@ def moe_forward(x, w_router, experts, H: int, I: int, k: int, bias=None, logits_
     if rc != 0:
         raise RuntimeError("oracle_moe_forward failed with %d" % rc)
     return out, logits, idx, w
+
+
+def _expert_ptrs(experts, E, H, I):
+    cp = (ctypes.c_void_p * E)()
+    sp = (ctypes.c_void_p * E)()
+    keep = []
+    items = experts.items() if isinstance(experts, dict) else enumerate(experts)
+    for e, pair in items:
+        if pair is None:
+            continue
+        c = _c(pair[0], np.uint8)
+        s = _c(pair[1], np.uint8)
+        assert c.size == 3 * I * H // 2 and s.size == 3 * I * H // 32
+        keep += [c, s]
+        cp[e] = c.ctypes.data
+        sp[e] = s.ctypes.data
+    return cp, sp, keep
+
+
+def moe_experts(x, idx, w, experts, H: int, I: int, E: int, nthreads: int = 0) -> np.ndarray:
+    """Expert part with the routing given: out[t] = sum_j w[t,j] FFN_{idx[t,j]}(x[t])."""
+    x = _c(x, np.float32)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    assert x.shape == (T, H) and w.shape == (T, k)
+    cp, sp, keep = _expert_ptrs(experts, E, H, I)
+    out = np.empty((T, H), np.float32)
+    rc = lib().oracle_moe_experts(T, H, I, E, k, x.ctypes.data, idx.ctypes.data, w.ctypes.data,
+                                  ctypes.cast(cp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                  out.ctypes.data, nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_moe_experts failed with %d" % rc)
+    return out
+
+
+def moe_abs_scale(x, idx, w, experts, H: int, I: int, E: int, nthreads: int = 0) -> np.ndarray:
+    """Per-element magnitude scale A [T][H] (float64) for the given routing:
+    A[t, n] = sum_j |w[t, j]| sum_i |h_j[i]| |Wd_j[n, i]| (see oracle.c)."""
+    x = _c(x, np.float32)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    cp, sp, keep = _expert_ptrs(experts, E, H, I)
+    A = np.empty((T, H), np.float64)
+    rc = lib().oracle_moe_abs_scale(T, H, I, E, k, x.ctypes.data, idx.ctypes.data, w.ctypes.data,
+                                    ctypes.cast(cp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                    A.ctypes.data, nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_moe_abs_scale failed with %d" % rc)
+    return A
 
 
 def rmsnorm(r, gamma, eps: float) -> np.ndarray:

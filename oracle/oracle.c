@@ -279,6 +279,135 @@ done:
     return rc;
 }
 
+/*
+ * The expert part of the layer with the routing given: out[t] = sum_{j<k}
+ * w[t][j] * FFN_{idx[t][j]}(x[t]), summed in ascending rank j, with the FFN
+ * of expert_ffn.  This is the layer above with its router, top-k and softmax
+ * steps replaced by given ids and weights ("Deltafin's custom compiled
+ * runtime", section "Complete target sequence tape": the provider receives
+ * the route and its fp32 weights).  Ids must lie in [0, E); a row may repeat
+ * an id.  Returns 0, -1 on a shape or id error, -2 when a used expert has no
+ * data, -3 on allocation failure.
+ */
+int oracle_moe_experts(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float* x,
+                       const int32_t* idx, const float* w, const uint8_t* const* codes_e,
+                       const uint8_t* const* scales_e, float* out, int nthreads) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || H % 32 || I % 32) return -1;
+    for (int64_t p = 0; p < T * k; ++p)
+        if (idx[p] < 0 || idx[p] >= E) return -1;
+#ifdef _OPENMP
+    int saved = omp_get_max_threads();
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int rc = 0;
+    float* wg = (float*)malloc(sizeof(float) * (size_t)(I * H));
+    float* wu = (float*)malloc(sizeof(float) * (size_t)(I * H));
+    float* wd = (float*)malloc(sizeof(float) * (size_t)(H * I));
+    float* a = (float*)malloc(sizeof(float) * (size_t)I);
+    float* y = (float*)malloc(sizeof(float) * (size_t)(T * k * H + 1));
+    if (!wg || !wu || !wd || !a || !y) { rc = -3; goto done; }
+    for (int64_t e = 0; e < E; ++e) {
+        int used = 0;
+        for (int64_t p = 0; p < T * k; ++p) used |= (idx[p] == e);
+        if (!used) continue;
+        if (!codes_e[e] || !scales_e[e]) { rc = -2; goto done; }
+        const uint8_t* c = codes_e[e];
+        const uint8_t* s = scales_e[e];
+        oracle_dequant(c, s, I, H, wg);
+        oracle_dequant(c + I * H / 2, s + I * H / 32, I, H, wu);
+        oracle_dequant(c + 2 * (I * H / 2), s + 2 * (I * H / 32), H, I, wd);
+        for (int64_t p = 0; p < T * k; ++p)
+            if (idx[p] == e) expert_ffn(x + (p / k) * H, H, I, wg, wu, wd, a, y + p * H);
+    }
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < H; ++n) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < k; ++j) acc = acc + w[t * k + j] * y[(t * k + j) * H + n];
+            out[t * H + n] = acc;
+        }
+    }
+done:
+    free(wg); free(wu); free(wd); free(a); free(y);
+#ifdef _OPENMP
+    omp_set_num_threads(saved);
+#endif
+    return rc;
+}
+
+/* ---------------------------------------------------------------- error scale */
+
+/*
+ * Magnitude scale of each output element, for an elementwise reading of the
+ * relative error bar: the layer's last two steps with every input replaced by
+ * its absolute value, A[t][n] = sum_j |w[t][j]| sum_i |h_j[i]| |Wd_j[n][i]|,
+ * where h_j = silu(Wg_j x[t]) * (Wu_j x[t]) is the intermediate this oracle
+ * computes (expert_ffn) and the sums run in double.  A sum evaluated in fp32
+ * in any order differs from the exact one by a small multiple of eps times
+ * the sum of its terms' magnitudes, so |gpu - oracle| <= tol * A is a
+ * per-element bar that stays meaningful where the output itself cancels
+ * towards 0.  Not part of the layer's definition: test infrastructure for the
+ * comparison.  Same arguments as oracle_moe_experts; A is [T][H] double.
+ */
+int oracle_moe_abs_scale(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float* x,
+                         const int32_t* idx, const float* w, const uint8_t* const* codes_e,
+                         const uint8_t* const* scales_e, double* A, int nthreads) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || H % 32 || I % 32) return -1;
+    for (int64_t p = 0; p < T * k; ++p)
+        if (idx[p] < 0 || idx[p] >= E) return -1;
+#ifdef _OPENMP
+    int saved = omp_get_max_threads();
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int rc = 0;
+    float* wg = (float*)malloc(sizeof(float) * (size_t)(I * H));
+    float* wu = (float*)malloc(sizeof(float) * (size_t)(I * H));
+    float* wd = (float*)malloc(sizeof(float) * (size_t)(H * I));
+    float* a = (float*)malloc(sizeof(float) * (size_t)I);
+    float* ytmp = (float*)malloc(sizeof(float) * (size_t)H);
+    double* y = (double*)malloc(sizeof(double) * (size_t)(T * k * H + 1));
+    if (!wg || !wu || !wd || !a || !ytmp || !y) { rc = -3; goto done; }
+    for (int64_t e = 0; e < E; ++e) {
+        int used = 0;
+        for (int64_t p = 0; p < T * k; ++p) used |= (idx[p] == e);
+        if (!used) continue;
+        if (!codes_e[e] || !scales_e[e]) { rc = -2; goto done; }
+        const uint8_t* c = codes_e[e];
+        const uint8_t* s = scales_e[e];
+        oracle_dequant(c, s, I, H, wg);
+        oracle_dequant(c + I * H / 2, s + I * H / 32, I, H, wu);
+        oracle_dequant(c + 2 * (I * H / 2), s + 2 * (I * H / 32), H, I, wd);
+        for (int64_t p = 0; p < T * k; ++p) {
+            if (idx[p] != e) continue;
+            expert_ffn(x + (p / k) * H, H, I, wg, wu, wd, a, ytmp);  /* a = h of this pair */
+            #pragma omp parallel for schedule(static)
+            for (int64_t n = 0; n < H; ++n) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < I; ++i) acc += fabs((double)a[i]) * fabs((double)wd[n * I + i]);
+                y[p * H + n] = acc;
+            }
+        }
+    }
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < H; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j) acc += fabs((double)w[t * k + j]) * y[(t * k + j) * H + n];
+            A[t * H + n] = acc;
+        }
+    }
+done:
+    free(wg); free(wu); free(wd); free(a); free(ytmp); free(y);
+#ifdef _OPENMP
+    omp_set_num_threads(saved);
+#endif
+    return rc;
+}
+
 /* ---------------------------------------------------------------- stack parts */
 
 /* RMSNorm with gain: n = r * (1 / sqrt(mean(r^2) + eps)) * gamma, per token;

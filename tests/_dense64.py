@@ -73,17 +73,36 @@ def layer64(x, w_router, experts, H, I, k, bias=None):
     return out, logits, idx, w
 
 
+def experts64(x, idx, w, experts, H, I):
+    """Expert part with given routing in float64: out[t] = sum_j w[t,j] FFN_{idx[t,j]}(x[t])."""
+    x = np.asarray(x, np.float64)
+    idx = np.asarray(idx)
+    w = np.asarray(w, np.float64)
+    T, k = idx.shape
+    out = np.zeros((T, H))
+    for e in np.unique(idx):
+        wg, wu, wd = expert_mats64(experts[e][0], experts[e][1], H, I)
+        for t, j in zip(*np.nonzero(idx == e)):
+            g = wg @ x[t]
+            u = wu @ x[t]
+            a = g / (1.0 + np.exp(-g)) * u
+            out[t] += w[t, j] * (wd @ a)
+    return out
+
+
 def scale_ref64(x, experts, idx, w, H, I):
-    """Magnitude scale A: the layer evaluated on |x|, |W| and |a| (for the
-    elementwise error diagnostic)."""
-    x = np.abs(np.asarray(x, np.float64))
+    """Magnitude scale A[t, n] = sum_j |w[t, j]| sum_i |h_j[i]| |Wd_j[n, i]| with
+    h evaluated in float64 (for the elementwise error diagnostic); each distinct
+    expert is decoded once."""
+    x = np.asarray(x, np.float64)
+    idx = np.asarray(idx)
     T = x.shape[0]
     out = np.zeros((T, H))
-    for t in range(T):
-        for j in range(idx.shape[1]):
-            wg, wu, wd = expert_mats64(experts[idx[t, j]][0], experts[idx[t, j]][1], H, I)
-            g = np.abs(wg) @ x[t]
-            u = np.abs(wu) @ x[t]
-            a = g * u
-            out[t] += abs(w[t, j]) * (np.abs(wd) @ a)
+    for e in np.unique(idx):
+        wg, wu, wd = expert_mats64(experts[e][0], experts[e][1], H, I)
+        for t, j in zip(*np.nonzero(idx == e)):
+            g = wg @ x[t]
+            u = wu @ x[t]
+            a = g / (1.0 + np.exp(-g)) * u
+            out[t] += abs(w[t, j]) * (np.abs(wd) @ np.abs(a))
     return out

@@ -10,6 +10,9 @@
 - Whole layer: dense fp64 brute force over all experts with a one-hot top-k mask
   (tests/_dense64.py, which never calls the oracle); closed-form special cases;
   permutation of expert storage; thread-count invariance.
+- Expert part with given routing: dense fp64 brute force (repeated ids
+  included) and the forward on the same routing.
+- Magnitude scale of the elementwise error bar: fp64 numpy and a closed form.
 - RMSNorm: constant-vector closed form and fp64.
 """
 import os
@@ -271,6 +274,63 @@ def test_logits_override_drives_selection():
     out, logits, idx, w = oracle.moe_forward(x, wr, ex, H, I, k, logits_override=lo)
     assert np.array_equal(idx[0], [4, 1])
     assert np.array_equal(logits, lo)
+
+
+def test_experts_given_routing_matches_dense_fp64():
+    H, I, E, k, T = 96, 64, 7, 3, 4
+    x, _, ex, _ = tiny_case(51, H, I, E, k, T=T)
+    idx = np.array([[6, 0, 3], [0, 3, 6], [2, 2, 5], [4, 1, 1]], np.int32)  # repeated ids in rows 2, 3
+    w = np.array([[0.5, 0.25, 0.25], [0.7, 0.2, 0.1], [0.3, 0.3, 0.4], [1.0, -0.5, 0.25]], np.float32)
+    got = oracle.moe_experts(x, idx, w, ex, H, I, E)
+    ref = d64.experts64(x, idx, w, ex, H, I)
+    assert np.all(normwise(got, ref) <= TOL / 4)
+    with pytest.raises(RuntimeError):
+        oracle.moe_experts(x, np.full((T, k), E, np.int32), w, ex, H, I, E)  # ids must lie in [0, E)
+
+
+def test_experts_given_routing_equals_forward_on_its_routing():
+    """On the forward's own selection and weights the given-routing entry is
+    the same computation, so the same bits (and the forward is pinned above)."""
+    H, I, E, k = 256, 128, 8, 2
+    x, wr, ex, b = tiny_case(52, H, I, E, k, bias=True, T=3)
+    out, _, idx, w = oracle.moe_forward(x, wr, ex, H, I, k, bias=b)
+    assert np.array_equal(bits(oracle.moe_experts(x, idx, w, ex, H, I, E)), bits(out))
+
+
+def test_abs_scale_matches_dense_fp64():
+    H, I, E, k, T = 128, 96, 6, 3, 3
+    x, _, ex, _ = tiny_case(53, H, I, E, k, T=T)
+    idx = np.array([[5, 0, 2], [1, 1, 4], [3, 2, 0]], np.int32)
+    w = np.array([[0.6, 0.3, 0.1], [0.5, -0.25, 0.25], [0.2, 0.2, 0.6]], np.float32)
+    got = oracle.moe_abs_scale(x, idx, w, ex, H, I, E)
+    ref = d64.scale_ref64(x, ex, idx, w, H, I)  # h in fp64 here, fp32 in the oracle
+    assert np.all(np.abs(got - ref) <= 1e-5 * ref)
+    # a closed form: every weight 1 (codes 0x22, scale byte 127) gives g = u = S
+    # = sum_h x[t, h], h = silu(S) * S for every i, and
+    # A[t, n] = sum_j |w[t, j]| * I * |silu(S) * S| for every n
+    ones = [(np.full_like(c, 0x22), np.full_like(s_, 127)) for c, s_ in ex]
+    got = oracle.moe_abs_scale(x, idx, w, ones, H, I, E)
+    S = x.astype(np.float64).sum(1)
+    want = np.abs(w.astype(np.float64)).sum(1) * I * np.abs(S / (1 + np.exp(-S)) * S)
+    assert np.all(np.abs(got - want[:, None]) <= 1e-5 * want[:, None])
+
+
+def test_oracle_meets_elementwise_bar_against_fp64():
+    """The elementwise reading of the 2e-5 bar, |oracle - exact| <= 2e-5 * A,
+    holds for the fp32 oracle itself at the model's width (one token, one
+    expert pair per rank), so a second fp32 implementation can be held to it."""
+    H, I, E, k = 7168, 1536, 4, 2
+    w_ = synth.Workload("pinw", 97, 1, H, I, E, k, "bf16", weight_seed=1097)
+    x = synth.tokens_f32(w_, [0])
+    c, s_ = synth.experts(w_)
+    ce, se = w_.code_bytes_per_expert, w_.scale_bytes_per_expert
+    ex = [(c[e * ce:(e + 1) * ce], s_[e * se:(e + 1) * se]) for e in range(E)]
+    idx = np.array([[2, 0]], np.int32)
+    w = np.array([[0.75, 0.25]], np.float32)
+    got = oracle.moe_experts(x, idx, w, ex, H, I, E).astype(np.float64)
+    ref = d64.experts64(x, idx, w, ex, H, I)
+    A = oracle.moe_abs_scale(x, idx, w, ex, H, I, E)
+    assert np.max(np.abs(got - ref) / A) <= TOL / 4
 
 
 # ------------------------------------------------------------------ stack parts
