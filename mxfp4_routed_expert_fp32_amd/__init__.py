@@ -30,7 +30,7 @@ EXPORTS = [
     "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_combine",
     "moe_router_logits", "moe_topk_softmax", "moe_sort_workspace_bytes", "moe_sort_by_expert",
     "moe_max_expert_blocks", "moe_expert_blocks", "moe_mxfp4_grouped_gate_up", "moe_mxfp4_grouped_down",
-    "moe_mxfp4_dequant", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_bytes",
+    "moe_mxfp4_dequant", "moe_mxfp4_dequant_bf16", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_bytes",
     "moe_mxfp4_stack_forward", "moe_stack_graph_create", "moe_stack_graph_launch",
     "moe_stack_graph_destroy",
 ]
@@ -91,6 +91,7 @@ def lib():
                 "moe_mxfp4_grouped_gate_up": ([D, vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_grouped_down": ([D, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_dequant": ([D, vp, vp, i64, i32, vp, vp], ctypes.c_int),
+                "moe_mxfp4_dequant_bf16": ([D, vp, vp, i64, i32, vp, vp], ctypes.c_int),
                 "moe_rmsnorm": ([vp, vp, ctypes.c_float, i32, i32, vp, vp], ctypes.c_int),
                 "moe_residual_add": ([vp, vp, i64, vp], ctypes.c_int),
                 "moe_stack_workspace_bytes": ([D, i32, i32, P(sz)], ctypes.c_int),
@@ -261,6 +262,12 @@ def moe_mxfp4_grouped_down(desc, hterm, pair_list, blocks, n_blocks, packed_code
 
 def moe_mxfp4_dequant(desc, packed_codes, packed_scales, expert, matrix, out, stream=None):
     _check("moe_mxfp4_dequant", lib().moe_mxfp4_dequant(
+        ctypes.byref(desc), _ptr(packed_codes), _ptr(packed_scales), expert, matrix, _ptr(out),
+        _stream(stream)))
+
+
+def moe_mxfp4_dequant_bf16(desc, packed_codes, packed_scales, expert, matrix, out, stream=None):
+    _check("moe_mxfp4_dequant_bf16", lib().moe_mxfp4_dequant_bf16(
         ctypes.byref(desc), _ptr(packed_codes), _ptr(packed_scales), expert, matrix, _ptr(out),
         _stream(stream)))
 

@@ -30,7 +30,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool mul_ok(size_t a, size_t b, size_t* r) { return !__builtin_mul_overflow(a, b, r); }
 inline bool add_ok(size_t a, size_t b, size_t* r) { return !__builtin_add_overflow(a, b, r); }
 
-int check_desc(const moe_layer_desc* d) {
+moe_status check_desc(const moe_layer_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->abi_version != MOE_ABI_VERSION || d->struct_size != sizeof(moe_layer_desc)) return MOE_ERR_ABI;
   if (d->reserved != 0) return MOE_ERR_ABI;
@@ -43,7 +43,7 @@ int check_desc(const moe_layer_desc* d) {
 }
 
 // Per-expert byte counts; checked.
-int expert_bytes(const moe_layer_desc* d, size_t* cb, size_t* sb) {
+moe_status expert_bytes(const moe_layer_desc* d, size_t* cb, size_t* sb) {
   size_t hi;
   if (!mul_ok((size_t)d->hidden, (size_t)d->inter, &hi)) return MOE_ERR_OVERFLOW;
   if (!mul_ok(hi, 3, &hi)) return MOE_ERR_OVERFLOW;
@@ -72,7 +72,7 @@ struct FwdLayout {
   bool has_rpart;
 };
 
-int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
+moe_status forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
   size_t TE, Tk, TkI, TkH;
   if (!mul_ok((size_t)T, (size_t)d->n_experts, &TE) || !mul_ok((size_t)T, (size_t)k, &Tk) ||
       !mul_ok(Tk, (size_t)d->inter, &TkI) || !mul_ok(Tk, (size_t)d->hidden, &TkH))
@@ -105,15 +105,15 @@ int forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) 
   return MOE_OK;
 }
 
-inline int dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+inline moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 #define MOE_TRY(expr)             \
   do {                            \
-    int rc_ = (expr);             \
+    moe_status rc_ = (expr);      \
     if (rc_ != MOE_OK) return rc_; \
   } while (0)
 
-int check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
+moe_status check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
   if (T < 1 || T > kMaxTokens) return MOE_ERR_SHAPE;
   if (k < 1 || k > d->top_k_max) return MOE_ERR_SHAPE;
   return MOE_OK;
@@ -153,7 +153,7 @@ hipError_t router(const moe_layer_desc* d, const void* x, bool x_f32, const floa
 
 // Expert part of the layer given the routing (idx, w on the device).  For one token the pairs are
 // the k ranks of that token and idx itself is the pair -> expert map.
-int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_t* idx, const float* w,
+moe_status run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_t* idx, const float* w,
                 const void* codes, const void* scales, int32_t T, int32_t k, float* out,
                 const float* resid, char* ws, const FwdLayout& L, hipStream_t s) {
   const int H = d->hidden, I = d->inter, E = d->n_experts;
@@ -194,7 +194,7 @@ int run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const int32_
   return MOE_OK;
 }
 
-int check_forward_args(const moe_layer_desc* d, const void* x, int32_t x_dtype, const void* codes,
+moe_status check_forward_args(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const void* codes,
                        const void* scales, int32_t T, int32_t k, const float* out, const void* ws,
                        size_t ws_bytes, FwdLayout* L) {
   MOE_TRY(check_desc(d));
@@ -209,7 +209,7 @@ int check_forward_args(const moe_layer_desc* d, const void* x, int32_t x_dtype, 
   return MOE_OK;
 }
 
-int forward_impl(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+moe_status forward_impl(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const float* router_w,
                  const float* router_bias, const void* codes, const void* scales, int32_t T, int32_t k,
                  float* out, float* logits_out, int32_t* idx_out, float* w_out, void* workspace,
                  const FwdLayout& L, const float* resid, hipStream_t s, const float* norm_gamma = nullptr,
@@ -265,8 +265,8 @@ extern "C" {
 
 uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-const char* moe_status_string(int status) {
-  switch (status) {
+const char* moe_status_string(moe_status status) {
+  switch ((int)status) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is out of range or not a multiple of 32";
@@ -283,9 +283,9 @@ const char* moe_status_string(int status) {
   }
 }
 
-int moe_layer_check(const moe_layer_desc* desc) { return check_desc(desc); }
+moe_status moe_layer_check(const moe_layer_desc* desc) { return check_desc(desc); }
 
-int moe_mxfp4_packed_bytes(const moe_layer_desc* d, size_t* codes_bytes, size_t* scales_bytes) {
+moe_status moe_mxfp4_packed_bytes(const moe_layer_desc* d, size_t* codes_bytes, size_t* scales_bytes) {
   MOE_TRY(check_desc(d));
   if (!codes_bytes || !scales_bytes) return MOE_ERR_NULL;
   size_t cb, sb;
@@ -297,7 +297,7 @@ int moe_mxfp4_packed_bytes(const moe_layer_desc* d, size_t* codes_bytes, size_t*
   return MOE_OK;
 }
 
-int moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
+moe_status moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
   MOE_TRY(check_desc(d));
   if (!bytes) return MOE_ERR_NULL;
   MOE_TRY(check_tokens(n_tokens, k, d));
@@ -307,7 +307,7 @@ int moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, si
   return MOE_OK;
 }
 
-int moe_mxfp4_pack(const moe_layer_desc* d, const void* logical_codes, const void* logical_scales,
+moe_status moe_mxfp4_pack(const moe_layer_desc* d, const void* logical_codes, const void* logical_scales,
                    int64_t expert_begin, int64_t expert_count, void* packed_codes, void* packed_scales,
                    void* stream) {
   MOE_TRY(check_desc(d));
@@ -331,7 +331,7 @@ int moe_mxfp4_pack(const moe_layer_desc* d, const void* logical_codes, const voi
   return MOE_OK;
 }
 
-int moe_mxfp4_forward(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+moe_status moe_mxfp4_forward(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const float* router_w,
                       const float* router_bias, const void* packed_codes, const void* packed_scales,
                       int32_t n_tokens, int32_t k, float* out, float* logits_out, int32_t* topk_idx_out,
                       float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -344,7 +344,7 @@ int moe_mxfp4_forward(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
                       out, logits_out, topk_idx_out, topk_w_out, workspace, L, nullptr, as_stream(stream));
 }
 
-int moe_mxfp4_experts(const moe_layer_desc* d, const void* x, int32_t x_dtype, const int32_t* topk_idx,
+moe_status moe_mxfp4_experts(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const int32_t* topk_idx,
                       const float* topk_w, const void* packed_codes, const void* packed_scales,
                       int32_t n_tokens, int32_t k, float* out, void* workspace, size_t workspace_bytes,
                       void* stream) {
@@ -356,7 +356,7 @@ int moe_mxfp4_experts(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
                      n_tokens, k, out, nullptr, static_cast<char*>(workspace), L, as_stream(stream));
 }
 
-int moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, int32_t x_dtype, const int32_t* pair_expert,
+moe_status moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const int32_t* pair_expert,
                       int32_t n_pairs, int32_t k, const void* codes, const void* scales, float* h,
                       void* stream) {
   MOE_TRY(check_desc(d));
@@ -369,7 +369,7 @@ int moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
                                      d->hidden, d->inter, d->n_experts, h, as_stream(stream)));
 }
 
-int moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t* pair_expert, int32_t n_pairs,
+moe_status moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t* pair_expert, int32_t n_pairs,
                    const void* codes, const void* scales, float* y, void* stream) {
   MOE_TRY(check_desc(d));
   if (!h || !pair_expert || !codes || !scales || !y) return MOE_ERR_NULL;
@@ -380,7 +380,7 @@ int moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t* pair_
                                    as_stream(stream)));
 }
 
-int moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden, const float* resid,
+moe_status moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden, const float* resid,
                 float* out, void* stream) {
   if (!y || !w || !out) return MOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens || k < 1 || k > kMaxTopK || hidden < 4 || hidden % 4)
@@ -389,7 +389,7 @@ int moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int
   return dev(moe::launch_combine(y, w, n_tokens, k, hidden, resid, out, as_stream(stream)));
 }
 
-int moe_router_logits(const moe_layer_desc* d, const void* x, int32_t x_dtype, const float* router_w,
+moe_status moe_router_logits(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const float* router_w,
                       const float* router_bias, int32_t n_tokens, float* logits, void* stream) {
   MOE_TRY(check_desc(d));
   if (!x || !router_w || !logits) return MOE_ERR_NULL;
@@ -400,7 +400,7 @@ int moe_router_logits(const moe_layer_desc* d, const void* x, int32_t x_dtype, c
                     as_stream(stream)));
 }
 
-int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* idx,
+moe_status moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k, int32_t* idx,
                      float* w, void* stream) {
   if (!logits || !idx || !w) return MOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
@@ -409,7 +409,7 @@ int moe_topk_softmax(const float* logits, int32_t n_tokens, int32_t n_experts, i
   return dev(moe::launch_topk_softmax(logits, n_tokens, n_experts, k, idx, w, as_stream(stream)));
 }
 
-int moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, size_t* bytes) {
+moe_status moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, size_t* bytes) {
   if (!bytes) return MOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens || n_experts < 1 || k < 1 || k > n_experts || k > kMaxTopK)
     return MOE_ERR_SHAPE;
@@ -418,7 +418,7 @@ int moe_sort_workspace_bytes(int32_t n_experts, int32_t n_tokens, int32_t k, siz
   return MOE_OK;
 }
 
-int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_experts, int32_t k,
+moe_status moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_experts, int32_t k,
                        int32_t* expert_offsets, int32_t* pair_list, void* workspace, size_t workspace_bytes,
                        void* stream) {
   if (!topk_idx || !expert_offsets || !pair_list) return MOE_ERR_NULL;
@@ -433,7 +433,7 @@ int moe_sort_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t n_expe
                                         need > 0 ? workspace : nullptr, as_stream(stream)));
 }
 
-int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks) {
+moe_status moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_blocks) {
   if (!max_blocks) return MOE_ERR_NULL;
   if (n_experts < 1 || n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
   if (n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -441,7 +441,7 @@ int moe_max_expert_blocks(int32_t n_experts, int32_t n_pairs, int32_t* max_block
   return MOE_OK;
 }
 
-int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,
+moe_status moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t n_pairs, int32_t* blocks,
                       int32_t max_blocks, int32_t* n_blocks, void* stream) {
   if (!expert_offsets || !blocks || !n_blocks) return MOE_ERR_NULL;
   if (n_experts < 1 || n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
@@ -452,7 +452,7 @@ int moe_expert_blocks(const int32_t* expert_offsets, int32_t n_experts, int32_t 
                                        n_blocks, as_stream(stream)));
 }
 
-int moe_mxfp4_grouped_gate_up(const moe_layer_desc* d, const void* x, int32_t n_tokens, int32_t k,
+moe_status moe_mxfp4_grouped_gate_up(const moe_layer_desc* d, const void* x, int32_t n_tokens, int32_t k,
                               const int32_t* pair_list, const int32_t* blocks, const int32_t* n_blocks,
                               int32_t max_blocks, const void* packed_codes, const void* packed_scales, void* hterm,
                               void* stream) {
@@ -472,7 +472,7 @@ int moe_mxfp4_grouped_gate_up(const moe_layer_desc* d, const void* x, int32_t n_
                                      k, (int)P, static_cast<uint16_t*>(hterm), as_stream(stream)));
 }
 
-int moe_mxfp4_grouped_down(const moe_layer_desc* d, const void* hterm, int32_t n_pairs, const int32_t* pair_list,
+moe_status moe_mxfp4_grouped_down(const moe_layer_desc* d, const void* hterm, int32_t n_pairs, const int32_t* pair_list,
                            const int32_t* blocks, const int32_t* n_blocks, int32_t max_blocks,
                            const void* packed_codes, const void* packed_scales, float* y, void* stream) {
   MOE_TRY(check_desc(d));
@@ -489,8 +489,8 @@ int moe_mxfp4_grouped_down(const moe_layer_desc* d, const void* hterm, int32_t n
                                    d->hidden, d->inter, d->n_experts, n_pairs, y, as_stream(stream)));
 }
 
-int moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
-                      int64_t expert, int32_t matrix, float* out, void* stream) {
+static moe_status dequant_entry(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
+                                int64_t expert, int32_t matrix, float* out, bool via_bf16, void* stream) {
   MOE_TRY(check_desc(d));
   if (!packed_codes || !packed_scales || !out) return MOE_ERR_NULL;
   if (expert < 0 || expert >= d->n_experts || matrix < 0 || matrix > 2) return MOE_ERR_RANGE;
@@ -502,10 +502,20 @@ int moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const v
   const int cols = matrix == 2 ? d->inter : d->hidden;
   const uint8_t* c = static_cast<const uint8_t*>(packed_codes) + (size_t)expert * cb + (size_t)matrix * mc;
   const uint8_t* s = static_cast<const uint8_t*>(packed_scales) + (size_t)expert * sb + (size_t)matrix * ms;
-  return dev(moe::launch_dequant(c, s, rows, cols, out, as_stream(stream)));
+  return dev(moe::launch_dequant(c, s, rows, cols, out, via_bf16, as_stream(stream)));
 }
 
-int moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden, float* n_out,
+moe_status moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
+                             int64_t expert, int32_t matrix, float* out, void* stream) {
+  return dequant_entry(d, packed_codes, packed_scales, expert, matrix, out, false, stream);
+}
+
+moe_status moe_mxfp4_dequant_bf16(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
+                                  int64_t expert, int32_t matrix, float* out, void* stream) {
+  return dequant_entry(d, packed_codes, packed_scales, expert, matrix, out, true, stream);
+}
+
+moe_status moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden, float* n_out,
                 void* stream) {
   if (!r || !gamma || !n_out) return MOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens || hidden < 4 || hidden % 4) return MOE_ERR_SHAPE;
@@ -513,7 +523,7 @@ int moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens,
   return dev(moe::launch_rmsnorm(r, gamma, eps, n_tokens, hidden, n_out, as_stream(stream)));
 }
 
-int moe_residual_add(float* r, const float* dlt, int64_t n, void* stream) {
+moe_status moe_residual_add(float* r, const float* dlt, int64_t n, void* stream) {
   if (!r || !dlt) return MOE_ERR_NULL;
   if (n < 0) return MOE_ERR_SHAPE;
   return dev(moe::launch_residual_add(r, dlt, (size_t)n, as_stream(stream)));
@@ -521,7 +531,7 @@ int moe_residual_add(float* r, const float* dlt, int64_t n, void* stream) {
 
 // ---------------------------------------------------------------- layer stack + graph
 
-static int stack_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L, size_t* nbuf_off,
+static moe_status stack_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L, size_t* nbuf_off,
                         size_t* total) {
   MOE_TRY(forward_layout(d, T, k, L));
   size_t nb;
@@ -534,7 +544,7 @@ static int stack_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout
   return MOE_OK;
 }
 
-int moe_stack_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
+moe_status moe_stack_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
   MOE_TRY(check_desc(d));
   if (!bytes) return MOE_ERR_NULL;
   MOE_TRY(check_tokens(n_tokens, k, d));
@@ -545,9 +555,9 @@ int moe_stack_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t
   return MOE_OK;
 }
 
-static int stack_check(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+static moe_status stack_check(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
                        const void* const* scales, const float* const* router_w, const float* const* gamma,
-                       const void* x, int32_t x_dtype, int32_t T, int32_t k, const float* residual,
+                       const void* x, moe_dtype x_dtype, int32_t T, int32_t k, const float* residual,
                        const void* ws, size_t ws_bytes, FwdLayout* L, size_t* nb_off) {
   MOE_TRY(check_desc(d));
   if (n_layers < 1 || n_layers > 4096) return MOE_ERR_SHAPE;
@@ -568,10 +578,10 @@ static int stack_check(const moe_layer_desc* d, int32_t n_layers, const void* co
   return MOE_OK;
 }
 
-static int stack_enqueue(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+static moe_status stack_enqueue(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
                          const void* const* scales, const float* const* router_w,
                          const float* const* router_bias, const float* const* gamma, float eps,
-                         const void* x, int32_t x_dtype, int32_t T, int32_t k, float* residual, void* ws,
+                         const void* x, moe_dtype x_dtype, int32_t T, int32_t k, float* residual, void* ws,
                          const FwdLayout& L, size_t nb_off, hipStream_t s) {
   const size_t n = (size_t)T * d->hidden;
   float* nbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + nb_off);
@@ -586,10 +596,10 @@ static int stack_enqueue(const moe_layer_desc* d, int32_t n_layers, const void* 
   return MOE_OK;
 }
 
-int moe_mxfp4_stack_forward(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+moe_status moe_mxfp4_stack_forward(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
                             const void* const* scales, const float* const* router_w,
                             const float* const* router_bias, const float* const* gamma, float eps,
-                            const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k, float* residual,
+                            const void* x, moe_dtype x_dtype, int32_t n_tokens, int32_t k, float* residual,
                             void* workspace, size_t workspace_bytes, void* stream) {
   FwdLayout L;
   size_t nb_off;
@@ -604,10 +614,10 @@ struct moe_stack_graph {
   hipGraphExec_t exec = nullptr;
 };
 
-int moe_stack_graph_create(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
+moe_status moe_stack_graph_create(const moe_layer_desc* d, int32_t n_layers, const void* const* codes,
                            const void* const* scales, const float* const* router_w,
                            const float* const* router_bias, const float* const* gamma, float eps,
-                           const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k, float* residual,
+                           const void* x, moe_dtype x_dtype, int32_t n_tokens, int32_t k, float* residual,
                            void* workspace, size_t workspace_bytes, void* stream, moe_stack_graph** out) {
   if (!out) return MOE_ERR_NULL;
   *out = nullptr;
@@ -619,7 +629,7 @@ int moe_stack_graph_create(const moe_layer_desc* d, int32_t n_layers, const void
   // caller's stream, which may be the null stream, is never in capture mode.
   hipStream_t cap = nullptr;
   if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_DEVICE;
-  int rc = MOE_OK;
+  moe_status rc = MOE_OK;
   hipGraph_t g = nullptr;
   if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
     (void)hipStreamDestroy(cap);
@@ -651,14 +661,14 @@ int moe_stack_graph_create(const moe_layer_desc* d, int32_t n_layers, const void
   return MOE_OK;
 }
 
-int moe_stack_graph_launch(moe_stack_graph* g, void* stream) {
+moe_status moe_stack_graph_launch(moe_stack_graph* g, void* stream) {
   if (!g) return MOE_ERR_NULL;
   return dev(hipGraphLaunch(g->exec, as_stream(stream)));
 }
 
-int moe_stack_graph_destroy(moe_stack_graph* g) {
+moe_status moe_stack_graph_destroy(moe_stack_graph* g) {
   if (!g) return MOE_OK;
-  int rc = MOE_OK;
+  moe_status rc = MOE_OK;
   if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = MOE_ERR_DEVICE;
   if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = MOE_ERR_DEVICE;
   delete g;

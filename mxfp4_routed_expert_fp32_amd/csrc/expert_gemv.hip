@@ -4,8 +4,11 @@
 // The fused dequant + GEMV follows brain.bigb.es "deltafin", section "The
 // techniques that bought the 82x" (E2M1 decode through a 16-entry table, E8M0
 // scale applied to the fp32 exponent, one pass over the weights).  Here the
-// decode is the gfx950 scaled FP4 conversion, which yields exactly
-// E2M1(code) * 2^(S-127) (checked bit for bit by the dequant export tests).
+// decode is a gfx950 scaled FP4 conversion: the bf16 form for bf16
+// activations, the fp32 form for fp32 activations and for the down
+// projection.  The library exports each conversion alone (moe_mxfp4_dequant
+// and moe_mxfp4_dequant_bf16), and the tests compare both bit for bit with
+// the oracle over every code and scale byte.
 //
 // Weight layout (row-major, per expert gate | up | down): a row of a
 // [rows][K] matrix is K/2 code bytes, plus K/32 scale bytes in the scale
@@ -360,6 +363,11 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
 // ---------------------------------------------------------------- down, K split across waves
 constexpr int kDnKsRing = 4;   // weight steps in flight + 1 (measured best of 2..8)
 constexpr int kDnKsPerCu = 8;  // workgroups per CU the grid aims at (measured best of 2..12)
+// Largest LDS table of row partials per workgroup: with many pairs the grid
+// target alone would give one workgroup all H rows (H * KS * 4 bytes, over
+// the 160 KiB a workgroup may have at H = 8192, I = 4096); capped, the rows
+// are split into more parts instead.
+constexpr int kDnKsLdsCap = 16384;
 // For I = 512*KS (I/32 = 16*KS blocks per row): wave ks of a workgroup takes
 // blocks 16*ks .. 16*ks+15 of every row of the workgroup's row range, 16
 // lanes per row and 4 rows per step (256 contiguous code bytes per row), so a
@@ -582,6 +590,8 @@ hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P
     const int want = (kDnKsPerCu * cu_count() + P - 1) / P;
     int rows = (H + want - 1) / want;
     rows = (rows + 4 * D - 1) / (4 * D) * (4 * D);
+    const int max_rows = kDnKsLdsCap / (ks * 4) / (4 * D) * (4 * D);
+    if (rows > max_rows) rows = max_rows;
     const int parts = (H + rows - 1) / rows;
     const size_t lds = (size_t)rows * ks * 4;
     const dim3 grid((unsigned)(P * parts));

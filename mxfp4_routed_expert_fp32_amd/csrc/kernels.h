@@ -78,8 +78,10 @@ hipError_t launch_router_reduce_topk(const float* part, int nsplit, int T, int E
                                      float* logits, int32_t* idx, float* w, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// via_bf16: decode through the bf16 conversion of the bf16 GEMV and the MFMA
+// kernels (widened to fp32), else through the fp32 conversion.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
-                          hipStream_t s);
+                          bool via_bf16, hipStream_t s);
 hipError_t launch_rmsnorm(const float* r, const float* gamma, float eps, int T, int H, float* out,
                           hipStream_t s);
 hipError_t launch_residual_add(float* r, const float* d, size_t n, hipStream_t s);

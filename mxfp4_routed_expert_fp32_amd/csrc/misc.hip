@@ -24,9 +24,17 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
 }
 
 // ---------------------------------------------------------------- dequant export
-// Each thread decodes 8 elements (one 32-bit word of codes) with the same
-// hardware conversion the expert kernels use.  A NaN scale gives the canonical
-// quiet NaN 0x7FC00000 (the conversion itself sets the sign bit).
+// Two exports of E2M1(code) * 2^(S-127), one per gfx950 scaled conversion the
+// expert kernels use; each thread decodes 8 elements (one 32-bit word of
+// codes).
+//  - k_dequant: v_cvt_scalef32_pk_f32_fp4, the conversion of the fp32-operand
+//    GEMVs (fp32 activations, and the down projection of the decode form),
+//    with the NaN scale byte 0xFF written as the canonical quiet NaN
+//    0x7FC00000.
+//  - k_dequant_bf16: decode8 (v_cvt_scalef32_pk_bf16_fp4), the conversion of
+//    the bf16-activation decode GEMV and of both MFMA kernels, widened to fp32
+//    by placing the 16 bits in the top half.  Nothing is canonicalised: the
+//    export shows exactly the bits those kernels multiply with.
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales, int rows, int cols,
                                                  float* __restrict__ out) {
@@ -53,12 +61,34 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   }
 }
 
+__global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales, int rows, int cols,
+                                                      float* __restrict__ out) {
+  const size_t words = (size_t)rows * cols / 8;
+  const int wpr = cols / 8;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < words; q += (size_t)gridDim.x * 256) {
+    const size_t n = q / wpr;
+    const int c8 = (int)(q % wpr);
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[q];
+    const uint32_t sbyte = scales[n * (cols / 32) + (c8 * 8) / 32];
+    const bf16x8 b = decode8(w, e8m0_operand(sbyte));
+    uint16_t u[8];
+    __builtin_memcpy(u, &b, 16);
+    float4* o = reinterpret_cast<float4*>(out + n * cols + (size_t)c8 * 8);
+    o[0] = make_float4(bf16_bits_to_f32(u[0]), bf16_bits_to_f32(u[1]), bf16_bits_to_f32(u[2]), bf16_bits_to_f32(u[3]));
+    o[1] = make_float4(bf16_bits_to_f32(u[4]), bf16_bits_to_f32(u[5]), bf16_bits_to_f32(u[6]), bf16_bits_to_f32(u[7]));
+  }
+}
+
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
-                          hipStream_t s) {
+                          bool via_bf16, hipStream_t s) {
   const size_t words = (size_t)rows * cols / 8;
   size_t blocks = (words + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  k_dequant<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
+  if (via_bf16)
+    k_dequant_bf16<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
+  else
+    k_dequant<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
   return hipGetLastError();
 }
 

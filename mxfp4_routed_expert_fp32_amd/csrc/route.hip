@@ -254,11 +254,17 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
 
 // ---------------------------------------------------------------- counting sort
 // Stable sort of the T*k (token, rank) pairs by expert: histogram ->
-// exclusive scan -> scatter.  Within an expert the pairs are in token order:
-// each token selects an expert at most once, so a pair's place is the number
-// of earlier tokens that selected the same expert.  Tokens are taken 64 at a
-// time; a 64-bit mask per expert records which tokens of the chunk selected
-// it, and a popcount below the token's bit gives its place.
+// exclusive scan -> scatter.  Within an expert the pairs are in pair order
+// (token, then rank).  Tokens are taken 64 at a time; a 64-bit mask per
+// expert records which tokens of the chunk selected it.  When every token of
+// the chunk names each expert at most once, a pair's place is the number of
+// earlier tokens that selected the same expert (a popcount below the token's
+// bit), and the pair of the lowest such token advances the expert's cursor by
+// the mask's popcount.  A token that names one expert twice (an invalid
+// route, or two out-of-range ids that clamp to the same expert) is seen when
+// its second bit is set: atomicOr returns the bit already set.  Such a chunk
+// is placed by one thread in pair order instead, so the pair list is still a
+// permutation of the pairs and every cursor stays inside its expert's range.
 //
 // Up to kSortMultiMinTokens tokens one workgroup does everything.  Above, the
 // tokens are cut into blocks of kSortBlockTokens: each block's histogram, a
@@ -270,31 +276,46 @@ constexpr int kSortMultiMinTokens = 1024;
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
-// Scatter of tokens [t0, t1) with cursors running[E] (LDS, advanced) and
-// mask[E] (LDS, zero on entry and exit); NT threads.
+// Scatter of tokens [t0, t1) with cursors running[E] (LDS, advanced),
+// mask[E] (LDS, zero on entry and exit) and the LDS flag *dup (zero on entry
+// and exit); NT threads.
 template <int NT>
 __device__ void scatter_tokens(const int32_t* __restrict__ idx, int t0, int t1, int E, int k,
-                               unsigned long long* mask, int32_t* running, int32_t* __restrict__ pairs) {
+                               unsigned long long* mask, int32_t* running, int* dup,
+                               int32_t* __restrict__ pairs) {
   const int tid = threadIdx.x;
   for (int c0 = t0; c0 < t1; c0 += 64) {
     const int np = min(64, t1 - c0) * k;
     const int32_t* ic = idx + (size_t)c0 * k;
-    for (int p = tid; p < np; p += NT) atomicOr(&mask[clamp_expert(ic[p], E)], 1ull << (p / k));
-    __syncthreads();
     for (int p = tid; p < np; p += NT) {
-      const int e = clamp_expert(ic[p], E);
-      const unsigned long long below = mask[e] & ((1ull << (p / k)) - 1ull);
-      pairs[running[e] + __popcll(below)] = c0 * k + p;
+      const unsigned long long bit = 1ull << (p / k);
+      if (atomicOr(&mask[clamp_expert(ic[p], E)], bit) & bit) *dup = 1;
     }
     __syncthreads();
-    // the pair of the lowest token of each expert advances that expert's cursor
-    for (int p = tid; p < np; p += NT) {
-      const int e = clamp_expert(ic[p], E);
-      const unsigned long long m = mask[e];
-      if ((m & ((1ull << (p / k)) - 1ull)) == 0ull) running[e] += __popcll(m);
+    if (*dup) {  // uniform: written before the barrier above, cleared after the one below
+      if (tid == 0) {
+        for (int p = 0; p < np; ++p) {
+          const int e = clamp_expert(ic[p], E);
+          pairs[running[e]++] = c0 * k + p;
+        }
+      }
+    } else {
+      for (int p = tid; p < np; p += NT) {
+        const int e = clamp_expert(ic[p], E);
+        const unsigned long long below = mask[e] & ((1ull << (p / k)) - 1ull);
+        pairs[running[e] + __popcll(below)] = c0 * k + p;
+      }
+      __syncthreads();
+      // the pair of the lowest token of each expert advances that expert's cursor
+      for (int p = tid; p < np; p += NT) {
+        const int e = clamp_expert(ic[p], E);
+        const unsigned long long m = mask[e];
+        if ((m & ((1ull << (p / k)) - 1ull)) == 0ull) running[e] += __popcll(m);
+      }
     }
     __syncthreads();
     for (int p = tid; p < np; p += NT) mask[clamp_expert(ic[p], E)] = 0ull;
+    if (tid == 0) *dup = 0;
     __syncthreads();
   }
 }
@@ -342,7 +363,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* 
   unsigned long long* mask = sort_lds;                               // [E]
   int32_t* running = reinterpret_cast<int32_t*>(sort_lds + E);       // [E]
   __shared__ int32_t part[kSortThreads];
+  __shared__ int dup;
   const int tid = threadIdx.x;
+  if (tid == 0) dup = 0;
   for (int e = tid; e < E; e += kSortThreads) { running[e] = 0; mask[e] = 0ull; }
   __syncthreads();
   const int P = T * k;
@@ -376,7 +399,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_by_expert(const int32_t* 
     if (tid == kSortThreads - 1) *nblocks = min(part[kSortThreads - 1], max_blocks);
     __syncthreads();  // the scatter below moves the cursors
   }
-  scatter_tokens<kSortThreads>(idx, 0, T, E, k, mask, running, pairs);
+  scatter_tokens<kSortThreads>(idx, 0, T, E, k, mask, running, &dup, pairs);
 }
 
 // Many tokens, step 1: counts[b][e] = pairs of token block b that chose e.
@@ -422,13 +445,16 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
   extern __shared__ unsigned long long sort_lds[];
   unsigned long long* mask = sort_lds;                          // [E]
   int32_t* running = reinterpret_cast<int32_t*>(sort_lds + E);  // [E]
+  __shared__ int dup;
   const int b = blockIdx.x;
+  if (threadIdx.x == 0) dup = 0;
   for (int e = threadIdx.x; e < E; e += 256) {
     running[e] = offsets[e] + counts[(size_t)b * E + e];
     mask[e] = 0ull;
   }
   __syncthreads();
-  scatter_tokens<256>(idx, b * kSortBlockTokens, min(T, (b + 1) * kSortBlockTokens), E, k, mask, running, pairs);
+  scatter_tokens<256>(idx, b * kSortBlockTokens, min(T, (b + 1) * kSortBlockTokens), E, k, mask, running, &dup,
+                      pairs);
 }
 
 size_t sort_workspace_bytes(int T, int E) {

@@ -23,6 +23,28 @@ def declared_functions():
     return sorted(set(names))
 
 
+PAGE_TITLES = ("Deltafin's custom compiled runtime", "How the native runtime works", "brain.bigb.es \"deltafin\"",
+               "Tarfa EXACTNESS")
+
+
+def test_every_entry_point_cites_its_passage():
+    """Each declaration's comment (the nearest one above it) names the page and
+    section that define the operation, or says the pages do not describe it."""
+    src = open(HEADER).read()
+    body = src[src.index("#ifdef __cplusplus"):]
+    decl = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(moe_[a-z0-9_]+)\s*\(", re.M)
+    base = src.index("#ifdef __cplusplus")
+    missing = []
+    for m in decl.finditer(body):
+        pos = base + m.start()
+        end = src.rfind("*/", 0, pos)
+        start = src.rfind("/*", 0, end)
+        comment = " ".join(re.sub(r"\n\s*\*(?!/)", " ", src[start:end]).split())
+        if not (any(t in comment for t in PAGE_TITLES) or "not on the pages" in comment.lower()):
+            missing.append(m.group(1))
+    assert not missing, missing
+
+
 def test_header_and_binding_agree():
     assert declared_functions() == sorted(moe.EXPORTS)
 
@@ -117,6 +139,9 @@ def test_other_entry_points_reject_before_launch():
     assert L.moe_mxfp4_pack(ctypes.byref(d), 8, 16, 0, 1, 16, 16, None) == -4
     assert L.moe_mxfp4_dequant(ctypes.byref(d), 16, 16, 896, 0, 16, None) == -11
     assert L.moe_mxfp4_dequant(ctypes.byref(d), 16, 16, 0, 3, 16, None) == -11
+    assert L.moe_mxfp4_dequant_bf16(ctypes.byref(d), 16, 16, 896, 0, 16, None) == -11
+    assert L.moe_mxfp4_dequant_bf16(ctypes.byref(d), 16, 16, 0, 0, 8, None) == -4
+    assert L.moe_mxfp4_dequant_bf16(ctypes.byref(d), None, 16, 0, 0, 16, None) == -1
     assert L.moe_topk_softmax(16, 1, 896, 65, 16, 16, None) == -2
     assert L.moe_topk_softmax(16, 1, 8, 9, 16, 16, None) == -2
     assert L.moe_topk_softmax(16, 1, 5000, 4, 16, 16, None) == -7

@@ -27,9 +27,19 @@ def k3_layer():
 
 
 def oracle_tokens(w, xf, wr_h, logits, k, bias=None, layer=0):
+    """Oracle on the GPU's logits; returns (out, idx, w, experts) with only the
+    selected experts regenerated."""
     sel = sorted(set(np.unique(oracle.topk(logits, k)).tolist()))
     ex = {e: synth.expert(w, e, layer) for e in sel}
-    return oracle.moe_forward(xf, wr_h, ex, w.H, w.I, k, bias=bias, logits_override=logits)
+    out, _, idx, wt = oracle.moe_forward(xf, wr_h, ex, w.H, w.I, k, bias=bias, logits_override=logits)
+    return out, idx, wt, ex
+
+
+def check_tokens(w, out, idx, wt, logits, xf, wr_h, bias=None, layer=0):
+    r_out, r_idx, r_w, ex = oracle_tokens(w, xf, wr_h, logits, w.k, bias=bias, layer=layer)
+    assert np.array_equal(idx, r_idx)
+    P.assert_weights_close(wt, r_w, w.k)
+    return P.assert_layer_close(out, r_out, xf, r_idx, r_w, ex, w.H, w.I, w.E)
 
 
 def forward(desc, x, wr, bias, codes, scales, k, E, H):
@@ -67,13 +77,12 @@ def test_decode_one_token(k3_layer, token):
     xf = synth.tokens_f32(w, [token])
     wr_h = wr.cpu().numpy()
     P.assert_logits_close(logits, oracle.router_logits(xf, wr_h), xf, wr_h)
-    r_out, _, r_idx, r_w = oracle_tokens(w, xf, wr_h, logits, w.k)
-    assert np.array_equal(idx, r_idx)
-    P.assert_weights_close(wt, r_w, w.k)
-    P.assert_out_close(out, r_out)
+    check_tokens(w, out, idx, wt, logits, xf, wr_h)
 
 
-def test_decode64_zipf_sampled(k3_layer):
+def test_decode64_zipf_all_tokens(k3_layer):
+    """64 tokens with Zipf(1.1) router bias: every token (and so every pair of
+    the three hottest experts, which every token selects) against the oracle."""
     w0, codes, scales, wr = k3_layer
     w = synth.WORKLOADS["decode64_zipf"]
     desc = sd.desc_for(w)
@@ -82,17 +91,47 @@ def test_decode64_zipf_sampled(k3_layer):
     out, logits, idx, wt = forward(desc, x, wr, bias, codes, scales, w.k, w.E, w.H)
     union = len(np.unique(idx))
     assert 150 < union < 600, union  # skewed, but a large union
+    counts = np.bincount(idx.reshape(-1), minlength=w.E)
+    assert np.sort(counts)[-3:].min() == w.T  # the three hottest experts take every token
     assert np.array_equal(idx, oracle.topk(logits, w.k))
-    sample = [0, 17, 63]
-    xf = synth.tokens_f32(w, sample)
-    r_out, _, r_idx, r_w = oracle_tokens(w, xf, wr.cpu().numpy(), logits[sample], w.k,
-                                          bias=bias.cpu().numpy())
-    assert np.array_equal(idx[sample], r_idx)
-    P.assert_weights_close(wt[sample], r_w, w.k)
-    P.assert_out_close(out[sample], r_out)
+    xf = synth.tokens_f32(w, range(w.T))
+    wr_h = wr.cpu().numpy()
+    b_h = bias.cpu().numpy()
+    P.assert_logits_close(logits, oracle.router_logits(xf, wr_h, bias=b_h), xf, wr_h, bias=b_h)
+    check_tokens(w, out, idx, wt, logits, xf, wr_h, bias=b_h)
 
 
-def test_prefill4096_sampled(k3_layer):
+def block_sample(idx, E, per_count=2, seed=0):
+    """Tokens whose pairs are the first and last pair of the prefill form's
+    128-pair expert blocks, for blocks of every m-tile count (16 pairs per
+    m-tile) the routing produces, preferring ragged ones (a partial last
+    m-tile), plus both ends of the batch and a few random tokens."""
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    by_tiles = {}
+    for e in range(E):
+        for m0 in range(offs[e], offs[e + 1], 128):
+            n = min(128, offs[e + 1] - m0)
+            tiles = (n + 15) // 16
+            by_tiles.setdefault(tiles, []).append((n % 16 != 0, e, m0, n))
+    toks = {0, 1, T - 1}
+    for tiles, blocks in sorted(by_tiles.items()):
+        blocks.sort(key=lambda b: (not b[0], b[1]))     # ragged blocks first
+        for _, e, m0, n in blocks[:per_count]:
+            toks.add(int(order[m0]) // k)
+            toks.add(int(order[m0 + n - 1]) // k)
+    rng = np.random.default_rng(seed)
+    toks.update(int(t) for t in rng.integers(0, T, 6))
+    return sorted(toks), sorted(by_tiles)
+
+
+def test_prefill4096_block_sample(k3_layer):
+    """4096 tokens, uniform routing: tokens covering the first and last pair
+    of expert blocks of every m-tile count the routing gives (ragged last
+    m-tiles preferred), checked against the oracle."""
     w0, codes, scales, wr = k3_layer
     w = synth.WORKLOADS["prefill4096"]
     desc = sd.desc_for(w)
@@ -101,13 +140,15 @@ def test_prefill4096_sampled(k3_layer):
     counts = np.bincount(idx.reshape(-1), minlength=w.E)
     assert counts.min() > 20 and counts.max() < 160  # near-uniform routing
     assert np.array_equal(idx, oracle.topk(logits, w.k))
-    sample = [0, 1, 2047, 4095]
+    sample, tiles = block_sample(idx, w.E, per_count=3)
+    # uniform routing gives every expert 47-102 pairs here: one block each, of
+    # 3-7 m-tiles (blocks of 8 m-tiles and the small second blocks of hot
+    # experts are covered by the small-shape prefill tests)
+    assert len(sample) >= 32 and set(range(3, 8)) <= set(tiles), (len(sample), tiles)
     xf = synth.tokens_f32(w, sample)
     wr_h = wr.cpu().numpy()
     P.assert_logits_close(logits[sample], oracle.router_logits(xf, wr_h), xf, wr_h)
-    r_out, _, r_idx, r_w = oracle_tokens(w, xf, wr_h, logits[sample], w.k)
-    assert np.array_equal(idx[sample], r_idx)
-    P.assert_out_close(out[sample], r_out)
+    check_tokens(w, out[sample], idx[sample], wt[sample], logits[sample], xf, wr_h)
     # every token is finite and tokens are independent of their batch: a token
     # alone gives the same top-k as inside the batch
     assert np.all(np.isfinite(out))
@@ -116,35 +157,65 @@ def test_prefill4096_sampled(k3_layer):
     P.assert_out_close(o1, out[4095:4096], tol=2e-5)
 
 
-def test_stack_two_layers_graph_and_eager(k3_layer):
-    """Two pre-norm layers at full shape: eager stack vs oracle layer by layer,
-    and graph replays bit-identical to the eager result."""
+def stack_layer_by_layer(w, desc, layers, gam, x, T, eps, k):
+    """Runs the stack on the GPU with 1, 2, ..., L layers and checks layer l
+    against the oracle started from the GPU's own residual after layer l - 1:
+    the oracle normalises it, takes the GPU's router logits of those rows for
+    selection (moe_rmsnorm + moe_router_logits give the stack kernel's bits),
+    runs the layer and adds the residual.  Returns the worst (normwise,
+    elementwise) errors and the GPU residual after the last layer."""
+    L = len(layers)
+    ws = torch.empty(moe.stack_workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
+    resid = torch.empty(T, w.H, dtype=torch.float32, device=DEV)
+    if x.dtype == torch.bfloat16:    # the stack starts from x widened exactly
+        r_prev = synth.bf16_bits_to_f32(x.view(torch.int16).cpu().numpy().view(np.uint16))
+    else:
+        r_prev = x.cpu().numpy()
+    worst = (0.0, 0.0)
+    for l in range(L):
+        moe.moe_mxfp4_stack_forward(desc, [a[0] for a in layers[:l + 1]], [a[1] for a in layers[:l + 1]],
+                                    [a[2] for a in layers[:l + 1]], None, gam[:l + 1], eps, x, k, resid, ws)
+        torch.cuda.synchronize()
+        r_gpu = resid.cpu().numpy().copy()
+        n = oracle.rmsnorm(r_prev, gam[l].cpu().numpy(), eps)
+        rp = torch.from_numpy(r_prev).to(DEV)
+        nd = torch.empty_like(rp)
+        moe.moe_rmsnorm(rp, gam[l], eps, nd)
+        lg = torch.empty(T, w.E, dtype=torch.float32, device=DEV)
+        moe.moe_router_logits(desc, nd, layers[l][2], None, lg)
+        torch.cuda.synchronize()
+        lg = lg.cpu().numpy()
+        sel = np.unique(oracle.topk(lg, k))
+        ex = {int(e): synth.expert(w, int(e), l) for e in sel}
+        o, _, r_idx, r_w = oracle.moe_forward(n, layers[l][2].cpu().numpy(), ex, w.H, w.I, k, logits_override=lg)
+        r_ref = oracle.residual_add(r_prev, o)
+        nw = P.assert_out_close(r_gpu, r_ref)
+        # the residual add rounds once on each side, on the same r_prev
+        A = oracle.moe_abs_scale(n, r_idx, r_w, ex, w.H, w.I, w.E) + 2.0 ** -23 * np.abs(r_ref) / P.OUT_TOL
+        ew = P.assert_elementwise(r_gpu, r_ref, A)
+        worst = (max(worst[0], nw), max(worst[1], ew))
+        r_prev = r_gpu
+    return worst, r_prev
+
+
+def test_stack_twelve_layers_layer_by_layer(k3_layer):
+    """The full 12-layer stack at the model shape (188.7 GB resident), one
+    token: every layer checked against the oracle from the GPU's residual
+    before it, and graph replays bit-identical to the eager stack."""
     w0, codes0, scales0, wr0 = k3_layer
     w = synth.WORKLOADS["stack12"]
-    codes1, scales1 = sd.upload_layer(w, 1)
-    layers = [(codes0, scales0, wr0), (codes1, scales1, sd.router_w(w, 1))]
-    gam = [sd.gamma(w, l) for l in range(2)]
     desc = sd.desc_for(w)
+    layers = [(codes0, scales0, wr0)]
+    for l in range(1, w.layers):
+        c, s = sd.upload_layer(w, l)
+        layers.append((c, s, sd.router_w(w, l)))
+    gam = [sd.gamma(w, l) for l in range(w.layers)]
     x = sd.tokens(w, [3])
+    worst, eager = stack_layer_by_layer(w, desc, layers, gam, x, 1, w.eps, w.k)
+    print("stack12 layer-by-layer worst normwise %.3g elementwise %.3g" % worst)
     resid = torch.empty(1, w.H, dtype=torch.float32, device=DEV)
     ws = torch.empty(moe.stack_workspace_bytes(desc, 1, w.k), dtype=torch.uint8, device=DEV)
     args = ([l[0] for l in layers], [l[1] for l in layers], [l[2] for l in layers], None, gam, w.eps)
-    moe.moe_mxfp4_stack_forward(desc, *args, x, w.k, resid, ws)
-    torch.cuda.synchronize()
-    eager = resid.cpu().numpy().copy()
-    # oracle, layer by layer, on the GPU's logits for each layer
-    r = synth.tokens_f32(w, [3])
-    for l in range(2):
-        n = oracle.rmsnorm(r, gam[l].cpu().numpy(), w.eps)
-        lg = torch.empty(1, w.E, dtype=torch.float32, device=DEV)
-        moe.moe_router_logits(desc, torch.from_numpy(n).to(DEV), layers[l][2], None, lg)
-        torch.cuda.synchronize()
-        lg = lg.cpu().numpy()
-        sel = np.unique(oracle.topk(lg, w.k))
-        ex = {int(e): synth.expert(w, int(e), l) for e in sel}
-        o, *_ = oracle.moe_forward(n, layers[l][2].cpu().numpy(), ex, w.H, w.I, w.k, logits_override=lg)
-        r = oracle.residual_add(r, o)
-    P.assert_out_close(eager, r)
     g = moe.StackGraph(desc, *args, x, w.k, resid, ws)
     for _ in range(3):
         resid.fill_(0.0)
@@ -153,4 +224,5 @@ def test_stack_two_layers_graph_and_eager(k3_layer):
         torch.cuda.synchronize()
         assert np.array_equal(P.bits(resid.cpu().numpy()), P.bits(eager))
     g.close()
-    del codes1, scales1
+    del layers
+    torch.cuda.empty_cache()

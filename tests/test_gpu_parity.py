@@ -75,6 +75,20 @@ def test_dequant_enumeration_bitexact():
         mcb, msb = rows * cols // 2, rows * cols // 32
         ref = oracle.dequant(c[m * mc:m * mc + mcb], s[m * (w.I * w.H // 32):m * (w.I * w.H // 32) + msb], rows, cols)
         assert np.array_equal(P.bits(out.cpu().numpy()), P.bits(ref)), "matrix %d" % m
+        assert_bf16_export_equals(desc, codes, scales, 0, m, ref)
+
+
+def assert_bf16_export_equals(desc, codes, scales, e, m, ref):
+    """The bf16-conversion export (the decode of the bf16 GEMV and both MFMA
+    kernels) equals the oracle bit for bit wherever the oracle is not NaN, and
+    is NaN exactly where the oracle is."""
+    out = torch.empty(ref.shape, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_dequant_bf16(desc, codes, scales, e, m, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), (e, m)
+    assert np.array_equal(P.bits(got)[~nan], P.bits(ref)[~nan]), (e, m)
 
 
 def test_dequant_real_shape_bitexact():
@@ -95,6 +109,7 @@ def test_dequant_real_shape_bitexact():
             mc, ms = w.I * w.H // 2, w.I * w.H // 32
             ref = oracle.dequant(ce_[m * mc:(m + 1) * mc], se_[m * ms:(m + 1) * ms], rows, cols)
             assert np.array_equal(P.bits(out.cpu().numpy()), P.bits(ref)), (e, m)
+            assert_bf16_export_equals(desc, codes, scales, e, m, ref)
 
 
 # ------------------------------------------------------------------ routing
@@ -210,6 +225,36 @@ def test_sort_by_expert_matches_stable_sort():
         assert np.array_equal(offs.cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
 
 
+@pytest.mark.parametrize("T,E,k", [(70, 40, 4), (130, 896, 16), (1100, 40, 4), (2048, 896, 16)])
+def test_sort_repeated_and_out_of_range_ids(T, E, k):
+    """Ids outside [0, E) are clamped into it and a row may name an expert
+    twice; on both sort paths (one workgroup below 1024 tokens, blocks of 256
+    above) the pair list is still numpy's stable argsort of the clamped ids (a
+    permutation of the pairs), the offsets are their counts, and the words
+    past the end of both outputs are untouched."""
+    rng = np.random.default_rng(T + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    for t in rng.integers(0, T, max(4, T // 16)):
+        j0, j1 = rng.integers(0, k, 2)
+        idx[t, j1] = idx[t, j0]                   # a repeated id
+    for t in rng.integers(0, T, max(4, T // 16)):
+        idx[t, rng.integers(0, k)] = rng.choice([E, E + 7, -1, -100])
+    idx[63, :2] = [E - 1, E + 2]                  # two ids that clamp to one expert, at a chunk's last token
+    idx[64, :] = -3                               # a whole row clamped to expert 0
+    guard = 64
+    offs = torch.full((E + 1 + guard,), -7, dtype=torch.int32, device=DEV)
+    pairs = torch.full((T * k + guard,), -7, dtype=torch.int32, device=DEV)
+    nws = moe.sort_workspace_bytes(E, T, k)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    moe.moe_sort_by_expert(torch.from_numpy(idx).to(DEV), E, offs[:E + 1], pairs[:T * k], ws)
+    torch.cuda.synchronize()
+    flat = np.clip(idx.reshape(-1), 0, E - 1)
+    p_h, o_h = pairs.cpu().numpy(), offs.cpu().numpy()
+    assert np.array_equal(p_h[:T * k], np.argsort(flat, kind="stable").astype(np.int32))
+    assert np.array_equal(o_h[:E + 1], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert np.all(p_h[T * k:] == -7) and np.all(o_h[E + 1:] == -7)
+
+
 # ------------------------------------------------------------------ whole layer, small shapes
 
 def oracle_layer(x_f32, wr, ex, H, I, k, bias, logits_gpu):
@@ -231,7 +276,7 @@ def test_forward_tiny_matches_oracle(seed):
     r_out, _, r_idx, r_w = oracle_layer(xf, wr_h, ex, w.H, w.I, w.k, None, logits)
     assert np.array_equal(idx, r_idx)
     P.assert_weights_close(wt, r_w, w.k)
-    P.assert_out_close(out, r_out)
+    P.assert_layer_close(out, r_out, xf, r_idx, r_w, ex, w.H, w.I, w.E)
 
 
 @pytest.mark.parametrize("H,I,E,k,T,xd", [(256, 128, 8, 2, 4, "f32"), (96, 64, 16, 4, 3, "bf16"),
@@ -262,35 +307,64 @@ def test_forward_small_shapes_matches_oracle(H, I, E, k, T, xd):
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, bias.cpu().numpy(), logits)
     assert np.array_equal(idx, r_idx)
     P.assert_weights_close(wt, r_w, k)
-    P.assert_out_close(out, r_out)
+    P.assert_layer_close(out, r_out, xf, r_idx, r_w, ex, H, I, E)
 
 
-def test_experts_entry_with_given_routing():
-    """Expert part on constructed routes: every token on the same experts, reversed rank order."""
-    w = synth.Workload("r", 61, 5, 256, 128, 8, 3, "f32", weight_seed=7300)
+@pytest.mark.parametrize("T,xd", [(5, "f32"), (1, "bf16"), (5, "bf16")])
+def test_experts_entry_with_given_routing(T, xd):
+    """Expert part on constructed routes (every token on the same experts,
+    reversed rank order in one row) on the decode forms (fp32 x; one bf16
+    token) and the prefill form (several bf16 tokens, H and I multiples of
+    256), against the oracle's given-routing entry with the same weights."""
+    w = synth.Workload("r", 61, T, 512, 256, 8, 3, xd, weight_seed=7300)
     c, s, ex = experts_host(w)
     desc, codes, scales = pack_whole(w, c, s)
-    T, k = 5, 3
+    k = 3
     x = sd.tokens(w, range(T))
     idx = np.array([[7, 0, 3]] * T, np.int32)
-    idx[1] = [0, 3, 7]
+    idx[T // 2] = [0, 3, 7]
     wts = np.array([[0.5, 0.25, 0.25]] * T, np.float32)
+    wts[0] = [0.125, 0.625, 0.25]
     out = torch.empty(T, w.H, dtype=torch.float32, device=DEV)
     ws = torch.empty(moe.workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
     moe.moe_mxfp4_experts(desc, x, torch.from_numpy(idx).to(DEV), torch.from_numpy(wts).to(DEV), codes, scales,
                           k, out, ws)
     torch.cuda.synchronize()
     xf = synth.tokens_f32(w, range(T))
-    # oracle with logits that select exactly these experts in this order and give these weights
-    lo = np.full((T, w.E), -np.inf, np.float32)
-    for t in range(T):
-        for j in range(k):
-            lo[t, idx[t, j]] = np.log(wts[t, j]) - j * 1e-7
-    r_out, _, r_idx, r_w = oracle.moe_forward(xf, np.zeros((w.E, w.H), np.float32), ex, w.H, w.I, k,
-                                              logits_override=lo)
-    assert np.array_equal(r_idx, idx)
-    # oracle weights equal the given ones to ~1 ulp; compare outputs normwise
-    P.assert_out_close(out.cpu().numpy(), r_out, tol=1e-4)
+    r_out = oracle.moe_experts(xf, idx, wts, ex, w.H, w.I, w.E)
+    P.assert_layer_close(out.cpu().numpy(), r_out, xf, idx, wts, ex, w.H, w.I, w.E)
+
+
+@pytest.mark.parametrize("T,xd", [(6, "f32"), (70, "bf16"), (1100, "bf16")])
+def test_experts_entry_repeated_and_out_of_range_ids(T, xd):
+    """Routes that name one expert twice in a row, or ids outside [0, E) (which
+    are clamped into it), on the decode form (fp32 x) and the prefill form
+    (bf16 x; 70 tokens sort in one workgroup, 1100 tokens in blocks of 256):
+    the output is the layer on the clamped routes, pair for pair."""
+    H, I, E, k = 256, 256, 6, 3
+    w = synth.Workload("dup", 71, T, H, I, E, k, xd, weight_seed=8200 + T)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[0] = [2, 2, 5]                 # a repeated id
+    idx[1] = [E + 3, -4, E - 1]        # out of range both ways; E + 3 clamps onto E - 1
+    idx[T - 1] = [1, 1, 1]
+    if T > 64:
+        idx[63] = [4, -1, 4]
+        idx[64] = [0, 0, E]
+    wts = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    x = sd.tokens(w, range(T))
+    out = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe.workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
+    moe.moe_mxfp4_experts(desc, x, torch.from_numpy(idx).to(DEV), torch.from_numpy(wts).to(DEV), codes, scales,
+                          k, out, ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, T - 1, np.arange(max(0, min(T, 70) - 8), min(T, 70)), rng.integers(0, T, 8)])
+    xf = synth.tokens_f32(w, rows)
+    cl = np.clip(idx[rows], 0, E - 1)
+    r_out = oracle.moe_experts(xf, cl, wts[rows], ex, H, I, E)
+    P.assert_layer_close(out.cpu().numpy()[rows], r_out, xf, cl, wts[rows], ex, H, I, E)
 
 
 def test_forward_is_deterministic():
@@ -356,7 +430,7 @@ def test_prefill_grouped_gemm_matches_oracle(H, I, E, k, T, hot):
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, b, logits)
     assert np.array_equal(idx, r_idx)
     P.assert_weights_close(wt, r_w, k)
-    err = P.assert_out_close(out, r_out)
+    err, _ = P.assert_layer_close(out, r_out, xf, r_idx, r_w, ex, H, I, E)
     assert err < 1e-5, err
 
 
@@ -387,7 +461,7 @@ def test_prefill_token_batches_equal_separate_calls():
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, None, logits[rows])
     assert np.array_equal(idx[rows], r_idx)
     P.assert_weights_close(wt[rows], r_w, k)
-    P.assert_out_close(out[rows], r_out)
+    P.assert_layer_close(out[rows], r_out, xf, r_idx, r_w, ex, H, I, E)
 
 
 def test_forward_max_tokens_sampled():
@@ -408,7 +482,7 @@ def test_forward_max_tokens_sampled():
     r_out, _, r_idx, r_w = oracle_layer(xf, wr.cpu().numpy(), ex, H, I, k, None, logits[rows])
     assert np.array_equal(idx[rows], r_idx)
     P.assert_weights_close(wt[rows], r_w, k)
-    P.assert_out_close(out[rows], r_out)
+    P.assert_layer_close(out[rows], r_out, xf, r_idx, r_w, ex, H, I, E)
 
 
 @pytest.mark.parametrize("H,I,E,k,T", [(512, 256, 16, 4, 3), (256, 128, 100, 3, 5), (1024, 256, 8, 2, 1),
@@ -496,3 +570,139 @@ def test_grouped_stages_equal_forward_and_skip_malformed_blocks():
     moe.moe_mxfp4_grouped_down(desc, hterm, pairs, bad, nbad, codes, scales, y2)
     torch.cuda.synchronize()
     assert bool((y2 == 7.0).all()) and bool((h2 == 3.0).all())
+
+
+# ------------------------------------------------------------------ extreme scale bytes through the forward
+
+def hostile_layer():
+    """A layer whose routed experts carry extreme E8M0 scale bytes.
+
+    Expert 1 (every token selects it, through its bias):
+      - gate/up blocks with scale bytes 0 and 1 (subnormal weights);
+      - gate row 6, block 3: scale 253 with codes of magnitude <= 1.5 (finite
+        weights near 2^126);
+      - down row 10, block 0: scale 255 (NaN), so output column 10 is NaN;
+      - down row 11, block 1: scale 254 with one code 2.0 (+inf weight);
+      - down row 12, block 2: scale 253 with one code 4.0 and one -4.0 (+inf
+        and -inf weights);
+      - down row 13, block 3: scale 253 with codes of magnitude <= 1.5.
+    Expert 5 (only token 2 selects it, through x[2][0]): gate row 0, block 0
+    has scale 255, so every h of that pair, and token 2's whole output, is NaN.
+    Activations are N(0,1) * 2^-20 (exact in bf16), so no finite sum comes near
+    the fp32 overflow threshold and every non-finite output is fixed by the
+    weights alone, whatever the summation order."""
+    H, I, E, k, T = 512, 256, 8, 2, 5
+    w = synth.Workload("hs", 69, T, H, I, E, k, "bf16", weight_seed=8100)
+    c, s, _ = experts_host(w)
+    ce, se = w.code_bytes_per_expert, w.scale_bytes_per_expert
+    mc, ms = I * H // 2, I * H // 32
+
+    def blk(e, m, row, b, cols):  # (first code byte, scale byte) of block b of a row
+        return e * ce + m * mc + row * (cols // 2) + 16 * b, e * se + m * ms + row * (cols // 32) + b
+
+    def set_scale(e, m, row, b, cols, v, codes=None, small=False):
+        cb, sb = blk(e, m, row, b, cols)
+        s[sb] = v
+        if small:
+            c[cb:cb + 16] &= 0xBB            # clear bit 2 of both nibbles: |value| <= 1.5
+        if codes is not None:
+            c[cb:cb + 16] = 0
+            for col, code in codes:          # col within the block
+                c[cb + col // 2] |= np.uint8(code << (4 * (col & 1)))
+
+    set_scale(1, 0, 3, 0, H, 0)
+    set_scale(1, 0, 4, 1, H, 1)
+    set_scale(1, 1, 5, 2, H, 0)
+    set_scale(1, 1, 7, 3, H, 1)
+    set_scale(1, 0, 6, 3, H, 253, small=True)
+    set_scale(1, 2, 10, 0, I, 255)
+    set_scale(1, 2, 11, 1, I, 254, codes=[(8, 4)])             # +2.0 * 2^127 = +inf
+    set_scale(1, 2, 12, 2, I, 253, codes=[(6, 6), (11, 14)])   # +4.0 and -4.0 times 2^126
+    set_scale(1, 2, 13, 3, I, 253, small=True)
+    set_scale(5, 0, 0, 0, H, 255)
+    ex = [(c[e * ce:(e + 1) * ce], s[e * se:(e + 1) * se]) for e in range(E)]
+    x = synth.tokens_f32(w, range(T)) * np.float32(2.0 ** -20)
+    x[:, 0] = 0.0
+    x[2, 0] = 2.0 ** -10
+    wr = synth.router_w(w)
+    wr[:, 0] = 0.0
+    wr[5, :] = 0.0
+    wr[5, 0] = 1.0                           # logit_5 = x[t][0]: 2^-10 for token 2, 0 otherwise
+    b = np.full(E, 1e-4, np.float32)         # the other logits are about 1e-4 +- 1e-6
+    b[1], b[5] = 8.0, 0.0
+    return w, c, s, ex, x, wr, b
+
+
+@pytest.mark.parametrize("form", ["decode_bf16", "decode_f32", "prefill_mfma"])
+def test_forward_extreme_scale_bytes(form):
+    """Scale bytes 0, 1, 253, 254 and 255 in selected experts, through each
+    kernel form of the forward: NaN and +-inf land where the oracle puts them
+    and every finite element meets both readings of the output bar.  The
+    decode forms multiply h in fp32, so every element's class matches exactly.
+    The prefill form feeds h to the bf16 matrix cores as two terms (hi + lo);
+    an infinite weight times a zero or opposite-signed lo term is NaN, so there
+    an element the oracle gives as +-inf may come out NaN (never finite, never
+    the other sign)."""
+    w, c, s, ex, x, wr, b = hostile_layer()
+    desc, codes, scales = pack_whole(w, c, s)
+    wr_d, b_d = torch.from_numpy(wr).to(DEV), torch.from_numpy(b).to(DEV)
+    xb_bits = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(xb_bits), x)    # x is exact in bf16
+    xb = torch.from_numpy(xb_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    if form == "decode_bf16":   # one token per call
+        parts = [run_forward(desc, w, xb[t:t + 1], wr_d, b_d, codes, scales, w.k) for t in range(w.T)]
+        out, logits, idx, wt = (np.concatenate([p[i] for p in parts]) for i in range(4))
+    elif form == "decode_f32":
+        out, logits, idx, wt = run_forward(desc, w, torch.from_numpy(x).to(DEV), wr_d, b_d, codes, scales, w.k)
+    else:
+        out, logits, idx, wt = run_forward(desc, w, xb, wr_d, b_d, codes, scales, w.k)
+    r_out, _, r_idx, r_w = oracle.moe_forward(x, wr, ex, w.H, w.I, w.k, bias=b, logits_override=logits)
+    assert np.array_equal(idx, r_idx)
+    assert np.all(idx[:, 0] == 1) and idx[2, 1] == 5 and np.all(np.delete(idx[:, 1], 2) != 5)
+    assert np.all(np.isnan(r_out[2])) and np.all(np.isnan(out[2]))
+    assert np.all(np.isnan(r_out[:, 10])) and np.any(np.isinf(r_out[:, 11:13]))
+    fin = np.isfinite(r_out)
+    assert np.array_equal(np.isfinite(out), fin)
+    assert np.all(np.isnan(out[np.isnan(r_out)]))
+    inf = np.isinf(r_out)
+    if form == "prefill_mfma":
+        same = (out[inf] == r_out[inf]) | np.isnan(out[inf])
+        assert np.all(same)
+    else:
+        assert np.array_equal(P.bits(out[inf]), P.bits(r_out[inf]))
+    A = oracle.moe_abs_scale(x, r_idx, r_w, ex, w.H, w.I, w.E)
+    for t in range(w.T):
+        f = fin[t]
+        if f.any():
+            P.assert_out_close(out[t][f][None], r_out[t][f][None])
+            P.assert_elementwise(out[t][f], r_out[t][f], A[t][f])
+
+
+def test_down_stage_wide_inter_many_pairs():
+    """The decode-form down projection (K split across I/512 waves) with many
+    pairs at the widest row of partial sums: H = 7168, I = 4096, 2048 pairs.
+    The grid target alone would give each workgroup all 7168 rows (7168 * 8
+    partials, over the LDS a workgroup may have); the rows are capped and split
+    into more workgroups.  Sampled pairs against the oracle's dequantised
+    matrix in fp64."""
+    H, I, E, P_ = 7168, 4096, 3, 2048
+    w = synth.Workload("wd", 72, 1, H, I, E, 1, "f32", weight_seed=8300)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    rng = np.random.default_rng(17)
+    pe = rng.integers(0, E, P_).astype(np.int32)
+    h = (rng.standard_normal((P_, I)) * 0.01).astype(np.float32)
+    y = torch.empty(P_, H, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_down(desc, torch.from_numpy(h).to(DEV), torch.from_numpy(pe).to(DEV), codes, scales, y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    mc, ms = I * H // 2, I * H // 32
+    for e in range(E):
+        rows = np.nonzero(pe == e)[0]
+        rows = np.unique(np.r_[rows[:2], rows[-2:], rng.choice(rows, 2)])
+        wd = oracle.dequant(ex[e][0][2 * mc:], ex[e][1][2 * ms:], H, I).astype(np.float64)
+        ref = h[rows].astype(np.float64) @ wd.T
+        A = np.abs(h[rows]).astype(np.float64) @ np.abs(wd).T
+        P.assert_out_close(got[rows], ref)
+        P.assert_elementwise(got[rows], ref, A)
