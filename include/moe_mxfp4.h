@@ -70,7 +70,8 @@ typedef enum moe_status {
     MOE_ERR_OVERFLOW = -8,    /* a byte count does not fit in 64 bits / the index types */
     MOE_ERR_DEVICE = -9,      /* a HIP call or kernel launch failed */
     MOE_ERR_ABI = -10,        /* descriptor abi_version / struct_size mismatch */
-    MOE_ERR_RANGE = -11       /* an index argument (expert, matrix) is out of range */
+    MOE_ERR_RANGE = -11,      /* an index argument (expert, matrix) is out of range */
+    MOE_ERR_SCRATCH_LIMIT = -12 /* moe_mxfp4_forward_noalloc: the call needs more than its static scratch */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -185,6 +186,28 @@ moe_status moe_mxfp4_forward(const moe_layer_desc* desc, const void* x, moe_dtyp
                              const void* packed_scales, int32_t n_tokens, int32_t k, float* out,
                              float* logits_out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * The whole layer as moe_mxfp4_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): there is no workspace argument.  The workspace
+ * lives in a static device array of the library, 64 MiB (67,108,864 bytes),
+ * one per GPU, which each GPU the library runs on holds until the process
+ * ends; a call uses the array of the current device (stream must belong to
+ * it).  A call whose moe_workspace_bytes(desc, n_tokens, k) exceeds 64 MiB
+ * returns MOE_ERR_SCRATCH_LIMIT and enqueues nothing (at the K3 shape,
+ * H = 7168, I = 1536, E = 896, k = 16, that admits up to 101 tokens).  The
+ * array keeps the last call's contents; the forward needs none of it cleared.
+ * Calls that overlap on one GPU (on different streams, or from different
+ * threads, without ordering between them) race on the array and give
+ * undefined output.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress); no call allocates or frees device memory.
+ * Same arguments, outputs and other errors as moe_mxfp4_forward.
+ */
+moe_status moe_mxfp4_forward_noalloc(const moe_layer_desc* desc, const void* x, moe_dtype x_dtype,
+                                     const float* router_w, const float* router_bias, const void* packed_codes,
+                                     const void* packed_scales, int32_t n_tokens, int32_t k, float* out,
+                                     float* logits_out, int32_t* topk_idx_out, float* topk_w_out, void* stream);
 
 /*
  * The expert part of the layer with the routing given ("Deltafin's custom

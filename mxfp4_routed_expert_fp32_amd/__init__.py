@@ -21,12 +21,12 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 STATUS = {
     0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_ALIGN",
     -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_LAYOUT", -7: "MOE_ERR_UNSUPPORTED", -8: "MOE_ERR_OVERFLOW",
-    -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_ABI", -11: "MOE_ERR_RANGE",
+    -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_ABI", -11: "MOE_ERR_RANGE", -12: "MOE_ERR_SCRATCH_LIMIT",
 }
 
 EXPORTS = [
     "moe_abi_version", "moe_status_string", "moe_layer_check", "moe_mxfp4_packed_bytes",
-    "moe_workspace_bytes", "moe_mxfp4_pack", "moe_mxfp4_forward", "moe_mxfp4_experts",
+    "moe_workspace_bytes", "moe_mxfp4_pack", "moe_mxfp4_forward", "moe_mxfp4_forward_noalloc", "moe_mxfp4_experts",
     "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_combine",
     "moe_router_logits", "moe_topk_softmax", "moe_sort_workspace_bytes", "moe_sort_by_expert",
     "moe_max_expert_blocks", "moe_expert_blocks", "moe_mxfp4_grouped_gate_up", "moe_mxfp4_grouped_down",
@@ -78,6 +78,8 @@ def lib():
                 "moe_mxfp4_pack": ([D, vp, vp, i64, i64, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_forward": ([D, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp],
                                       ctypes.c_int),
+                "moe_mxfp4_forward_noalloc": ([D, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp],
+                                              ctypes.c_int),
                 "moe_mxfp4_experts": ([D, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
                 "moe_mxfp4_gate_up": ([D, vp, i32, vp, i32, i32, vp, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_down": ([D, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
@@ -179,6 +181,14 @@ def moe_mxfp4_forward(desc, x, router_w, router_bias, packed_codes, packed_scale
         ctypes.byref(desc), _ptr(x), _xdtype(x), _ptr(router_w), _ptr(router_bias), _ptr(packed_codes),
         _ptr(packed_scales), x.shape[0], k, _ptr(out), _ptr(logits_out), _ptr(topk_idx_out),
         _ptr(topk_w_out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_mxfp4_forward_noalloc(desc, x, router_w, router_bias, packed_codes, packed_scales, k, out,
+                              logits_out=None, topk_idx_out=None, topk_w_out=None, stream=None):
+    _check("moe_mxfp4_forward_noalloc", lib().moe_mxfp4_forward_noalloc(
+        ctypes.byref(desc), _ptr(x), _xdtype(x), _ptr(router_w), _ptr(router_bias), _ptr(packed_codes),
+        _ptr(packed_scales), x.shape[0], k, _ptr(out), _ptr(logits_out), _ptr(topk_idx_out),
+        _ptr(topk_w_out), _stream(stream)))
 
 
 def moe_mxfp4_experts(desc, x, topk_idx, topk_w, packed_codes, packed_scales, k, out, workspace,

@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "moe_mxfp4.h"
@@ -194,18 +195,52 @@ moe_status run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const
   return MOE_OK;
 }
 
-moe_status check_forward_args(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const void* codes,
-                       const void* scales, int32_t T, int32_t k, const float* out, const void* ws,
-                       size_t ws_bytes, FwdLayout* L) {
+// Checks of a forward / experts call except its workspace; fills the layout.
+moe_status check_forward_core(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const void* codes,
+                              const void* scales, int32_t T, int32_t k, const float* out, FwdLayout* L) {
   MOE_TRY(check_desc(d));
   if (!x || !codes || !scales || !out) return MOE_ERR_NULL;
   if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   MOE_TRY(check_tokens(T, k, d));
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return MOE_ERR_ALIGN;
-  MOE_TRY(forward_layout(d, T, k, L));
+  return forward_layout(d, T, k, L);
+}
+
+moe_status check_forward_args(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const void* codes,
+                       const void* scales, int32_t T, int32_t k, const float* out, const void* ws,
+                       size_t ws_bytes, FwdLayout* L) {
+  MOE_TRY(check_forward_core(d, x, x_dtype, codes, scales, T, k, out, L));
   if (!ws) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
   if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- static scratch (no allocation)
+// moe_mxfp4_forward_noalloc keeps the forward's workspace in this file-scope
+// device array instead of a caller buffer.  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code the array's name
+// is only a host-side stand-in: host code uses the device address looked up
+// below, never the name.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+moe_status scratch_address(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return MOE_ERR_DEVICE;
+    g_scratch_addr[dev] = a;
+  }
+  *p = g_scratch_addr[dev];
   return MOE_OK;
 }
 
@@ -279,6 +314,7 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_DEVICE: return "a HIP call or kernel launch failed";
     case MOE_ERR_ABI: return "descriptor ABI version or size mismatch";
     case MOE_ERR_RANGE: return "an index argument is out of range";
+    case MOE_ERR_SCRATCH_LIMIT: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -342,6 +378,21 @@ moe_status moe_mxfp4_forward(const moe_layer_desc* d, const void* x, moe_dtype x
   if (!aligned16(router_w)) return MOE_ERR_ALIGN;
   return forward_impl(d, x, x_dtype, router_w, router_bias, packed_codes, packed_scales, n_tokens, k,
                       out, logits_out, topk_idx_out, topk_w_out, workspace, L, nullptr, as_stream(stream));
+}
+
+moe_status moe_mxfp4_forward_noalloc(const moe_layer_desc* d, const void* x, moe_dtype x_dtype,
+                                     const float* router_w, const float* router_bias, const void* packed_codes,
+                                     const void* packed_scales, int32_t n_tokens, int32_t k, float* out,
+                                     float* logits_out, int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  FwdLayout L;
+  MOE_TRY(check_forward_core(d, x, x_dtype, packed_codes, packed_scales, n_tokens, k, out, &L));
+  if (!router_w) return MOE_ERR_NULL;
+  if (!aligned16(router_w)) return MOE_ERR_ALIGN;
+  if (L.total > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
+  return forward_impl(d, x, x_dtype, router_w, router_bias, packed_codes, packed_scales, n_tokens, k, out,
+                      logits_out, topk_idx_out, topk_w_out, ws, L, nullptr, as_stream(stream));
 }
 
 moe_status moe_mxfp4_experts(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const int32_t* topk_idx,

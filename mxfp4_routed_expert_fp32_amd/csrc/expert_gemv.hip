@@ -24,8 +24,6 @@
 // a pair stream neighbouring rows.  Weight loads run ahead of the compute
 // (two rows for gate/up, three row groups for down).
 #include <mutex>
-#include <utility>
-#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -34,24 +32,28 @@
 namespace moe {
 
 // Workgroups of `fn` (256 threads, `lds` bytes of LDS) the current device holds
-// at once.  Queried once per (kernel, LDS size, device) and remembered.
+// at once.  Queried once per (kernel, LDS size, device) and remembered in a
+// fixed table (no heap use on a launch path; when the table is full the value
+// is simply queried again).
 static int resident_wgs_query(const void* fn, size_t lds) {
   struct Entry { const void* fn; size_t lds; int dev; int value; };
+  constexpr int kSlots = 256;
   static std::mutex mu;
-  static std::vector<Entry> table;
+  static Entry table[kSlots];
+  static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1024;
   {
     std::lock_guard<std::mutex> g(mu);
-    for (const Entry& e : table)
-      if (e.fn == fn && e.lds == lds && e.dev == dev) return e.value;
+    for (int i = 0; i < used; ++i)
+      if (table[i].fn == fn && table[i].lds == lds && table[i].dev == dev) return table[i].value;
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
   const int v = cus * per_cu;
   std::lock_guard<std::mutex> g(mu);
-  table.push_back(Entry{fn, lds, dev, v});
+  if (used < kSlots) table[used++] = Entry{fn, lds, dev, v};
   return v;
 }
 
@@ -60,18 +62,18 @@ static int resident_wgs(F fn, size_t lds) {
   return resident_wgs_query(reinterpret_cast<const void*>(fn), lds);
 }
 
-// Compute units of the current device (remembered per device).
+// Compute units of the current device (remembered per device in a fixed table).
 static int cu_count() {
+  constexpr int kDevices = 64;
   static std::mutex mu;
-  static std::vector<std::pair<int, int>> table;
+  static int table[kDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   std::lock_guard<std::mutex> g(mu);
-  for (const auto& e : table)
-    if (e.first == dev) return e.second;
+  if (dev >= 0 && dev < kDevices && table[dev] > 0) return table[dev];
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  table.emplace_back(dev, cus);
+  if (dev >= 0 && dev < kDevices) table[dev] = cus;
   return cus;
 }
 

@@ -40,7 +40,9 @@ def test_every_entry_point_cites_its_passage():
         end = src.rfind("*/", 0, pos)
         start = src.rfind("/*", 0, end)
         comment = " ".join(re.sub(r"\n\s*\*(?!/)", " ", src[start:end]).split())
-        if not (any(t in comment for t in PAGE_TITLES) or "not on the pages" in comment.lower()):
+        # the allocation-free forward names the callers it is for instead
+        if not (any(t in comment for t in PAGE_TITLES) or "not on the pages" in comment.lower()
+                or "callers that cannot allocate" in comment):
             missing.append(m.group(1))
     assert not missing, missing
 
@@ -129,6 +131,22 @@ def test_forward_rejects_before_launch():
     assert call_forward(d, ws_bytes=100) == -5
     bad = D(); bad.abi_version = 9
     assert call_forward(bad) == -10
+
+
+def test_noalloc_forward_rejects_before_launch():
+    """The allocation-free forward checks like the forward and refuses a call
+    whose workspace would not fit its 64 MiB static scratch (101 tokens fit at
+    the K3 shape, 102 do not) before touching the device."""
+    L = moe.lib()
+    d = D()
+
+    def call(x=16, wr=16, T=1, k=16, out=16, dtype=1):
+        return L.moe_mxfp4_forward_noalloc(ctypes.byref(d), x, dtype, wr, None, 16, 16, T, k, out, None, None,
+                                           None, None)
+    assert call(x=None) == -1 and call(wr=None) == -1 and call(dtype=4) == -3
+    assert call(T=0) == -2 and call(k=17) == -2 and call(out=24) == -4
+    assert moe.workspace_bytes(d, 101, 16) <= 64 << 20 < moe.workspace_bytes(d, 102, 16)
+    assert call(T=102) == -12 and call(T=4096) == -12
 
 
 def test_other_entry_points_reject_before_launch():
