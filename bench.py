@@ -1,26 +1,34 @@
 """Benchmark of the routed MXFP4 MoE layer on one MI355X.
 
-Default workload (`--workload decode`): single-token decode of one K3-shape
-layer (H=7168, I=1536, E=896, top-16, bf16 activations, every expert resident
-in HBM).  A step is one moe_mxfp4_forward call for one token: router logits,
-top-k + softmax, expert gate/up + SwiGLU, expert down, rank-ordered combine.
-Steps rotate over a pool of 256 distinct seeded tokens so that consecutive
-steps route to different experts and the 256 MB last-level cache cannot serve
-a replayed expert set.
+The default run (`--workload all`) measures the four model-shape workloads in
+one process and prints ONE JSON line.  Its top-level figures are single-token
+decode of one K3-shape layer (H=7168, I=1536, E=896, top-16, bf16
+activations, every expert resident in HBM); the other three are sub-objects
+under "workloads":
+  - decode64_zipf: 64 tokens per step, Zipf(1.1) router bias;
+  - prefill4096: 4096 tokens per step, uniform routing (grouped GEMMs on MFMA);
+  - stack12: 12 layers with RMSNorm + residual, one token per step, replayed
+    as a HIP graph.
+A step is one call of the layer (or of the stack graph).  Decode steps
+rotate over a pool of 256 distinct seeded tokens and batch steps over
+distinct token batches, so consecutive steps route to different experts and
+the 256 MB last-level cache cannot serve a replayed expert set.
 
-Other workloads (same layer shape): `decode64_zipf` (64 tokens per step,
-Zipf(1.1) router bias), `prefill4096` (4096 tokens per step, uniform routing),
-`stack12` (12 layers with RMSNorm + residual, one token per step, replayed
-as a HIP graph).
-
-Prints one JSON line.  The roofline object describes the dominant kernel
-(decode: the gate/up GEMV, timed over a run of back-to-back launches with
-HIP events on the stream it runs on); `cpu_baseline` times the CPU oracle on the host cores on a
-bounded sample of the same workload.
+Every workload is gated on parity first: sample tokens are checked against
+the CPU oracle (run on the GPU's own logits) on both readings of the output
+bar, and no number is printed if they disagree.  Each workload's `roofline`
+object describes the kernels its timed step runs: their algorithmic bytes
+(or flops) per launch divided by their mean launch time, measured here with
+HIP events over back-to-back launches on the stream they run on.  `traffic`
+is the HBM bytes of the same kernels read from rocprofv3 counter summaries
+under profiles/ (null when those kernels' sources changed since).
+`cpu_baseline` times the oracle on the host cores on a bounded sample of the
+decode workload.
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,27 +39,36 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MXFP4_PEAK_TFLOPS = 10100.0
 
+WORKLOADS = ["decode", "decode64_zipf", "prefill4096", "stack12"]
+DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096": (20, 3), "stack12": (100, 10)}
+
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--steps", type=int, default=None, help="timed steps of the primary workload")
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="decode", choices=["decode", "decode64_zipf", "prefill4096", "stack12"])
+    p.add_argument("--workload", default="all", choices=["all"] + WORKLOADS)
     p.add_argument("--pool", type=int, default=256)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args()
 
 
-DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096": (20, 3), "stack12": (100, 10)}
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
 
-# Source files each dominant kernel is built from: HBM traffic measured with
+
+# --------------------------------------------------------------------------- counter traffic
+
+# Source files each measured kernel is built from: HBM traffic measured with
 # rocprofv3 counters is reported only while these files still hash to the
 # value recorded next to the counters.
 KERNEL_SOURCES = {
     "k_gateup_gemv": ["expert_gemv.hip", "common.h", "topk.h"],
+    "k_down_ks": ["expert_gemv.hip", "common.h"],
     "k_gateup_mfma": ["expert_mfma.hip", "common.h"],
+    "k_down_mfma": ["expert_mfma.hip", "common.h"],
 }
 
 
@@ -85,30 +102,12 @@ def measured_traffic(kernel, workload):
         return None
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
-        sys.exit(2)
-    steps, warmup = DEFAULT_STEPS[a.workload]
-    a.steps = steps if a.steps is None else a.steps
-    a.warmup = warmup if a.warmup is None else a.warmup
-    if a.workload == "decode":
-        res = bench_decode(a)
-    elif a.workload in ("decode64_zipf", "prefill4096"):
-        res = bench_batch(a)
-    else:
-        res = bench_stack(a)
-    print(json.dumps(res), flush=True)
+def sum_traffic(items):
+    vals = [measured_traffic(k, w) for k, w in items]
+    return None if any(v is None for v in vals) else float(sum(vals))
 
 
-def common_fields(a, metric, value, unit, ms_step, config, roofline):
-    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f32 accumulate; bf16 activations; mxfp4 weights", "data": "synthetic (seeded)",
-            "config": config, "roofline": roofline, "cpu_baseline": None}
-
+# --------------------------------------------------------------------------- timing
 
 def hold_queue(seconds):
     """Keep the GPU busy on the current stream for about `seconds` (a bounded
@@ -144,23 +143,112 @@ def warm(launch, n):
     return host, e0.elapsed_time(e1) * 1e-3 / n
 
 
-def timed(step, n, warmup):
+def kernel_us(launch, n, warmup):
+    """Mean duration of one launch over n back-to-back launches (HIP events on
+    the current stream, after a queue hold)."""
+    import torch
+    enqueue_s, kernel_s = warm(launch, max(2, warmup))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_for(n, enqueue_s, kernel_s)
+    e0.record()
+    for i in range(n):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def time_steps(step, n, warmup, groups=5):
+    """Times exactly n steps after `warmup` untimed ones, between two events
+    with a device synchronisation on both sides.  Events between equal groups
+    of steps give the spread: median, min and max of the group means."""
     import torch
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(n):
-        step(warmup + i)
-    ev1.record()
+    groups = max(1, min(groups, n))
+    sizes = [n // groups + (1 if g < n % groups else 0) for g in range(groups)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    evs[0].record()
+    i = 0
+    for g, sz in enumerate(sizes):
+        for _ in range(sz):
+            step(warmup + i)
+            i += 1
+        evs[g + 1].record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / n
+    ms = evs[0].elapsed_time(evs[-1]) / n
+    per = [evs[g].elapsed_time(evs[g + 1]) / sizes[g] for g in range(groups)]
+    return ms, {"median_ms": statistics.median(per), "min_ms": min(per), "max_ms": max(per),
+                "groups": groups}
+
+
+# --------------------------------------------------------------------------- parity gates
+
+def refuse(msg):
+    log("parity gate failed: " + msg)
+    raise SystemExit("parity gate failed: " + msg)
+
+
+def gate_tokens(w, xf, logits, idx, wt, out, wr_h, bias=None, layer=0):
+    """Oracle on the GPU's logits for the given tokens; returns (normwise,
+    elementwise) maxima or refuses."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from tests import _parity as P
+
+    sel = np.unique(oracle.topk(logits, w.k))
+    ex = {int(e): synth.expert(w, int(e), layer) for e in sel}
+    r_out, _, r_idx, r_w = oracle.moe_forward(xf, wr_h, ex, w.H, w.I, w.k, bias=bias, logits_override=logits)
+    if not np.array_equal(idx, r_idx):
+        refuse("top-k differs from the oracle")
+    if P.weights_rel_err(wt, r_w) > 2 * (w.k + 4) * 2.0 ** -24:
+        refuse("combine weights differ from the oracle")
+    if not np.all(np.isfinite(out)):
+        refuse("non-finite output")
+    nw = float(P.normwise_err(out, r_out).max())
+    A = oracle.moe_abs_scale(xf, r_idx, r_w, ex, w.H, w.I, w.E)
+    ew = P.elementwise_ratio(out, r_out, A)
+    if not (nw <= P.OUT_TOL and ew <= P.OUT_TOL):
+        refuse("normwise %g, elementwise %g" % (nw, ew))
+    return nw, ew
+
+
+def parity_obj(tokens, nw, ew):
+    return {"tokens_checked": tokens, "normwise_max": nw, "elementwise_max": ew, "tolerance": 2e-5,
+            "readings": "normwise max|g-r|/max|r| per token; elementwise |g-r|/A with A the oracle's "
+                        "magnitude scale"}
+
+
+# --------------------------------------------------------------------------- shared state
+
+class Ctx:
+    """The model-shape layer 0 (shared by decode, the batch workloads and the
+    stack's first layer) and its router."""
+
+    def __init__(self):
+        import synth
+        import synth.device as sd
+        t0 = time.time()
+        w = synth.WORKLOADS["decode"]
+        self.codes, self.scales = sd.upload_layer(w, 0)
+        self.wr = sd.router_w(w)
+        log("setup: layer 0 resident (%.2f GB) in %.1f s" % ((self.codes.numel() + self.scales.numel()) / 1e9,
+                                                            time.time() - t0))
+
+
+def base_fields(metric, value, unit, steps, warmup, ms_step, spread, config, roofline, parity):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": ms_step, "ms_per_step_spread": spread, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32 accumulate; bf16 activations; mxfp4 weights",
+            "data": "synthetic (seeded)", "config": config, "parity": parity, "roofline": roofline}
 
 
 # --------------------------------------------------------------------------- decode
 
-def bench_decode(a):
+def bench_decode(a, ctx, steps, warmup):
     import numpy as np
     import torch
 
@@ -171,12 +259,8 @@ def bench_decode(a):
     w = synth.WORKLOADS["decode"]
     desc = sd.desc_for(w)
     dev = "cuda"
-    t0 = time.time()
-    codes, scales = sd.upload_layer(w, 0)
-    wr = sd.router_w(w)
+    codes, scales, wr = ctx.codes, ctx.scales, ctx.wr
     pool = sd.tokens(w, range(a.pool))                      # [pool, H] bf16
-    print("setup: layer resident (%.2f GB) in %.1f s" % ((codes.numel() + scales.numel()) / 1e9,
-                                                          time.time() - t0), file=sys.stderr, flush=True)
     k, H, I, E = w.k, w.H, w.I, w.E
     out = torch.empty(1, H, dtype=torch.float32, device=dev)
     logits = torch.empty(1, E, dtype=torch.float32, device=dev)
@@ -188,57 +272,87 @@ def bench_decode(a):
         x = pool[i % a.pool:i % a.pool + 1]
         moe.moe_mxfp4_forward(desc, x, wr, None, codes, scales, k, out, ws, logits, idx, wt)
 
-    parity = parity_gate(w, step, out, logits, idx, wr, lambda t: synth.tokens_f32(w, [t]), [0, 1])
+    # parity gate on two tokens
+    wr_h = wr.cpu().numpy()
+    gate = (0.0, 0.0)
+    for t in (0, 1):
+        step(t)
+        torch.cuda.synchronize()
+        r = gate_tokens(w, synth.tokens_f32(w, [t]), logits.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(),
+                        out.cpu().numpy(), wr_h)
+        gate = (max(gate[0], r[0]), max(gate[1], r[1]))
+    log("decode: parity ok (normwise %.3g, elementwise %.3g)" % gate)
 
-    # routes of every pool token (for the stage timing below)
+    # logits and routes of every pool token (for the kernel timing below)
+    logits_all = torch.empty(a.pool, E, dtype=torch.float32, device=dev)
     routes = torch.empty(a.pool, k, dtype=torch.int32, device=dev)
     for i in range(a.pool):
         step(i)
+        logits_all[i].copy_(logits[0])
         routes[i].copy_(idx[0])
     torch.cuda.synchronize()
 
-    ms_step = timed(step, a.steps, a.warmup)
+    ms_step, spread = time_steps(step, steps, warmup)
 
-    # dominant kernel: gate/up + SwiGLU GEMV, timed over back-to-back launches on the
-    # stream it runs on, with the same routes and tokens as the steps above
+    # the expert phase as the forward runs it: the selecting gate/up GEMV, then
+    # the down GEMV, each timed over back-to-back launches on its stream
     hbuf = torch.empty(k, I, dtype=torch.float32, device=dev)
-    enqueue_s, kernel_s = warm(
-        lambda i: moe.moe_mxfp4_gate_up(desc, pool[i % a.pool:i % a.pool + 1], routes[i % a.pool], k, codes,
-                                        scales, hbuf), max(1, a.warmup))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_for(a.steps, enqueue_s, kernel_s)
-    e0.record()
-    for i in range(a.steps):
-        j = (a.warmup + i) % a.pool
-        moe.moe_mxfp4_gate_up(desc, pool[j:j + 1], routes[j], k, codes, scales, hbuf)
-    e1.record()
-    torch.cuda.synchronize()
-    gu_ms = e0.elapsed_time(e1) / a.steps
-    gu_bytes = k * 2 * (I * H // 2 + I * H // 32) + H * 2 + k * I * 4
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    ybuf = torch.empty(k, H, dtype=torch.float32, device=dev)
+    sel_i = torch.empty(1, k, dtype=torch.int32, device=dev)
+    sel_w = torch.empty(1, k, dtype=torch.float32, device=dev)
+    n = max(steps, 64)
 
-    expert_bytes = k * w.expert_bytes
+    def gu_sel(i):
+        j = (warmup + i) % a.pool
+        moe.moe_mxfp4_gate_up_select(desc, pool[j:j + 1], logits_all[j:j + 1], k, codes, scales, sel_i, sel_w, hbuf)
+
+    def down(i):
+        j = (warmup + i) % a.pool
+        moe.moe_mxfp4_down(desc, hbuf, routes[j], codes, scales, ybuf)
+
+    def gu_given(i):
+        j = (warmup + i) % a.pool
+        moe.moe_mxfp4_gate_up(desc, pool[j:j + 1], routes[j], k, codes, scales, hbuf)
+
+    gu_us = kernel_us(gu_sel, n, warmup)
+    dn_us = kernel_us(down, n, warmup)
+    gv_us = kernel_us(gu_given, n, warmup)
+    gu_w = k * 2 * (I * H // 2 + I * H // 32)      # gate + up rows of the k experts
+    dn_w = k * (H * I // 2 + H * I // 32)          # down rows of the k experts
+    expert_bytes = k * w.expert_bytes              # 280,756,224 B
+    assert gu_w + dn_w == expert_bytes
+    ach = expert_bytes / ((gu_us + dn_us) * 1e-6) / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": "expert phase as the forward runs it: k_gateup_gemv (selecting) + k_down_ks",
+        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+        "traffic": sum_traffic([("k_gateup_gemv", "decode"), ("k_down_ks", "decode")]),
+        "bytes_per_launch": expert_bytes, "avg_launch_us": gu_us + dn_us,
+        "kernels": {
+            "k_gateup_gemv_select": {"avg_launch_us": gu_us, "weight_bytes": gu_w,
+                                     "frac": gu_w / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                     "traffic": measured_traffic("k_gateup_gemv", "decode")},
+            "k_down_ks": {"avg_launch_us": dn_us, "weight_bytes": dn_w,
+                          "frac": dn_w / (dn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "traffic": measured_traffic("k_down_ks", "decode")},
+            "k_gateup_gemv_routes_given": {"avg_launch_us": gv_us,
+                                           "frac": gu_w / (gv_us * 1e-6) / 1e9 / HBM_PEAK_GBS}},
+    }
     layer_bytes = expert_bytes + E * H * 4 + H * 2 + H * 4
-    res = common_fields(
-        a, "MoE-layer decode tokens/s (one token per step, one K3-shape layer)", 1.0 / (ms_step * 1e-3),
-        "tokens/s", ms_step,
-        {"workload": "decode: T=1, H=7168, I=1536, E=896, k=16, bf16 x, all experts resident, "
-                     "256-token rotating pool",
-         "global_batch": 1, "layer_bytes_per_token": layer_bytes,
-         "layer_GBps": layer_bytes / (ms_step * 1e-3) / 1e9, "expert_bytes_per_token": expert_bytes,
-         "parity_max_err": parity},
-        {"bound": "hbm", "kernel": "k_gateup_gemv (routes given)", "achieved": achieved, "peak": HBM_PEAK_GBS,
-         "unit": "GB/s",
-         "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("k_gateup_gemv", "decode"),
-         "avg_launch_us": gu_ms * 1e3, "bytes_per_launch": gu_bytes})
-    if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, 1)
-    return res
+    cfg = {"workload": "decode: T=1, H=7168, I=1536, E=896, k=16, bf16 x, all experts resident, "
+                       "256-token rotating pool",
+           "global_batch": 1, "layer_bytes_per_token": layer_bytes,
+           "layer_GBps": layer_bytes / (ms_step * 1e-3) / 1e9, "layer_frac_hbm":
+               layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, "expert_bytes_per_token": expert_bytes}
+    log("decode: %.2f us/step, expert phase %.1f + %.1f us (frac %.3f)" % (ms_step * 1e3, gu_us, dn_us,
+                                                                          ach / HBM_PEAK_GBS))
+    return base_fields("MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill)",
+                       1.0 / (ms_step * 1e-3), "tokens/s", steps, warmup, ms_step, spread, cfg, roofline,
+                       parity_obj([0, 1], *gate))
 
 
 # --------------------------------------------------------------------------- batched decode / prefill
 
-def bench_batch(a):
+def bench_batch(a, ctx, name, steps, warmup):
     import numpy as np
     import torch
 
@@ -246,17 +360,14 @@ def bench_batch(a):
     import synth.device as sd
     import mxfp4_routed_expert_fp32_amd as moe
 
-    w = synth.WORKLOADS[a.workload]
+    w = synth.WORKLOADS[name]
     desc = sd.desc_for(w)
     dev = "cuda"
     T, k, H, I, E = w.T, w.k, w.H, w.I, w.E
-    t0 = time.time()
-    codes, scales = sd.upload_layer(w, 0)
-    wr = sd.router_w(w)
+    codes, scales, wr = ctx.codes, ctx.scales, ctx.wr
     bias = sd.router_bias(w)
     nbatch = 8 if T <= 64 else 2                 # rotating batches of distinct tokens
     xs = [sd.tokens(w, range(b * T, (b + 1) * T)) for b in range(nbatch)]
-    print("setup in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
     out = torch.empty(T, H, dtype=torch.float32, device=dev)
     logits = torch.empty(T, E, dtype=torch.float32, device=dev)
     idx = torch.empty(T, k, dtype=torch.int32, device=dev)
@@ -266,9 +377,26 @@ def bench_batch(a):
     def step(i):
         moe.moe_mxfp4_forward(desc, xs[i % nbatch], wr, bias, codes, scales, k, out, ws, logits, idx, wt)
 
+    # parity gate on sample tokens of batch 0: for the Zipf batch the tokens
+    # also cover the hottest experts (every token selects the top three)
+    step(0)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    if T <= 64:
+        sample = sorted({0, 1, 17, 31, 40, 63} & set(range(T)))
+    else:   # first and last pair of two expert blocks (sorted order), plus both ends
+        flat = idx_h.reshape(-1)
+        order = np.argsort(flat, kind="stable")
+        offs = np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))])
+        sample = {0, T - 1}
+        for e in (int(np.argmax(np.diff(offs))), int(np.argmin(np.diff(offs)))):
+            sample.update({int(order[offs[e]]) // k, int(order[offs[e + 1] - 1]) // k})
+        sample = sorted(sample)
     b_h = None if bias is None else bias.cpu().numpy()
-    parity = parity_gate(w, step, out, logits, idx, wr, lambda t: synth.tokens_f32(w, range(T))[[t]], [0, T - 1],
-                         bias=b_h, rows=True)
+    gate = gate_tokens(w, synth.tokens_f32(w, sample), logits.cpu().numpy()[sample], idx_h[sample],
+                       wt.cpu().numpy()[sample], out.cpu().numpy()[sample], wr.cpu().numpy(), bias=b_h)
+    log("%s: parity ok on %d tokens (normwise %.3g, elementwise %.3g)" % (name, len(sample), *gate))
+
     unions, maxload = [], []
     for b in range(nbatch):
         step(b)
@@ -276,98 +404,114 @@ def bench_batch(a):
         ids = idx.cpu().numpy()
         unions.append(len(np.unique(ids)))
         maxload.append(int(np.bincount(ids.reshape(-1), minlength=E).max()))
-    ms_step = timed(step, a.steps, a.warmup)
+    ms_step, spread = time_steps(step, steps, warmup)
     union = float(np.mean(unions))
     touched = union * w.expert_bytes + E * H * 4 + T * H * 2 + T * H * 4
-    gbps = touched / (ms_step * 1e-3) / 1e9
     flops = 2.0 * T * k * 3 * H * I + 2.0 * T * E * H
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    cfg = {"workload": "%s: T=%d, H=%d, I=%d, E=%d, k=%d, bf16 x%s" % (
-               a.workload, T, H, I, E, k, ", Zipf(1.1) router bias" if bias is not None else ", uniform routing"),
-           "global_batch": T, "experts_touched_mean": union, "max_expert_load": max(maxload),
-           "touched_bytes_per_step": touched, "layer_GBps": gbps, "algorithmic_TFLOPs": tflops,
-           "frac_bf16_mfma_peak": tflops / BF16_PEAK_TFLOPS, "frac_mxfp4_mfma_peak": tflops / MXFP4_PEAK_TFLOPS,
-           "parity_max_err": parity}
-    # dominant kernel: the grouped gate/up GEMM (k_gateup_mfma), timed over a
-    # run of back-to-back launches with HIP events on its stream, over the sorted
-    # routes of each rotating batch
-    P = T * k
-    mb = moe.max_expert_blocks(E, P)
+
+    # the expert phase as the forward runs it (grouped gate/up, grouped down),
+    # each kernel timed over back-to-back launches, over the sorted routes of
+    # every rotating batch
+    P_ = T * k
+    mb = moe.max_expert_blocks(E, P_)
     nsw = moe.sort_workspace_bytes(E, T, k)
     sort_ws = torch.empty(nsw, dtype=torch.uint8, device=dev) if nsw else None
     stage = []
     for b in range(nbatch):
         step(b)
         offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
-        pairs = torch.empty(P, dtype=torch.int32, device=dev)
+        pairs = torch.empty(P_, dtype=torch.int32, device=dev)
         moe.moe_sort_by_expert(idx, E, offs, pairs, sort_ws)
         blocks = torch.empty(mb, 4, dtype=torch.int32, device=dev)
         nb = torch.empty(1, dtype=torch.int32, device=dev)
-        moe.moe_expert_blocks(offs, P, blocks, nb)
+        moe.moe_expert_blocks(offs, P_, blocks, nb)
         stage.append((pairs, blocks, nb))
-    hterm = torch.empty(2, P, I, dtype=torch.bfloat16, device=dev)
+    hterm = torch.empty(2, P_, I, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(P_, H, dtype=torch.float32, device=dev)
 
     def gate_up(i):
         j = i % nbatch
         moe.moe_mxfp4_grouped_gate_up(desc, xs[j], k, stage[j][0], stage[j][1], stage[j][2], codes, scales, hterm)
 
-    enqueue_s, kernel_s = warm(gate_up, max(2, a.warmup))
-    nl = max(a.steps, 2 * nbatch)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_for(nl, enqueue_s, kernel_s)
-    e0.record()
-    for i in range(nl):
-        gate_up(i)
-    e1.record()
-    torch.cuda.synchronize()
-    gu_avg_ms = e0.elapsed_time(e1) / nl
-    gu_ms = [gu_avg_ms] * nl
-    gu_w = 2 * (I * H // 2 + I * H // 32)                     # gate + up bytes of one expert
-    gu_bytes = [unions[i % nbatch] * gu_w + T * H * 2 + P * I * 4 for i in range(nl)]
-    gu_flops = 4.0 * H * I * P
-    cfg["gate_up_avg_launch_us"] = gu_avg_ms * 1e3
-    if a.workload == "prefill4096":
-        ach = gu_flops / (gu_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "k_gateup_mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
-                "traffic": measured_traffic("k_gateup_mfma", a.workload), "avg_launch_us": gu_avg_ms * 1e3,
-                "flops_per_launch": gu_flops, "frac_mxfp4_mfma_peak": ach / MXFP4_PEAK_TFLOPS,
-                "weight_GBps": float(np.mean(gu_bytes)) / (gu_avg_ms * 1e-3) / 1e9}
+    def down(i):
+        j = i % nbatch
+        moe.moe_mxfp4_grouped_down(desc, hterm, stage[j][0], stage[j][1], stage[j][2], codes, scales, y)
+
+    nl = max(steps, 2 * nbatch)
+    gu_us = kernel_us(gate_up, nl, warmup)
+    dn_us = kernel_us(down, nl, warmup)
+    del hterm, y
+    exp_us = gu_us + dn_us
+    wbytes = union * w.expert_bytes
+    roof_common = {"avg_launch_us": exp_us,
+                   "kernels": {"k_gateup_mfma": {"avg_launch_us": gu_us,
+                                                 "traffic": measured_traffic("k_gateup_mfma", name)},
+                               "k_down_mfma": {"avg_launch_us": dn_us,
+                                               "traffic": measured_traffic("k_down_mfma", name)}},
+                   "traffic": sum_traffic([("k_gateup_mfma", name), ("k_down_mfma", name)])}
+    if name == "prefill4096":
+        eflops = 2.0 * P_ * 3 * H * I
+        ach = eflops / (exp_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "expert phase as the forward runs it: k_gateup_mfma + k_down_mfma "
+                                               "(bf16 MFMA, fp32 accumulate)",
+                    "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                    "flops_per_launch": eflops, "frac_mxfp4_mfma_peak": ach / MXFP4_PEAK_TFLOPS,
+                    "weight_bytes_per_launch": wbytes,
+                    "frac_hbm_weights": wbytes / (exp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, **roof_common}
+        for kn, us, fl in (("k_gateup_mfma", gu_us, 4.0 * H * I * P_), ("k_down_mfma", dn_us, 2.0 * H * I * P_)):
+            roofline["kernels"][kn]["frac"] = fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
     else:
-        ach = float(np.sum(gu_bytes)) / (float(np.sum(gu_ms)) * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_gateup_mfma", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("k_gateup_mfma", a.workload),
-                "avg_launch_us": gu_avg_ms * 1e3, "bytes_per_launch": float(np.mean(gu_bytes))}
-    res = common_fields(a, "MoE-layer tokens/s (%s)" % a.workload, T / (ms_step * 1e-3), "tokens/s", ms_step, cfg,
-                        roof)
-    if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, 1)
+        ach = wbytes / (exp_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "expert phase as the forward runs it: k_gateup_mfma + k_down_mfma",
+                    "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                    "bytes_per_launch": wbytes, **roof_common}
+        for kn, us, frac in (("k_gateup_mfma", gu_us, 2 / 3), ("k_down_mfma", dn_us, 1 / 3)):
+            roofline["kernels"][kn]["frac"] = frac * wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    cfg = {"workload": "%s: T=%d, H=%d, I=%d, E=%d, k=%d, bf16 x%s" % (
+               name, T, H, I, E, k, ", Zipf(1.1) router bias" if bias is not None else ", uniform routing"),
+           "global_batch": T, "experts_touched_mean": union, "max_expert_load": max(maxload),
+           "touched_bytes_per_step": touched, "layer_GBps": touched / (ms_step * 1e-3) / 1e9,
+           "algorithmic_TFLOPs": tflops, "frac_bf16_mfma_peak": tflops / BF16_PEAK_TFLOPS,
+           "frac_mxfp4_mfma_peak": tflops / MXFP4_PEAK_TFLOPS}
+    log("%s: %.3f ms/step, expert phase %.1f + %.1f us (frac %.3f)" % (name, ms_step, gu_us, dn_us,
+                                                                       roofline["frac"]))
+    res = base_fields("MoE-layer tokens/s (%s)" % name, T / (ms_step * 1e-3), "tokens/s", steps, warmup, ms_step,
+                      spread, cfg, roofline, parity_obj(sample, *gate))
+    del ws, out, logits
+    torch.cuda.empty_cache()
     return res
 
 
 # --------------------------------------------------------------------------- stack
 
-def bench_stack(a):
+def bench_stack(a, ctx, steps, warmup):
     import numpy as np
     import torch
 
     import synth
     import synth.device as sd
     import mxfp4_routed_expert_fp32_amd as moe
+    from tests._stack_check import stack_layer_by_layer
 
     w = synth.WORKLOADS["stack12"]
     desc = sd.desc_for(w)
     dev = "cuda"
     t0 = time.time()
-    layers = [sd.upload_layer(w, l) for l in range(w.layers)]
-    wrs = [sd.router_w(w, l) for l in range(w.layers)]
+    layers = [(ctx.codes, ctx.scales, ctx.wr)]     # layer 0 is the decode layer (same seed)
+    for l in range(1, w.layers):
+        c, s = sd.upload_layer(w, l)
+        layers.append((c, s, sd.router_w(w, l)))
     gam = [sd.gamma(w, l) for l in range(w.layers)]
-    print("setup: %d layers resident in %.1f s" % (w.layers, time.time() - t0), file=sys.stderr, flush=True)
+    log("stack12: %d layers resident in %.1f s" % (w.layers, time.time() - t0))
     pool = sd.tokens(w, range(a.pool))
+    # refusal gate: every layer against the oracle, from the GPU's residual before it
+    (nw, ew), eager0 = stack_layer_by_layer(w, desc, layers, gam, pool[0:1].contiguous(), 1, w.eps, w.k)
+    log("stack12: parity ok, 12 layers (normwise %.3g, elementwise %.3g)" % (nw, ew))
     x = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
     resid = torch.empty(1, w.H, dtype=torch.float32, device=dev)
     ws = torch.empty(moe.stack_workspace_bytes(desc, 1, w.k), dtype=torch.uint8, device=dev)
-    args = ([l[0] for l in layers], [l[1] for l in layers], wrs, None, gam, w.eps)
+    args = ([l[0] for l in layers], [l[1] for l in layers], [l[2] for l in layers], None, gam, w.eps)
     graph = moe.StackGraph(desc, *args, x, w.k, resid, ws)
 
     def step(i):
@@ -380,67 +524,44 @@ def bench_stack(a):
 
     step(0)
     torch.cuda.synchronize()
-    g0 = resid.cpu().numpy().copy()
-    eager(0)
-    torch.cuda.synchronize()
-    assert np.array_equal(g0.view(np.uint32), resid.cpu().numpy().view(np.uint32)), "graph != eager"
-    ms_graph = timed(step, a.steps, a.warmup)
-    ms_eager = timed(eager, max(10, a.steps // 4), 3)
+    if not np.array_equal(resid.cpu().numpy().view(np.uint32), eager0.view(np.uint32)):
+        refuse("stack graph replay differs from the checked eager stack")
+    ms_graph, spread = time_steps(step, steps, warmup)
+    ms_eager, _ = time_steps(eager, max(10, steps // 4), 3)
     per_tok = w.layers * (w.k * w.expert_bytes + w.E * w.H * 4)
     gbps = per_tok / (ms_graph * 1e-3) / 1e9
     cfg = {"workload": "stack12: 12 layers x (RMSNorm eps=1e-6 + MoE H=7168 I=1536 E=896 k=16 + residual), T=1, "
                        "hipGraph replay, 256-token rotating pool",
            "global_batch": 1, "bytes_per_token": per_tok, "GBps": gbps, "ms_per_token_eager": ms_eager,
            "graph_equals_eager": True}
-    roof = {"bound": "hbm", "kernel": "stack", "achieved": gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbps / HBM_PEAK_GBS, "traffic": None}
+    roofline = {"bound": "hbm", "kernel": "whole step (12 layers, graph replay)", "achieved": gbps,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBS, "traffic": None,
+                "bytes_per_launch": per_tok, "avg_launch_us": ms_graph * 1e3}
     graph.close()
-    return common_fields(a, "12-layer MoE stack decode tokens/s", 1.0 / (ms_graph * 1e-3), "tokens/s", ms_graph,
-                         cfg, roof)
+    log("stack12: %.3f ms/token (eager %.3f), frac %.3f" % (ms_graph, ms_eager, gbps / HBM_PEAK_GBS))
+    return base_fields("12-layer MoE stack decode tokens/s", 1.0 / (ms_graph * 1e-3), "tokens/s", steps, warmup,
+                       ms_graph, spread, cfg, roofline, parity_obj([0], nw, ew))
 
 
-# --------------------------------------------------------------------------- checks and CPU baseline
+# --------------------------------------------------------------------------- CPU baseline
 
-def parity_gate(w, step, out, logits, idx, wr, tokens_of, ts, bias=None, rows=False):
-    """Refuse to report a number if the layer disagrees with the oracle (run on
-    the GPU's logits) on sample tokens."""
-    import numpy as np
-    import torch
-
-    import oracle
-    import synth
-    from tests import _parity as P
-
-    worst = 0.0
-    wr_h = wr.cpu().numpy()
-    for t in ts:
-        if rows:           # one batch holds every sample token: row t of step 0
-            if t == ts[0]:
-                step(0)
-                torch.cuda.synchronize()
-            r = t
-        else:              # one token per step: step t, row 0
-            step(t)
-            torch.cuda.synchronize()
-            r = 0
-        lg_all, idx_all, out_all = logits.cpu().numpy(), idx.cpu().numpy(), out.cpu().numpy()
-        lg = lg_all[r:r + 1]
-        sel = np.unique(oracle.topk(lg, w.k))
-        ex = {int(e): synth.expert(w, int(e)) for e in sel}
-        r_out, _, r_idx, _ = oracle.moe_forward(tokens_of(t), wr_h, ex, w.H, w.I, w.k, bias=bias,
-                                                logits_override=lg)
-        if not np.array_equal(idx_all[r:r + 1], r_idx):
-            raise SystemExit("parity gate failed: top-k differs from the oracle")
-        err = float(P.normwise_err(out_all[r:r + 1], r_out).max())
-        if not err <= P.OUT_TOL:
-            raise SystemExit("parity gate failed: normwise error %g" % err)
-        worst = max(worst, err)
-    return worst
+def cpu_info():
+    model, mhz = None, []
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name") and model is None:
+                model = line.split(":", 1)[1].strip()
+            elif line.startswith("cpu MHz"):
+                mhz.append(float(line.split(":", 1)[1]))
+    except OSError:
+        pass
+    return model, (statistics.mean(mhz) if mhz else None)
 
 
-def cpu_baseline(w, seconds, tokens_per_call):
-    """The oracle as it is, on the host cores, on whole tokens of the same
-    workload until `seconds` of wall time have been spent (at least 2 tokens)."""
+def cpu_baseline(w, seconds):
+    """The oracle as it is, on the host cores, on whole tokens of the decode
+    workload until `seconds` of oracle time have been spent (at least 3
+    tokens, one oracle call each); per-call times give the median and range."""
     import numpy as np
 
     import oracle
@@ -451,21 +572,58 @@ def cpu_baseline(w, seconds, tokens_per_call):
     cores = len(os.sched_getaffinity(0))
     if os.environ.get("OMP_NUM_THREADS", "").isdigit():
         cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
-    n, spent = 0, 0.0
-    while n < 2 or spent < seconds:
-        t = 100000 + n
+    model, mhz = cpu_info()
+    times = []
+    while len(times) < 3 or sum(times) < seconds:
+        t = 100000 + len(times)
         x = synth.tokens_f32(w, [t])
         sel = np.unique(oracle.topk(oracle.router_logits(x, wr, bias), w.k))
         ex = {int(e): synth.expert(w, int(e)) for e in sel}
         t0 = time.perf_counter()
         oracle.moe_forward(x, wr, ex, w.H, w.I, w.k, bias=bias, nthreads=cores)
-        spent += time.perf_counter() - t0
-        n += 1
-        if n >= 512:
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 512:
             break
-    return {"value": n / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d tokens of the %s workload, one oracle call each, %.1f s of oracle time" % (
-                n, w.name, spent)}
+    spent = sum(times)
+    return {"value": len(times) / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "median_tokens_per_s": 1.0 / statistics.median(times), "min_tokens_per_s": 1.0 / max(times),
+            "max_tokens_per_s": 1.0 / min(times), "cpu_model": model, "cpu_mhz_mean": mhz,
+            "sample": "%d tokens of the decode workload, one oracle call each (router, top-k, 16 experts "
+                      "dequantised and applied, combine), %.1f s of oracle time; expert generation not timed"
+                      % (len(times), spent)}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    names = WORKLOADS if a.workload == "all" else [a.workload]
+    primary = names[0]
+    ctx = Ctx()
+    results = {}
+    for name in names:
+        steps, warmup = DEFAULT_STEPS[name]
+        if name == primary:
+            steps = steps if a.steps is None else a.steps
+            warmup = warmup if a.warmup is None else a.warmup
+        if name == "decode":
+            results[name] = bench_decode(a, ctx, steps, warmup)
+        elif name == "stack12":
+            results[name] = bench_stack(a, ctx, steps, warmup)
+        else:
+            results[name] = bench_batch(a, ctx, name, steps, warmup)
+    res = results[primary]
+    if len(names) > 1:
+        res["workloads"] = {n: results[n] for n in names[1:]}
+    res["cpu_baseline"] = None
+    if not a.no_cpu_baseline:
+        import synth
+        res["cpu_baseline"] = cpu_baseline(synth.WORKLOADS["decode"], a.cpu_seconds)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -255,6 +255,21 @@ moe_status moe_mxfp4_down(const moe_layer_desc* desc, const float* h, const int3
 moe_status moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden,
                        const float* resid, float* out, void* stream);
 
+/* The gate/up stage as the decode-form forward runs it, with the selection
+ * fused in: each workgroup takes its pair's expert from the exact top-k of its
+ * token's logits [n_tokens][E] (as moe_topk_softmax) and computes h as
+ * moe_mxfp4_gate_up does; topk_idx [n_tokens][k] and topk_w [n_tokens][k]
+ * receive the selection and its softmax weights ("Tarfa EXACTNESS" page,
+ * opening list, and "Deltafin's custom compiled runtime", sections "Weight
+ * fidelity" and "Complete target sequence tape", for the selection;
+ * brain.bigb.es "deltafin", section "The techniques that bought the 82x",
+ * for the fused dequant + GEMV).  Errors: as
+ * moe_mxfp4_gate_up, and MOE_ERR_NULL for logits, topk_idx or topk_w. */
+moe_status moe_mxfp4_gate_up_select(const moe_layer_desc* desc, const void* x, moe_dtype x_dtype,
+                                    const float* logits, int32_t n_tokens, int32_t k, const void* packed_codes,
+                                    const void* packed_scales, int32_t* topk_idx, float* topk_w, float* h,
+                                    void* stream);
+
 /* Router logits alone: logits [n_tokens][E] = x . router_w^T (+ bias), fp32
  * accumulation ("Tarfa EXACTNESS" page, opening list: fp32 logits with fp32
  * accumulation).  x [n_tokens][H] (x_dtype), router_w [E][H] fp32 row-major,

@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = [
     "moe_abi_version", "moe_status_string", "moe_layer_check", "moe_mxfp4_packed_bytes",
     "moe_workspace_bytes", "moe_mxfp4_pack", "moe_mxfp4_forward", "moe_mxfp4_forward_noalloc", "moe_mxfp4_experts",
-    "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_combine",
+    "moe_mxfp4_gate_up", "moe_mxfp4_gate_up_select", "moe_mxfp4_down", "moe_combine",
     "moe_router_logits", "moe_topk_softmax", "moe_sort_workspace_bytes", "moe_sort_by_expert",
     "moe_max_expert_blocks", "moe_expert_blocks", "moe_mxfp4_grouped_gate_up", "moe_mxfp4_grouped_down",
     "moe_mxfp4_dequant", "moe_mxfp4_dequant_bf16", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_bytes",
@@ -82,6 +82,7 @@ def lib():
                                               ctypes.c_int),
                 "moe_mxfp4_experts": ([D, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
                 "moe_mxfp4_gate_up": ([D, vp, i32, vp, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+                "moe_mxfp4_gate_up_select": ([D, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
                 "moe_mxfp4_down": ([D, vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
                 "moe_combine": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
                 "moe_router_logits": ([D, vp, i32, vp, vp, i32, vp, vp], ctypes.c_int),
@@ -203,6 +204,12 @@ def moe_mxfp4_gate_up(desc, x, pair_expert, k, packed_codes, packed_scales, h, s
     _check("moe_mxfp4_gate_up", lib().moe_mxfp4_gate_up(
         ctypes.byref(desc), _ptr(x), _xdtype(x), _ptr(pair_expert), pair_expert.numel(), k,
         _ptr(packed_codes), _ptr(packed_scales), _ptr(h), _stream(stream)))
+
+
+def moe_mxfp4_gate_up_select(desc, x, logits, k, packed_codes, packed_scales, topk_idx, topk_w, h, stream=None):
+    _check("moe_mxfp4_gate_up_select", lib().moe_mxfp4_gate_up_select(
+        ctypes.byref(desc), _ptr(x), _xdtype(x), _ptr(logits), x.shape[0], k, _ptr(packed_codes),
+        _ptr(packed_scales), _ptr(topk_idx), _ptr(topk_w), _ptr(h), _stream(stream)))
 
 
 def moe_mxfp4_down(desc, h, pair_expert, packed_codes, packed_scales, y, stream=None):

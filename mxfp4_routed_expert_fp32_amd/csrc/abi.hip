@@ -420,6 +420,21 @@ moe_status moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, moe_dtype x
                                      d->hidden, d->inter, d->n_experts, h, as_stream(stream)));
 }
 
+moe_status moe_mxfp4_gate_up_select(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const float* logits,
+                                    int32_t n_tokens, int32_t k, const void* codes, const void* scales,
+                                    int32_t* topk_idx, float* topk_w, float* h, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!x || !logits || !codes || !scales || !topk_idx || !topk_w || !h) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  MOE_TRY(check_tokens(n_tokens, k, d));
+  if ((int64_t)n_tokens * k > kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_gateup_select_gemv(x, x_dtype == MOE_DTYPE_F32, logits, n_tokens, k,
+                                            static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                                            d->hidden, d->inter, d->n_experts, topk_idx, topk_w, h,
+                                            as_stream(stream)));
+}
+
 moe_status moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t* pair_expert, int32_t n_pairs,
                    const void* codes, const void* scales, float* y, void* stream) {
   MOE_TRY(check_desc(d));

@@ -706,3 +706,29 @@ def test_down_stage_wide_inter_many_pairs():
         A = np.abs(h[rows]).astype(np.float64) @ np.abs(wd).T
         P.assert_out_close(got[rows], ref)
         P.assert_elementwise(got[rows], ref, A)
+
+
+@pytest.mark.parametrize("T,E,k,xd", [(1, 896, 16, "bf16"), (3, 300, 7, "f32"), (2, 4096, 64, "bf16")])
+def test_gate_up_select_stage(T, E, k, xd):
+    """The selecting gate/up stage (the decode forward's first expert kernel):
+    its selection and weights equal moe_topk_softmax on the same logits, and
+    its h equals the routes-given gate/up stage on that selection, bit for bit."""
+    H, I = 512, 256
+    w = synth.Workload("gs2", 74, T, H, I, E, k, xd, weight_seed=8500 + E)
+    c, s, ex = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    lg = torch.from_numpy(np.random.default_rng(E).standard_normal((T, E)).astype(np.float32)).to(DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    h = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_gate_up_select(desc, x, lg, k, codes, scales, idx, wt, h)
+    idx2 = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wt2 = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    moe.moe_topk_softmax(lg, k, idx2, wt2)
+    h2 = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_gate_up(desc, x, idx2.reshape(-1), k, codes, scales, h2)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    assert np.array_equal(P.bits(wt.cpu().numpy()), P.bits(wt2.cpu().numpy()))
+    assert np.array_equal(P.bits(h.cpu().numpy()), P.bits(h2.cpu().numpy()))
