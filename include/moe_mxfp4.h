@@ -29,8 +29,10 @@
  * "Coarse provider binding"; explicit unsupported requests fail early, section
  * "Configuration and device selection"; lengths and offsets in checked
  * arithmetic, section "Model contract and pack authentication")
- *  - All functions are extern "C", never throw, and keep no state between
- *    calls.  They return MOE_OK (0) or a negative moe_status.
+ *  - All functions are extern "C", never throw, and return MOE_OK (0) or a
+ *    negative moe_status.  Apart from the objects they create and destroy
+ *    explicitly (the stack graph, the expert residency cache), they keep no
+ *    state between calls, and only those object constructors allocate.
  *  - Every argument check runs on the host before anything is enqueued; on an
  *    error nothing is launched and no output is touched.
  *  - Device pointers are plain device addresses; the caller owns every buffer
@@ -71,7 +73,10 @@ typedef enum moe_status {
     MOE_ERR_DEVICE = -9,      /* a HIP call or kernel launch failed */
     MOE_ERR_ABI = -10,        /* descriptor abi_version / struct_size mismatch */
     MOE_ERR_RANGE = -11,      /* an index argument (expert, matrix) is out of range */
-    MOE_ERR_SCRATCH_LIMIT = -12 /* moe_mxfp4_forward_noalloc: the call needs more than its static scratch */
+    MOE_ERR_SCRATCH_LIMIT = -12, /* moe_mxfp4_forward_noalloc: the call needs more than its static scratch */
+    MOE_ERR_POISONED = -13,   /* the residency cache failed terminally earlier and refuses further work */
+    MOE_ERR_STATE = -14,      /* a call out of order (a second plan before finish, finish without a plan) */
+    MOE_ERR_IO = -15          /* a trace file operation failed, or the trace reached its size limit */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -433,6 +438,128 @@ moe_status moe_stack_graph_create(const moe_layer_desc* desc, int32_t n_layers,
                                   size_t workspace_bytes, void* stream, moe_stack_graph** graph);
 moe_status moe_stack_graph_launch(moe_stack_graph* graph, void* stream);
 moe_status moe_stack_graph_destroy(moe_stack_graph* graph);
+
+#define MOE_CACHE_PREFETCH 1
+typedef struct moe_expert_cache moe_expert_cache;
+typedef struct moe_cache_stats {
+    uint32_t struct_size;     /* set by the caller: sizeof(moe_cache_stats) */
+    int32_t capacity;         /* slots in the pool */
+    int32_t poisoned;         /* 1 after a terminal failure */
+    int32_t alloc_retries;    /* failed pool allocations before the one that succeeded */
+    int64_t plans, hits, misses, prefetched, evictions;
+    uint64_t bytes_uploaded;  /* host -> device bytes enqueued by finish */
+} moe_cache_stats;
+
+/*
+ * Host-streamed experts with a device residency cache ("Deltafin's custom
+ * compiled runtime", section "CUDA pre-I/O planning and residency"; "How the
+ * native runtime works", section "Automatic PILOT prefetch and CUDA expert
+ * residency"): the layers' experts live in host memory (logical layout,
+ * experts back to back per layer, or any span per expert) and a bounded set
+ * of them is resident in a device slot pool.  One layer call is:
+ *   1. moe_cache_plan freezes a plan for the call's route ids (host array,
+ *      ids in [0, E)): every distinct expert keeps or gets a slot, the hits
+ *      first, then the misses in route order, each miss evicting a free slot
+ *      or the least recently used one across all layers that the plan does
+ *      not use.  slots_out[i] is the slot of ids[i]; miss_ids lists the
+ *      misses in order (room for n_ids entries); *n_miss their count.
+ *      MOE_ERR_UNSUPPORTED if the union exceeds the capacity, MOE_ERR_RANGE
+ *      for a bad layer or id, MOE_ERR_STATE if a plan is already frozen.
+ *      flags MOE_CACHE_PREFETCH makes it a prefetch plan (a hint: its
+ *      entries become resident like misses, slots_out may be NULL, and it
+ *      counts as prefetched, not as hits or misses).
+ *   2. moe_cache_finish consumes the plan with one host span per miss (its
+ *      codes, 3*H*I/2 bytes, and scales, 3*H*I/32 bytes, in the logical
+ *      layout) and enqueues the uploads on `stream`.  With host_pinned the
+ *      spans are DMAed directly (they must stay alive until the stream has
+ *      passed the copies); otherwise each span is copied on the host into one
+ *      of two pinned staging slabs, alternately, and the copy waits for that
+ *      slab's previous DMA (an event) before reusing it.  An all-hit plan
+ *      uploads nothing.  moe_cache_cancel drops a frozen plan instead.
+ *   3. The experts run on the slot pool (moe_cache_slots: codes and scales of
+ *      `capacity` experts in the device layout) with every route id replaced
+ *      by its slot: moe_mxfp4_experts on a descriptor with n_experts =
+ *      capacity.  The output equals the all-resident layer's bit for bit.
+ * Uploads, the experts call and any earlier use of an evicted slot must be
+ * ordered on one stream (a plan may evict a slot that work already enqueued
+ * still reads; stream order keeps the upload after it).
+ * moe_cache_create: capacity 0 sizes the pool from free device memory,
+ * keeping max(2 GiB, 20%) free, at most 4096 slots; the pool is allocated
+ * with up to max_retries further attempts, each a quarter smaller; fails
+ * with MOE_ERR_UNSUPPORTED below top_k_max slots.  A failed copy or event
+ * poisons the cache: every later call returns MOE_ERR_POISONED.  One caller
+ * at a time per cache.  moe_cache_layer_forward runs one whole layer call
+ * (router and top-k on the device, the route read back -- this entry
+ * synchronises the host with `stream` --, plan, finish from the layer's
+ * experts at host_codes / host_scales, experts on the slots) for up to 4096
+ * tokens; its workspace is moe_cache_workspace_bytes.
+ */
+moe_status moe_cache_create(const moe_layer_desc* desc, int32_t n_layers, int32_t capacity, int32_t max_retries,
+                            moe_expert_cache** cache);
+moe_status moe_cache_destroy(moe_expert_cache* cache);
+moe_status moe_cache_slots(moe_expert_cache* cache, void** slot_codes, void** slot_scales, int32_t* capacity);
+moe_status moe_cache_get_stats(moe_expert_cache* cache, moe_cache_stats* stats);
+moe_status moe_cache_plan(moe_expert_cache* cache, int32_t layer, const int32_t* ids, int32_t n_ids, int32_t flags,
+                          int32_t* slots_out, int32_t* miss_ids, int32_t* n_miss);
+moe_status moe_cache_finish(moe_expert_cache* cache, const void* const* miss_codes, const void* const* miss_scales,
+                            int32_t host_pinned, void* stream);
+moe_status moe_cache_cancel(moe_expert_cache* cache);
+moe_status moe_cache_workspace_bytes(moe_expert_cache* cache, int32_t n_tokens, int32_t k, size_t* bytes);
+moe_status moe_cache_layer_forward(moe_expert_cache* cache, int32_t layer, const void* x, moe_dtype x_dtype,
+                                   const float* router_w, const float* router_bias, const void* host_codes,
+                                   const void* host_scales, int32_t host_pinned, int32_t n_tokens, int32_t k,
+                                   float* out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Next-layer route hint ("Deltafin's custom compiled runtime", section "Exact
+ * next-layer expert prefetch"; "How the native runtime works", section
+ * "Automatic PILOT prefetch and CUDA expert residency"): the k experts the
+ * next layer's router would select if its input were the current activation
+ * r [n_tokens][H] fp32, i.e. the exact top-k of router_w_next .
+ * RMSNorm(r; gamma_next, eps) (+ bias), computed with the stack's own norm +
+ * router kernel and top-k, so for r equal to the next layer's input the hint
+ * is that layer's route.  hint_idx [n_tokens][k] int32 on the device, rank
+ * order.  The hint schedules prefetches (moe_cache_plan with
+ * MOE_CACHE_PREFETCH) and never enters the computation.  desc is the next
+ * layer's descriptor; workspace: moe_route_hint_workspace_bytes.  Errors:
+ * descriptor errors, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_OVERFLOW, MOE_ERR_DEVICE.
+ */
+moe_status moe_route_hint_workspace_bytes(const moe_layer_desc* desc, int32_t n_tokens, int32_t k, size_t* bytes);
+moe_status moe_route_hint(const moe_layer_desc* desc, const float* r, const float* gamma_next, float eps,
+                          const float* router_w_next, const float* router_bias_next, int32_t n_tokens, int32_t k,
+                          int32_t* hint_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+#define MOE_TRACE_BUFFERED 0
+#define MOE_TRACE_SYNC 1
+typedef struct moe_trace moe_trace;
+/*
+ * Router trace ("How the native runtime works", section "Router tracing and
+ * offline expert warming"; "Deltafin's custom compiled runtime", section
+ * "Router traces and cache warming"): one text line per traced token,
+ *   {"layer":L,"pos":P,"ids":[i0,...],"w":["xxxxxxxx",...]}
+ * the routed ids in rank order and the 8 hex digits of each combine weight's
+ * fp32 bits.  moe_trace_open refuses a path whose last component is a symlink
+ * or that is not a regular file (MOE_ERR_IO), truncates it, and caps the
+ * trace at max_bytes (0 = 8 GiB): a record that would pass the cap is refused
+ * with MOE_ERR_IO and the trace stops.  MOE_TRACE_BUFFERED batches records in
+ * a 1 MiB buffer written when full and at close; MOE_TRACE_SYNC writes and
+ * syncs each call's records before returning.  moe_trace_record appends
+ * n_tokens lines for tokens at positions position .. position + n_tokens - 1
+ * from host arrays ids [n_tokens][k] and w [n_tokens][k] (k <= 64).
+ * moe_trace_count reads a trace back for offline warming: counts
+ * [n_layers][n_experts] receives how often each (layer, expert) was routed and
+ * *n_records the line count; a malformed line, an unterminated or over-long
+ * line (4096 bytes), an id or layer out of range, a symlink or a file over
+ * 8 GiB is MOE_ERR_IO.  Tracing reads routes only and never changes them.
+ */
+moe_status moe_trace_open(const char* path, int32_t mode, uint64_t max_bytes, moe_trace** trace);
+moe_status moe_trace_record(moe_trace* trace, int32_t layer, int64_t position, int32_t n_tokens, int32_t k,
+                            const int32_t* ids, const float* w);
+moe_status moe_trace_close(moe_trace* trace);
+moe_status moe_trace_count(const char* path, int32_t n_layers, int32_t n_experts, int64_t* counts,
+                           int64_t* n_records);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ STATUS = {
     0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_ALIGN",
     -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_LAYOUT", -7: "MOE_ERR_UNSUPPORTED", -8: "MOE_ERR_OVERFLOW",
     -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_ABI", -11: "MOE_ERR_RANGE", -12: "MOE_ERR_SCRATCH_LIMIT",
+    -13: "MOE_ERR_POISONED", -14: "MOE_ERR_STATE", -15: "MOE_ERR_IO",
 }
 
 EXPORTS = [
@@ -32,8 +33,23 @@ EXPORTS = [
     "moe_max_expert_blocks", "moe_expert_blocks", "moe_mxfp4_grouped_gate_up", "moe_mxfp4_grouped_down",
     "moe_mxfp4_dequant", "moe_mxfp4_dequant_bf16", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_bytes",
     "moe_mxfp4_stack_forward", "moe_stack_graph_create", "moe_stack_graph_launch",
-    "moe_stack_graph_destroy",
+    "moe_stack_graph_destroy", "moe_cache_create", "moe_cache_destroy", "moe_cache_slots", "moe_cache_get_stats",
+    "moe_cache_plan", "moe_cache_finish", "moe_cache_cancel", "moe_cache_workspace_bytes", "moe_cache_layer_forward",
+    "moe_route_hint_workspace_bytes", "moe_route_hint", "moe_trace_open", "moe_trace_record", "moe_trace_close",
+    "moe_trace_count",
 ]
+MOE_TRACE_BUFFERED, MOE_TRACE_SYNC = 0, 1
+MOE_CACHE_PREFETCH = 1
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("capacity", ctypes.c_int32), ("poisoned", ctypes.c_int32),
+                ("alloc_retries", ctypes.c_int32), ("plans", ctypes.c_int64), ("hits", ctypes.c_int64),
+                ("misses", ctypes.c_int64), ("prefetched", ctypes.c_int64), ("evictions", ctypes.c_int64),
+                ("bytes_uploaded", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "struct_size"}
 
 
 class MoeError(RuntimeError):
@@ -104,6 +120,22 @@ def lib():
                                             vp, vp, sz, vp, P(vp)], ctypes.c_int),
                 "moe_stack_graph_launch": ([vp, vp], ctypes.c_int),
                 "moe_stack_graph_destroy": ([vp], ctypes.c_int),
+                "moe_cache_create": ([D, i32, i32, i32, P(vp)], ctypes.c_int),
+                "moe_cache_destroy": ([vp], ctypes.c_int),
+                "moe_cache_slots": ([vp, P(vp), P(vp), P(i32)], ctypes.c_int),
+                "moe_cache_get_stats": ([vp, P(CacheStats)], ctypes.c_int),
+                "moe_cache_plan": ([vp, i32, vp, i32, i32, vp, vp, P(i32)], ctypes.c_int),
+                "moe_cache_finish": ([vp, vp, vp, i32, vp], ctypes.c_int),
+                "moe_cache_cancel": ([vp], ctypes.c_int),
+                "moe_cache_workspace_bytes": ([vp, i32, i32, P(sz)], ctypes.c_int),
+                "moe_cache_layer_forward": ([vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz,
+                                             vp], ctypes.c_int),
+                "moe_route_hint_workspace_bytes": ([D, i32, i32, P(sz)], ctypes.c_int),
+                "moe_route_hint": ([D, vp, vp, ctypes.c_float, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+                "moe_trace_open": ([ctypes.c_char_p, i32, ctypes.c_uint64, P(vp)], ctypes.c_int),
+                "moe_trace_record": ([vp, i32, i64, i32, i32, vp, vp], ctypes.c_int),
+                "moe_trace_close": ([vp], ctypes.c_int),
+                "moe_trace_count": ([ctypes.c_char_p, i32, i32, vp, P(i64)], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -338,3 +370,136 @@ class StackGraph:
             self.close()
         except Exception:
             pass
+
+
+class ExpertCache:
+    """moe_cache_*: host-streamed experts with a device residency cache.
+
+    Host spans are numpy arrays (or raw addresses) of one layer's experts in
+    the logical layout, experts back to back; pinned=True when they live in
+    pinned host memory (direct DMA, no staging)."""
+
+    def __init__(self, desc, n_layers, capacity=0, max_retries=4):
+        h = ctypes.c_void_p()
+        _check("moe_cache_create", lib().moe_cache_create(ctypes.byref(desc), n_layers, capacity, max_retries,
+                                                          ctypes.byref(h)))
+        self._h = h
+        self.desc = desc
+        c, s, n = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int32()
+        _check("moe_cache_slots", lib().moe_cache_slots(h, ctypes.byref(c), ctypes.byref(s), ctypes.byref(n)))
+        self.slot_codes, self.slot_scales, self.capacity = c.value, s.value, n.value
+        self.slot_desc = LayerDesc.make(desc.hidden, desc.inter, self.capacity, min(desc.top_k_max, self.capacity))
+
+    def stats(self):
+        st = CacheStats()
+        st.struct_size = ctypes.sizeof(CacheStats)
+        _check("moe_cache_get_stats", lib().moe_cache_get_stats(self._h, ctypes.byref(st)))
+        return st.as_dict()
+
+    def plan(self, layer, ids, prefetch=False):
+        """ids: host int32 array.  Returns (slots [n] or None, ordered miss ids)."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids, np.int32).reshape(-1)
+        slots = None if prefetch else np.empty(ids.size, np.int32)
+        miss = np.empty(ids.size, np.int32)
+        nm = ctypes.c_int32()
+        _check("moe_cache_plan", lib().moe_cache_plan(
+            self._h, layer, ids.ctypes.data, ids.size, MOE_CACHE_PREFETCH if prefetch else 0,
+            None if slots is None else slots.ctypes.data, miss.ctypes.data, ctypes.byref(nm)))
+        return slots, miss[:nm.value].copy()
+
+    def finish(self, miss_codes, miss_scales, pinned=False, stream=None):
+        """miss_codes / miss_scales: per-miss host spans (numpy arrays or addresses), in miss order."""
+        n = len(miss_codes)
+        pc = (ctypes.c_void_p * max(n, 1))()
+        ps = (ctypes.c_void_p * max(n, 1))()
+        for i in range(n):
+            pc[i] = _addr(miss_codes[i])
+            ps[i] = _addr(miss_scales[i])
+        _check("moe_cache_finish", lib().moe_cache_finish(self._h, pc, ps, 1 if pinned else 0, _stream(stream)))
+
+    def cancel(self):
+        _check("moe_cache_cancel", lib().moe_cache_cancel(self._h))
+
+    def workspace_bytes(self, n_tokens, k):
+        b = ctypes.c_size_t()
+        _check("moe_cache_workspace_bytes", lib().moe_cache_workspace_bytes(self._h, n_tokens, k, ctypes.byref(b)))
+        return b.value
+
+    def layer_forward(self, layer, x, router_w, router_bias, host_codes, host_scales, k, out, workspace,
+                      topk_idx_out=None, topk_w_out=None, pinned=False, stream=None):
+        _check("moe_cache_layer_forward", lib().moe_cache_layer_forward(
+            self._h, layer, _ptr(x), _xdtype(x), _ptr(router_w), _ptr(router_bias), _addr(host_codes),
+            _addr(host_scales), 1 if pinned else 0, x.shape[0], k, _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+    def close(self):
+        if self._h:
+            _check("moe_cache_destroy", lib().moe_cache_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _addr(a):
+    """Host address of a numpy array, a torch CPU tensor or a raw integer address."""
+    if isinstance(a, int):
+        return ctypes.c_void_p(a)
+    if hasattr(a, "ctypes"):
+        return ctypes.c_void_p(a.ctypes.data)
+    return ctypes.c_void_p(a.data_ptr())
+
+
+def route_hint_workspace_bytes(desc, n_tokens, k) -> int:
+    b = ctypes.c_size_t()
+    _check("moe_route_hint_workspace_bytes",
+           lib().moe_route_hint_workspace_bytes(ctypes.byref(desc), n_tokens, k, ctypes.byref(b)))
+    return b.value
+
+
+def moe_route_hint(desc, r, gamma_next, eps, router_w_next, router_bias_next, k, hint_idx, workspace, stream=None):
+    _check("moe_route_hint", lib().moe_route_hint(
+        ctypes.byref(desc), _ptr(r), _ptr(gamma_next), eps, _ptr(router_w_next), _ptr(router_bias_next), r.shape[0], k,
+        _ptr(hint_idx), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class RouteTrace:
+    """moe_trace_open / record / close (host arrays)."""
+
+    def __init__(self, path, mode=MOE_TRACE_BUFFERED, max_bytes=0):
+        h = ctypes.c_void_p()
+        _check("moe_trace_open", lib().moe_trace_open(os.fsencode(path), mode, max_bytes, ctypes.byref(h)))
+        self._h = h
+
+    def record(self, layer, position, ids, w):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, np.int32)
+        w = np.ascontiguousarray(w, np.float32)
+        T, k = ids.shape
+        _check("moe_trace_record", lib().moe_trace_record(self._h, layer, position, T, k, ids.ctypes.data,
+                                                          w.ctypes.data))
+
+    def close(self):
+        if self._h:
+            h, self._h = self._h, ctypes.c_void_p()
+            _check("moe_trace_close", lib().moe_trace_close(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def trace_count(path, n_layers, n_experts):
+    """(counts [n_layers, n_experts] int64, number of records) of a router trace."""
+    import numpy as np
+    counts = np.zeros((n_layers, n_experts), np.int64)
+    n = ctypes.c_int64()
+    _check("moe_trace_count", lib().moe_trace_count(os.fsencode(path), n_layers, n_experts, counts.ctypes.data,
+                                                    ctypes.byref(n)))
+    return counts, n.value

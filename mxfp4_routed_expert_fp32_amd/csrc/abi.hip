@@ -315,6 +315,9 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_ABI: return "descriptor ABI version or size mismatch";
     case MOE_ERR_RANGE: return "an index argument is out of range";
     case MOE_ERR_SCRATCH_LIMIT: return "the call needs more than the library's static scratch";
+    case MOE_ERR_POISONED: return "the residency cache failed earlier and refuses further work";
+    case MOE_ERR_STATE: return "call out of order for the object's state";
+    case MOE_ERR_IO: return "a file operation failed, or the trace reached its size limit";
     default: return "unknown status";
   }
 }
@@ -593,6 +596,48 @@ moe_status moe_residual_add(float* r, const float* dlt, int64_t n, void* stream)
   if (!r || !dlt) return MOE_ERR_NULL;
   if (n < 0) return MOE_ERR_SHAPE;
   return dev(moe::launch_residual_add(r, dlt, (size_t)n, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- next-layer route hint
+
+static moe_status hint_layout(const moe_layer_desc* d, int32_t T, int32_t k, size_t* nout_off, size_t* w_off,
+                              size_t* total) {
+  MOE_TRY(check_desc(d));
+  MOE_TRY(check_tokens(T, k, d));
+  size_t lg, nb, wb;
+  if (!mul_ok((size_t)T * (size_t)d->n_experts, 4, &lg) || !mul_ok((size_t)T * (size_t)d->hidden, 4, &nb) ||
+      !mul_ok((size_t)T * (size_t)k, 4, &wb))
+    return MOE_ERR_OVERFLOW;
+  Carve c;
+  c.take(lg);
+  *nout_off = c.take(nb);
+  *w_off = c.take(wb);
+  *total = c.take(0);
+  return c.overflow ? MOE_ERR_OVERFLOW : MOE_OK;
+}
+
+moe_status moe_route_hint_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens, int32_t k, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  size_t a, b;
+  return hint_layout(d, n_tokens, k, &a, &b, bytes);
+}
+
+moe_status moe_route_hint(const moe_layer_desc* d, const float* r, const float* gamma, float eps, const float* router_w,
+                          const float* router_bias, int32_t n_tokens, int32_t k, int32_t* hint_idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!r || !gamma || !router_w || !hint_idx || !workspace) return MOE_ERR_NULL;
+  size_t nout_off, w_off, total;
+  MOE_TRY(hint_layout(d, n_tokens, k, &nout_off, &w_off, &total));
+  if (d->hidden % 4 || d->hidden > 8192) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(r) || !aligned16(gamma) || !aligned16(router_w) || !aligned16(workspace)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < total) return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws);
+  hipStream_t s = as_stream(stream);
+  MOE_TRY(dev(moe::launch_norm_router_logits(r, gamma, eps, router_w, router_bias, n_tokens, d->hidden, d->n_experts,
+                                             logits, reinterpret_cast<float*>(ws + nout_off), s)));
+  return dev(moe::launch_topk_softmax(logits, n_tokens, d->n_experts, k, hint_idx,
+                                      reinterpret_cast<float*>(ws + w_off), s));
 }
 
 // ---------------------------------------------------------------- layer stack + graph
