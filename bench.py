@@ -1,14 +1,16 @@
 """Benchmark of the routed MXFP4 MoE layer on one MI355X.
 
-The default run (`--workload all`) measures the four model-shape workloads in
-one process and prints ONE JSON line.  Its top-level figures are single-token
+The default run (`--workload all`) measures the model-shape workloads in one
+process and prints ONE JSON line.  Its top-level figures are single-token
 decode of one K3-shape layer (H=7168, I=1536, E=896, top-16, bf16
-activations, every expert resident in HBM); the other three are sub-objects
-under "workloads":
+activations, every expert resident in HBM); the others are sub-objects under
+"workloads":
   - decode64_zipf: 64 tokens per step, Zipf(1.1) router bias;
   - prefill4096: 4096 tokens per step, uniform routing (grouped GEMMs on MFMA);
   - stack12: 12 layers with RMSNorm + residual, one token per step, replayed
-    as a HIP graph.
+    as a HIP graph (plus the next-layer route hint's accuracy);
+  - decode_streamed: the decode workload with the experts in host memory and
+    a device residency cache (host-link GB/s, pageable and pinned).
 A step is one call of the layer (or of the stack graph).  Decode steps
 rotate over a pool of 256 distinct seeded tokens and batch steps over
 distinct token batches, so consecutive steps route to different experts and
@@ -39,8 +41,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MXFP4_PEAK_TFLOPS = 10100.0
 
-WORKLOADS = ["decode", "decode64_zipf", "prefill4096", "stack12"]
-DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096": (20, 3), "stack12": (100, 10)}
+WORKLOADS = ["decode", "decode64_zipf", "prefill4096", "stack12", "decode_streamed"]
+DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096": (20, 3), "stack12": (100, 10),
+                 "decode_streamed": (40, 0)}
 
 
 def parse():
@@ -506,8 +509,23 @@ def bench_stack(a, ctx, steps, warmup):
     log("stack12: %d layers resident in %.1f s" % (w.layers, time.time() - t0))
     pool = sd.tokens(w, range(a.pool))
     # refusal gate: every layer against the oracle, from the GPU's residual before it
-    (nw, ew), eager0 = stack_layer_by_layer(w, desc, layers, gam, pool[0:1].contiguous(), 1, w.eps, w.k)
+    (nw, ew), eager0, inputs = stack_layer_by_layer(w, desc, layers, gam, pool[0:1].contiguous(), 1, w.eps, w.k)
     log("stack12: parity ok, 12 layers (normwise %.3g, elementwise %.3g)" % (nw, ew))
+    # next-layer route hint (prefetch only): the top-k of layer l's norm +
+    # router on the input of layer l-1, against layer l's actual route (the
+    # same function on layer l's input); overlap of the two sets
+    hws = torch.empty(moe.route_hint_workspace_bytes(desc, 1, w.k), dtype=torch.uint8, device=dev)
+    hint = torch.empty(1, w.k, dtype=torch.int32, device=dev)
+    route = torch.empty(1, w.k, dtype=torch.int32, device=dev)
+    overlaps = []
+    for l in range(1, w.layers):
+        moe.moe_route_hint(desc, torch.from_numpy(inputs[l - 1]).to(dev), gam[l], w.eps, layers[l][2], None, w.k,
+                           hint, hws)
+        moe.moe_route_hint(desc, torch.from_numpy(inputs[l]).to(dev), gam[l], w.eps, layers[l][2], None, w.k,
+                           route, hws)
+        torch.cuda.synchronize()
+        overlaps.append(len(set(hint.cpu().numpy()[0].tolist()) & set(route.cpu().numpy()[0].tolist())) / w.k)
+    log("stack12: next-layer hint overlap %.3f" % float(np.mean(overlaps)))
     x = torch.empty(1, w.H, dtype=torch.bfloat16, device=dev)
     resid = torch.empty(1, w.H, dtype=torch.float32, device=dev)
     ws = torch.empty(moe.stack_workspace_bytes(desc, 1, w.k), dtype=torch.uint8, device=dev)
@@ -533,7 +551,11 @@ def bench_stack(a, ctx, steps, warmup):
     cfg = {"workload": "stack12: 12 layers x (RMSNorm eps=1e-6 + MoE H=7168 I=1536 E=896 k=16 + residual), T=1, "
                        "hipGraph replay, 256-token rotating pool",
            "global_batch": 1, "bytes_per_token": per_tok, "GBps": gbps, "ms_per_token_eager": ms_eager,
-           "graph_equals_eager": True}
+           "graph_equals_eager": True,
+           "route_hint": {"mean_overlap": float(np.mean(overlaps)), "min_overlap": float(np.min(overlaps)),
+                          "layers": w.layers - 1, "tokens": 1,
+                          "what": "fraction of layer l's routed experts that the hint computed from layer l-1's "
+                                  "input predicts (prefetch only; never used for compute)"}}
     roofline = {"bound": "hbm", "kernel": "whole step (12 layers, graph replay)", "achieved": gbps,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBS, "traffic": None,
                 "bytes_per_launch": per_tok, "avg_launch_us": ms_graph * 1e3}
@@ -541,6 +563,89 @@ def bench_stack(a, ctx, steps, warmup):
     log("stack12: %.3f ms/token (eager %.3f), frac %.3f" % (ms_graph, ms_eager, gbps / HBM_PEAK_GBS))
     return base_fields("12-layer MoE stack decode tokens/s", 1.0 / (ms_graph * 1e-3), "tokens/s", steps, warmup,
                        ms_graph, spread, cfg, roofline, parity_obj([0], nw, ew))
+
+
+# --------------------------------------------------------------------------- host-streamed decode
+
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_streamed(a, ctx, steps):
+    """Single-token decode of the model-shape layer with its experts in host
+    memory and a 256-slot device residency cache: each step routes on the
+    device, reads the route back, plans, uploads the misses and runs the
+    experts on the cache's slots.  Measured with pageable host memory (two
+    pinned staging slabs) and with pinned host memory (direct DMA)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as sd
+    import mxfp4_routed_expert_fp32_amd as moe
+
+    w = synth.WORKLOADS["decode"]
+    desc = sd.desc_for(w)
+    dev = "cuda"
+    k, H, E = w.k, w.H, w.E
+    t0 = time.time()
+    host_c, host_s = synth.experts(w, 0)          # 15.72 GB of pageable host memory
+    log("decode_streamed: layer 0 in host memory in %.1f s" % (time.time() - t0))
+    pool = sd.tokens(w, range(a.pool))
+    out = torch.empty(1, H, dtype=torch.float32, device=dev)
+    ref = torch.empty(1, H, dtype=torch.float32, device=dev)
+    ws_r = torch.empty(moe.workspace_bytes(desc, 1, k), dtype=torch.uint8, device=dev)
+    res = {}
+    for mode in ("pageable", "pinned"):
+        if mode == "pinned":
+            t0 = time.time()
+            pc = torch.empty(host_c.size, dtype=torch.uint8, pin_memory=True)
+            ps = torch.empty(host_s.size, dtype=torch.uint8, pin_memory=True)
+            pc.numpy()[:] = host_c
+            ps.numpy()[:] = host_s
+            src = (pc, ps)
+            log("decode_streamed: pinned copy in %.1f s" % (time.time() - t0))
+        else:
+            src = (host_c, host_s)
+        cache = moe.ExpertCache(desc, 1, capacity=256)
+        ws = torch.empty(cache.workspace_bytes(1, k), dtype=torch.uint8, device=dev)
+        # gate: bit-identical to the all-resident forward on two tokens
+        for t in (0, 1):
+            x = pool[t:t + 1]
+            moe.moe_mxfp4_forward(desc, x, ctx.wr, None, ctx.codes, ctx.scales, k, ref, ws_r)
+            cache.layer_forward(0, x, ctx.wr, None, src[0], src[1], k, out, ws, pinned=(mode == "pinned"))
+            torch.cuda.synchronize()
+            if not torch.equal(out.view(torch.int32), ref.view(torch.int32)):
+                refuse("streamed layer differs from the resident forward")
+        s0 = cache.stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            x = pool[(2 + i) % a.pool:(2 + i) % a.pool + 1]
+            cache.layer_forward(0, x, ctx.wr, None, src[0], src[1], k, out, ws, pinned=(mode == "pinned"))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        s1 = cache.stats()
+        up = s1["bytes_uploaded"] - s0["bytes_uploaded"]
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        gbps = up / dt / 1e9
+        res[mode] = {"tokens_per_s": steps / dt, "ms_per_token": dt * 1e3 / steps, "host_link_GBps": gbps,
+                     "frac_host_link": gbps / HOST_LINK_PEAK_GBS, "hits": hits, "misses": misses,
+                     "bytes_uploaded": up, "capacity_slots": cache.capacity}
+        log("decode_streamed %s: %.2f ms/token, %.1f GB/s host link, %d hits / %d misses" % (
+            mode, dt * 1e3 / steps, gbps, hits, misses))
+        cache.close()
+        del src
+    best = res["pinned"]
+    cfg = {"workload": "decode_streamed: decode workload (T=1, K3 shape) with the 896 experts in host memory and a "
+                       "256-slot device residency cache (LRU), 256-token rotating pool",
+           "global_batch": 1, "pageable": res["pageable"], "pinned": res["pinned"]}
+    roofline = {"bound": "host-link", "kernel": "expert uploads host -> device (pinned host memory, direct DMA)",
+                "achieved": best["host_link_GBps"], "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                "frac": best["host_link_GBps"] / HOST_LINK_PEAK_GBS, "traffic": None,
+                "bytes_per_launch": best["bytes_uploaded"] / steps, "avg_launch_us": best["ms_per_token"] * 1e3}
+    return base_fields("MoE-layer tokens/s (decode, experts streamed from host memory)", best["tokens_per_s"],
+                       "tokens/s", steps, 0, best["ms_per_token"], None, cfg, roofline,
+                       {"tokens_checked": [0, 1], "bit_identical_to_resident_forward": True})
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -614,6 +719,8 @@ def main():
             results[name] = bench_decode(a, ctx, steps, warmup)
         elif name == "stack12":
             results[name] = bench_stack(a, ctx, steps, warmup)
+        elif name == "decode_streamed":
+            results[name] = bench_streamed(a, ctx, steps)
         else:
             results[name] = bench_batch(a, ctx, name, steps, warmup)
     res = results[primary]

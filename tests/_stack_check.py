@@ -18,7 +18,8 @@ def stack_layer_by_layer(w, desc, layers, gam, x, T, eps, k):
     the oracle normalises it, takes the GPU's router logits of those rows for
     selection (moe_rmsnorm + moe_router_logits give the stack kernel's bits),
     runs the layer and adds the residual.  Returns the worst (normwise,
-    elementwise) errors and the GPU residual after the last layer."""
+    elementwise) errors, the GPU residual after the last layer, and the GPU
+    residual entering each layer (its input before the norm)."""
     L = len(layers)
     ws = torch.empty(moe.stack_workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
     resid = torch.empty(T, w.H, dtype=torch.float32, device=DEV)
@@ -27,7 +28,9 @@ def stack_layer_by_layer(w, desc, layers, gam, x, T, eps, k):
     else:
         r_prev = x.cpu().numpy()
     worst = (0.0, 0.0)
+    inputs = []
     for l in range(L):
+        inputs.append(r_prev)
         moe.moe_mxfp4_stack_forward(desc, [a[0] for a in layers[:l + 1]], [a[1] for a in layers[:l + 1]],
                                     [a[2] for a in layers[:l + 1]], None, gam[:l + 1], eps, x, k, resid, ws)
         torch.cuda.synchronize()
@@ -50,4 +53,4 @@ def stack_layer_by_layer(w, desc, layers, gam, x, T, eps, k):
         ew = P.assert_elementwise(r_gpu, r_ref, A)
         worst = (max(worst[0], nw), max(worst[1], ew))
         r_prev = r_gpu
-    return worst, r_prev
+    return worst, r_prev, inputs

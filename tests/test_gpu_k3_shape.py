@@ -171,7 +171,7 @@ def test_stack_twelve_layers_layer_by_layer(k3_layer):
         layers.append((c, s, sd.router_w(w, l)))
     gam = [sd.gamma(w, l) for l in range(w.layers)]
     x = sd.tokens(w, [3])
-    worst, eager = stack_layer_by_layer(w, desc, layers, gam, x, 1, w.eps, w.k)
+    worst, eager, _ = stack_layer_by_layer(w, desc, layers, gam, x, 1, w.eps, w.k)
     print("stack12 layer-by-layer worst normwise %.3g elementwise %.3g" % worst)
     resid = torch.empty(1, w.H, dtype=torch.float32, device=DEV)
     ws = torch.empty(moe.stack_workspace_bytes(desc, 1, w.k), dtype=torch.uint8, device=DEV)
