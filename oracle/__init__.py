@@ -56,6 +56,10 @@ def lib():
             L.oracle_moe_experts.restype = ctypes.c_int
             L.oracle_moe_abs_scale.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
             L.oracle_moe_abs_scale.restype = ctypes.c_int
+            L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+            L.oracle_f16_to_f32.restype = f32
+            L.oracle_int8_dequant.argtypes = [vp, vp, i64, i64, vp]
+            L.oracle_int8_gemv.argtypes = [vp, vp, i64, i64, vp, i64, vp]
             L.oracle_rmsnorm.argtypes = [vp, vp, f32, i64, i64, vp]
             L.oracle_residual_add.argtypes = [vp, vp, i64]
             _lib = L
@@ -213,6 +217,32 @@ def moe_abs_scale(x, idx, w, experts, H: int, I: int, E: int, nthreads: int = 0)
     if rc != 0:
         raise RuntimeError("oracle_moe_abs_scale failed with %d" % rc)
     return A
+
+
+def f16_to_f32(h: int) -> float:
+    return lib().oracle_f16_to_f32(h)
+
+
+def int8_dequant(q, s_f16_bits) -> np.ndarray:
+    """W[n, k] = q[n, k] * s[n] for packed int8 rows q [N, K] and fp16 scale bits s [N]."""
+    q = _c(q, np.int8)
+    s = _c(s_f16_bits, np.uint16)
+    N, K = q.shape
+    out = np.empty((N, K), np.float32)
+    lib().oracle_int8_dequant(q.ctypes.data, s.ctypes.data, N, K, out.ctypes.data)
+    return out
+
+
+def int8_gemv(q, s_f16_bits, x) -> np.ndarray:
+    """y [T, N] = x [T, K] . W^T with W = q * s (fp32, ascending k)."""
+    q = _c(q, np.int8)
+    s = _c(s_f16_bits, np.uint16)
+    x = _c(x, np.float32)
+    N, K = q.shape
+    T = x.shape[0]
+    y = np.empty((T, N), np.float32)
+    lib().oracle_int8_gemv(q.ctypes.data, s.ctypes.data, N, K, x.ctypes.data, T, y.ctypes.data)
+    return y
 
 
 def rmsnorm(r, gamma, eps: float) -> np.ndarray:

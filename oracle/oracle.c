@@ -408,6 +408,56 @@ done:
     return rc;
 }
 
+/* ---------------------------------------------------------------- packed-int8 rows */
+
+/* IEEE binary16 -> fp32, from the bit fields: sign bit 15, exponent bits 14-10
+ * (bias 15), mantissa bits 9-0; exponent 0 is subnormal (mantissa * 2^-24),
+ * exponent 31 is inf (mantissa 0) or NaN.  Every binary16 value is exact in
+ * fp32. */
+float oracle_f16_to_f32(uint16_t h) {
+    unsigned sign = (h >> 15) & 1u, ex = (h >> 10) & 0x1Fu, man = h & 0x3FFu;
+    double mag;
+    if (ex == 0x1Fu) {
+        if (man) return NAN;
+        mag = INFINITY;
+    } else if (ex == 0) {
+        mag = ldexp((double)man, -24);
+    } else {
+        mag = ldexp(1.0 + (double)man / 1024.0, (int)ex - 15);
+    }
+    return (float)(sign ? -mag : mag);
+}
+
+/* A resident-spine matrix in packed int8 with one fp16 scale per row (the
+ * pages' explicit int8 spine: row rounding and fp16 scales, so not
+ * weight-exact with respect to the source weights; "Deltafin's custom
+ * compiled runtime", section "Weight fidelity"): W[n][k] = q[n][k] * s[n].
+ * The product of an int8 and a binary16 value has at most 7 + 11 significant
+ * bits, so it is exact in fp32 (brain.bigb.es "deltafin", section "The
+ * techniques that bought the 82x": the fused int8 -> fp32 + scale copy
+ * reproduces the weights with max|diff| = 0). */
+void oracle_int8_dequant(const int8_t* q, const uint16_t* s, int64_t rows, int64_t cols, float* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < rows; ++n) {
+        float sc = oracle_f16_to_f32(s[n]);
+        for (int64_t c = 0; c < cols; ++c) out[n * cols + c] = (float)q[n * cols + c] * sc;
+    }
+}
+
+/* y[t][n] = sum_k W[n][k] * x[t][k], W as oracle_int8_dequant, fp32, ascending k. */
+void oracle_int8_gemv(const int8_t* q, const uint16_t* s, int64_t rows, int64_t cols, const float* x,
+                      int64_t T, float* y) {
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < rows; ++n) {
+            float sc = oracle_f16_to_f32(s[n]);
+            float acc = 0.0f;
+            for (int64_t k = 0; k < cols; ++k) acc = acc + ((float)q[n * cols + k] * sc) * x[t * cols + k];
+            y[t * rows + n] = acc;
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- stack parts */
 
 /* RMSNorm with gain: n = r * (1 / sqrt(mean(r^2) + eps)) * gamma, per token;

@@ -14,6 +14,9 @@
   included) and the forward on the same routing.
 - Magnitude scale of the elementwise error bar: fp64 numpy and a closed form.
 - RMSNorm: constant-vector closed form and fp64.
+- Packed-int8 rows: binary16 decode against numpy's float16 over all 65536
+  patterns; int8 dequant bit-exact against fp64 products; the GEMV against
+  fp64 within the textbook summation bound.
 """
 import os
 import shutil
@@ -355,6 +358,36 @@ def test_residual_add():
                           np.array([[1.5, -1.5, 0.0]], np.float32))
 
 
+# ------------------------------------------------------------------ packed-int8 rows
+
+def test_f16_decode_matches_numpy_all_patterns():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(v)) for v in h], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(bits(got)[~nan], bits(ref)[~nan])
+
+
+def test_int8_dequant_exact_and_gemv_within_bound():
+    rng = np.random.default_rng(12)
+    N, K, T = 40, 320, 3
+    q = rng.integers(-128, 128, (N, K), dtype=np.int64).astype(np.int8)
+    s = (rng.uniform(0.5, 1.5, N) * 2.0 ** -9).astype(np.float16)
+    s[3] = np.float16(6.0e-8)           # a subnormal scale
+    s[4] = np.float16(-0.25)            # a negative scale
+    w = oracle.int8_dequant(q, s.view(np.uint16))
+    ref = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    assert np.array_equal(bits(w), bits(ref.astype(np.float32)))
+    assert np.all(w.astype(np.float64) == ref)          # every product exact in fp32
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    y = oracle.int8_gemv(q, s.view(np.uint16), x).astype(np.float64)
+    y64 = x.astype(np.float64) @ ref.T
+    bound = K * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(ref).T)
+    assert np.all(np.abs(y - y64) <= bound)
+    assert np.any(y != y64.astype(np.float32))          # really fp32, not a wider type
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 MUTANTS = {
@@ -365,6 +398,7 @@ MUTANTS = {
     "ties to higher index": ("return ia < ib;\n}", "return ia > ib;\n}"),
     "block axis wrong": ("scales[n * (cols / 32) + c / 32]", "scales[(n / 32) * (cols / 32) + c % (cols / 32)]"),
     "combine drops last rank": ("for (int64_t j = 0; j < k; ++j) acc = acc + w", "for (int64_t j = 0; j + 1 < k; ++j) acc = acc + w"),
+    "fp16 exponent bias off by one": ("(int)ex - 15);", "(int)ex - 14);"),
 }
 
 
@@ -375,7 +409,7 @@ def _pins_pass(lib_path):
     orig = oracle._LIB_PATH
     try:
         oracle._LIB_PATH = lib_path
-        checks = [test_dequant_exhaustive_enumeration,
+        checks = [test_dequant_exhaustive_enumeration, test_f16_decode_matches_numpy_all_patterns,
                   lambda: test_dequant_nibble_order_worked_example(os.path.join(os.path.dirname(__file__), "golden")),
                   lambda: test_layer_matches_dense_fp64(0, (256, 128, 8, 2)),
                   lambda: test_layer_matches_dense_fp64(4, (96, 64, 16, 4)),
