@@ -10,7 +10,8 @@ activations, every expert resident in HBM); the others are sub-objects under
   - stack12: 12 layers with RMSNorm + residual, one token per step, replayed
     as a HIP graph (plus the next-layer route hint's accuracy);
   - decode_streamed: the decode workload with the experts in host memory and
-    a device residency cache (host-link GB/s, pageable and pinned).
+    a device residency cache (host-link GB/s, pageable and pinned);
+  - spine_int8: the packed-int8 resident-spine GEMV (12288 x 7168).
 A step is one call of the layer (or of the stack graph).  Decode steps
 rotate over a pool of 256 distinct seeded tokens and batch steps over
 distinct token batches, so consecutive steps route to different experts and
@@ -41,9 +42,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MXFP4_PEAK_TFLOPS = 10100.0
 
-WORKLOADS = ["decode", "decode64_zipf", "prefill4096", "stack12", "decode_streamed"]
+WORKLOADS = ["decode", "decode64_zipf", "prefill4096", "stack12", "decode_streamed", "spine_int8"]
 DEFAULT_STEPS = {"decode": (400, 40), "decode64_zipf": (100, 10), "prefill4096": (20, 3), "stack12": (100, 10),
-                 "decode_streamed": (40, 0)}
+                 "decode_streamed": (40, 0), "spine_int8": (200, 20)}
 
 
 def parse():
@@ -648,6 +649,68 @@ def bench_streamed(a, ctx, steps):
                        {"tokens_checked": [0, 1], "bit_identical_to_resident_forward": True})
 
 
+# --------------------------------------------------------------------------- packed-int8 spine GEMV
+
+def bench_int8(a, steps, warmup):
+    """The resident-spine GEMV of packed-int8 rows with fp16 row scales at the
+    pages' 12288 x 7168 shape, one fp32 token; launches rotate over four
+    distinct matrices (352 MB, more than the 256 MB last-level cache)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import mxfp4_routed_expert_fp32_amd as moe
+    from tests import _parity as P
+
+    N, K, NM = 12288, 7168, 4
+    dev = "cuda"
+    mats = []
+    for m in range(NM):
+        q, s = synth.int8_rows(100 + m, N, K)
+        mats.append((q, s, torch.from_numpy(q).to(dev), torch.from_numpy(s.view(np.int16)).to(dev)))
+    x = synth.normal_f32(synth.key(5, 0, 1, 777), K).reshape(1, K)
+    xd = torch.from_numpy(x).to(dev)
+    y = torch.empty(1, N, dtype=torch.float32, device=dev)
+    # gate: every row of matrix 0 against the oracle, both readings
+    moe.moe_int8_gemv(mats[0][2], mats[0][3], xd, y)
+    torch.cuda.synchronize()
+    ref = oracle.int8_gemv(mats[0][0], mats[0][1], x)
+    W = oracle.int8_dequant(mats[0][0], mats[0][1]).astype(np.float64)
+    A = np.abs(x).astype(np.float64) @ np.abs(W).T
+    got = y.cpu().numpy()
+    nw_, ew_ = float(P.normwise_err(got, ref).max()), P.elementwise_ratio(got, ref, A)
+    if not (nw_ <= P.OUT_TOL and ew_ <= P.OUT_TOL):
+        refuse("int8 GEMV: normwise %g, elementwise %g" % (nw_, ew_))
+    log("spine_int8: parity ok (normwise %.3g, elementwise %.3g)" % (nw_, ew_))
+    bytes_per = N * K + N * 2 + K * 4 + N * 4
+    sweep = {}
+    for rpw in (0, 16, 24, 32, 40, 56, 64):
+        us = kernel_us(lambda i: moe.moe_int8_gemv(mats[i % NM][2], mats[i % NM][3], xd, y, rows_per_workgroup=rpw),
+                       max(steps, 4 * NM), warmup)
+        sweep[rpw] = us
+    best = min(sweep, key=sweep.get)
+    us = sweep[0]
+    ach = bytes_per / (us * 1e-6) / 1e9
+    out = torch.empty(N, K, dtype=torch.float32, device=dev)
+    dq_us = kernel_us(lambda i: moe.moe_int8_dequant(mats[i % NM][2], mats[i % NM][3], out), max(steps, 4 * NM),
+                      warmup)
+    dq_bytes = N * K + N * 2 + N * K * 4
+    log("spine_int8: %.1f us per GEMV (%.0f GB/s, frac %.3f); dequant export %.1f us (%.0f GB/s)" % (
+        us, ach, ach / HBM_PEAK_GBS, dq_us, dq_bytes / (dq_us * 1e-6) / 1e9))
+    cfg = {"workload": "spine_int8: packed-int8 rows with fp16 row scales, 12288 x 7168, one fp32 token, four "
+                       "rotating matrices", "global_batch": 1,
+           "rows_per_workgroup_sweep_us": {str(k_): v for k_, v in sweep.items()}, "best_rows_per_workgroup": best,
+           "dequant_export": {"avg_launch_us": dq_us, "bytes_per_launch": dq_bytes,
+                              "GBps": dq_bytes / (dq_us * 1e-6) / 1e9,
+                              "frac": dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+    roofline = {"bound": "hbm", "kernel": "k_int8_gemv (default split)", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_per,
+                "avg_launch_us": us}
+    return base_fields("packed-int8 spine GEMV rows/s (12288 x 7168)", N / (us * 1e-6), "rows/s", max(steps, 4 * NM),
+                       warmup, us * 1e-3, None, cfg, roofline, parity_obj([0], nw_, ew_))
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def cpu_info():
@@ -721,6 +784,8 @@ def main():
             results[name] = bench_stack(a, ctx, steps, warmup)
         elif name == "decode_streamed":
             results[name] = bench_streamed(a, ctx, steps)
+        elif name == "spine_int8":
+            results[name] = bench_int8(a, steps, warmup)
         else:
             results[name] = bench_batch(a, ctx, name, steps, warmup)
     res = results[primary]

@@ -512,6 +512,29 @@ moe_status moe_cache_layer_forward(moe_expert_cache* cache, int32_t layer, const
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Packed-int8 rows with one fp16 scale per row: the resident-spine matrices
+ * of the pages' explicit, non-weight-exact int8 option ("Deltafin's custom
+ * compiled runtime", section "Weight fidelity": row rounding and fp16 scales;
+ * the 12288 x 7168 packed-int8 shape of section "One native build and test
+ * graph").  q [rows][cols] int8 row-major, scales_f16 [rows] IEEE binary16
+ * bits; W[n][k] = q[n][k] * s[n], exact in fp32.
+ *  - moe_int8_dequant: out [rows][cols] fp32 = W, bit for bit (the fused
+ *    int8 -> fp32 + scale copy of brain.bigb.es "deltafin", section "The
+ *    techniques that bought the 82x").
+ *  - moe_int8_gemv: y [n_tokens][rows] fp32 = x [n_tokens][cols] . W^T, fp32
+ *    accumulation, 1 <= n_tokens <= 4, x fp32 or bf16; rows_per_workgroup 0
+ *    picks the default split (else a multiple of 8, for tuning).
+ * cols a multiple of 16, at most 16384 (MOE_ERR_UNSUPPORTED above); rows at
+ * most 2^20.  q, x, y and out 16-byte aligned.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED,
+ * MOE_ERR_DEVICE.
+ */
+moe_status moe_int8_dequant(const int8_t* q, const uint16_t* scales_f16, int32_t rows, int32_t cols, float* out,
+                            void* stream);
+moe_status moe_int8_gemv(const int8_t* q, const uint16_t* scales_f16, int32_t rows, int32_t cols, const void* x,
+                         moe_dtype x_dtype, int32_t n_tokens, float* y, int32_t rows_per_workgroup, void* stream);
+
+/*
  * Next-layer route hint ("Deltafin's custom compiled runtime", section "Exact
  * next-layer expert prefetch"; "How the native runtime works", section
  * "Automatic PILOT prefetch and CUDA expert residency"): the k experts the

@@ -36,7 +36,7 @@ EXPORTS = [
     "moe_stack_graph_destroy", "moe_cache_create", "moe_cache_destroy", "moe_cache_slots", "moe_cache_get_stats",
     "moe_cache_plan", "moe_cache_finish", "moe_cache_cancel", "moe_cache_workspace_bytes", "moe_cache_layer_forward",
     "moe_route_hint_workspace_bytes", "moe_route_hint", "moe_trace_open", "moe_trace_record", "moe_trace_close",
-    "moe_trace_count",
+    "moe_trace_count", "moe_int8_dequant", "moe_int8_gemv",
 ]
 MOE_TRACE_BUFFERED, MOE_TRACE_SYNC = 0, 1
 MOE_CACHE_PREFETCH = 1
@@ -136,6 +136,8 @@ def lib():
                 "moe_trace_record": ([vp, i32, i64, i32, i32, vp, vp], ctypes.c_int),
                 "moe_trace_close": ([vp], ctypes.c_int),
                 "moe_trace_count": ([ctypes.c_char_p, i32, i32, vp, P(i64)], ctypes.c_int),
+                "moe_int8_dequant": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+                "moe_int8_gemv": ([vp, vp, i32, i32, vp, i32, i32, vp, i32, vp], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -503,3 +505,16 @@ def trace_count(path, n_layers, n_experts):
     _check("moe_trace_count", lib().moe_trace_count(os.fsencode(path), n_layers, n_experts, counts.ctypes.data,
                                                     ctypes.byref(n)))
     return counts, n.value
+
+
+def moe_int8_dequant(q, scales_f16, out, stream=None):
+    """q: int8 [N, K]; scales_f16: int16/float16 [N] (binary16 bits); out: fp32 [N, K]."""
+    N, K = q.shape
+    _check("moe_int8_dequant", lib().moe_int8_dequant(_ptr(q), _ptr(scales_f16), N, K, _ptr(out), _stream(stream)))
+
+
+def moe_int8_gemv(q, scales_f16, x, y, rows_per_workgroup=0, stream=None):
+    """y [T, N] = x [T, K] . (q * s)^T."""
+    N, K = q.shape
+    _check("moe_int8_gemv", lib().moe_int8_gemv(_ptr(q), _ptr(scales_f16), N, K, _ptr(x), _xdtype(x), x.shape[0],
+                                                _ptr(y), rows_per_workgroup, _stream(stream)))

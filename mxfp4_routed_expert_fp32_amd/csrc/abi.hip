@@ -598,6 +598,37 @@ moe_status moe_residual_add(float* r, const float* dlt, int64_t n, void* stream)
   return dev(moe::launch_residual_add(r, dlt, (size_t)n, as_stream(stream)));
 }
 
+// ---------------------------------------------------------------- packed-int8 rows
+
+static moe_status int8_check(const int8_t* q, const uint16_t* sc, int32_t rows, int32_t cols, const void* out) {
+  if (!q || !sc || !out) return MOE_ERR_NULL;
+  if (rows < 1 || rows > (1 << 20) || cols < 16 || cols % 16) return MOE_ERR_SHAPE;
+  if (cols > 16384) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status moe_int8_gemv(const int8_t* q, const uint16_t* scales_f16, int32_t rows, int32_t cols, const void* x,
+                         moe_dtype x_dtype, int32_t n_tokens, float* y, int32_t rows_per_workgroup, void* stream) {
+  MOE_TRY(int8_check(q, scales_f16, rows, cols, y));
+  if (!x) return MOE_ERR_NULL;
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (n_tokens < 1 || n_tokens > 4) return MOE_ERR_SHAPE;
+  if (rows_per_workgroup < 0 || rows_per_workgroup % 8 || (int64_t)rows_per_workgroup * cols >= (int64_t{1} << 31))
+    return MOE_ERR_SHAPE;
+  const int rpw = rows_per_workgroup ? rows_per_workgroup : moe::int8_rows_per_wg(rows, cols);
+  if ((size_t)n_tokens * rpw * ((cols + 1023) / 1024) * 4 > 65536) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_int8_gemv(q, scales_f16, rows, cols, x, x_dtype == MOE_DTYPE_F32, n_tokens, y, rpw,
+                                   as_stream(stream)));
+}
+
+moe_status moe_int8_dequant(const int8_t* q, const uint16_t* scales_f16, int32_t rows, int32_t cols, float* out,
+                            void* stream) {
+  MOE_TRY(int8_check(q, scales_f16, rows, cols, out));
+  return dev(moe::launch_int8_dequant(q, scales_f16, rows, cols, out, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- next-layer route hint
 
 static moe_status hint_layout(const moe_layer_desc* d, int32_t T, int32_t k, size_t* nout_off, size_t* w_off,

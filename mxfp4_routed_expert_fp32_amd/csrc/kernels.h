@@ -77,6 +77,13 @@ hipError_t launch_router_mfma(const uint16_t* x, const float* wr, const float* b
 hipError_t launch_router_reduce_topk(const float* part, int nsplit, int T, int E, const float* bias, int k,
                                      float* logits, int32_t* idx, float* w, hipStream_t s);
 
+// Packed-int8 rows with fp16 row scales: y [T][N] = x [T][K] . (q * s)^T for
+// T <= 4 (rows_per_wg <= 0: the default split), and the fp32 export of q * s.
+int int8_rows_per_wg(int N, int K);
+hipError_t launch_int8_gemv(const int8_t* q, const uint16_t* s, int N, int K, const void* x, bool x_f32, int T,
+                            float* y, int rows_per_wg, hipStream_t st);
+hipError_t launch_int8_dequant(const int8_t* q, const uint16_t* s, int N, int K, float* out, hipStream_t st);
+
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // via_bf16: decode through the bf16 conversion of the bf16 GEMV and the MFMA
 // kernels (widened to fp32), else through the fp32 conversion.

@@ -27,6 +27,7 @@ BASE_SEED = 0x4D4F45  # "MOE"
 # tensor ids inside the stream key (kept in step with synth.c)
 T_X, T_ROUTER_W, T_GATE_CODES, T_UP_CODES, T_DOWN_CODES = 1, 2, 3, 4, 5
 T_GATE_SCALES, T_UP_SCALES, T_DOWN_SCALES, T_GAMMA, T_ZIPF_PERM = 6, 7, 8, 9, 10
+T_INT8_CODES, T_INT8_SCALES = 11, 12
 
 
 def build(force: bool = True) -> str:
@@ -240,3 +241,14 @@ def experts(w: Workload, layer: int = 0, e0: int = 0, count=None):
     s = np.empty(count * w.scale_bytes_per_expert, np.uint8)
     experts_into(w, layer, e0, count, c, s)
     return c, s
+
+
+def int8_rows(seed: int, N: int, K: int):
+    """Packed-int8 rows for the resident-spine GEMV: q [N, K] int8 uniform over
+    -127..127, and one fp16 row scale [N] (as uint16 bits) uniform in
+    [0.5, 1.5) * 2^-12, so that a row dotted with N(0,1) activations of
+    K = 7168 is of order 1."""
+    k = key(seed, 0, T_INT8_CODES, (N << 20) | K)
+    q = (uint_range(k, N * K, 0, 255).astype(np.int16) - 127).astype(np.int8).reshape(N, K)
+    sc = uniform_f32(key(seed, 0, T_INT8_SCALES, (N << 20) | K), N, 0.5, 1.5) * np.float32(2.0 ** -12)
+    return q, sc.astype(np.float16).view(np.uint16)
