@@ -341,9 +341,44 @@ def bench_decode(a, ctx, steps, warmup):
             "k_gateup_gemv_routes_given": {"avg_launch_us": gv_us,
                                            "frac": gu_w / (gv_us * 1e-6) / 1e9 / HBM_PEAK_GBS}},
     }
+    # the same layer with the lossless scale4 side-car (2.88% fewer expert
+    # bytes): bit-identical output, same steps and kernel timing
+    s4 = None
+    enc = moe.encode_scale4_layer(desc, scales)
+    if enc is not None:
+        desc4, scale4 = enc
+        out4 = torch.empty(1, H, dtype=torch.float32, device=dev)
+        for t in (0, 1):
+            step(t)
+            moe.moe_mxfp4_forward(desc4, pool[t:t + 1], wr, None, codes, scale4, k, out4, ws)
+            torch.cuda.synchronize()
+            if not torch.equal(out4.view(torch.int32), out.view(torch.int32)):
+                refuse("scale4 forward differs from the 8-bit forward")
+
+        def step4(i):
+            x = pool[i % a.pool:i % a.pool + 1]
+            moe.moe_mxfp4_forward(desc4, x, wr, None, codes, scale4, k, out4, ws)
+
+        ms4, spread4 = time_steps(step4, steps, warmup)
+        gu4 = kernel_us(lambda i: moe.moe_mxfp4_gate_up_select(
+            desc4, pool[(warmup + i) % a.pool:(warmup + i) % a.pool + 1],
+            logits_all[(warmup + i) % a.pool:(warmup + i) % a.pool + 1], k, codes, scale4, sel_i, sel_w, hbuf),
+            n, warmup)
+        dn4 = kernel_us(lambda i: moe.moe_mxfp4_down(desc4, hbuf, routes[(warmup + i) % a.pool], codes, scale4, ybuf),
+                        n, warmup)
+        eb4 = k * (sum(moe.packed_bytes(desc4)) // E)
+        s4 = {"tokens_per_s": 1.0 / (ms4 * 1e-3), "ms_per_step": ms4, "ms_per_step_spread": spread4,
+              "expert_bytes_per_token": eb4, "bytes_saved_frac": 1.0 - eb4 / expert_bytes,
+              "expert_phase_us": {"k_gateup_gemv_select": gu4, "k_down_ks": dn4},
+              "expert_phase_GBps": eb4 / ((gu4 + dn4) * 1e-6) / 1e9,
+              "expert_phase_frac": eb4 / ((gu4 + dn4) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+              "expert_phase_speedup": (gu_us + dn_us) / (gu4 + dn4), "bit_identical_to_8bit": True}
+        log("decode scale4: %.2f us/step, expert phase %.1f + %.1f us (%.3f fewer bytes)" % (
+            ms4 * 1e3, gu4, dn4, 1.0 - eb4 / expert_bytes))
+        del scale4
     layer_bytes = expert_bytes + E * H * 4 + H * 2 + H * 4
     cfg = {"workload": "decode: T=1, H=7168, I=1536, E=896, k=16, bf16 x, all experts resident, "
-                       "256-token rotating pool",
+                       "256-token rotating pool", "scale4": s4,
            "global_batch": 1, "layer_bytes_per_token": layer_bytes,
            "layer_GBps": layer_bytes / (ms_step * 1e-3) / 1e9, "layer_frac_hbm":
                layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, "expert_bytes_per_token": expert_bytes}

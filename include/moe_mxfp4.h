@@ -86,6 +86,7 @@ typedef enum moe_dtype {
 
 /* Device weight layout ids. */
 #define MOE_LAYOUT_ROWMAJOR_V1 1u
+#define MOE_LAYOUT_SCALE4_V1 2u
 /*
  * MOE_LAYOUT_ROWMAJOR_V1 -- per expert e (experts back to back, e = 0..E-1):
  *   codes  : gate [I][H/2] | up [I][H/2] | down [H][I/2]      (uint8, 3*I*H/2 bytes)
@@ -98,6 +99,19 @@ typedef enum moe_dtype {
  * techniques that bought the 82x": an expert's six tensors are contiguous).
  * This is also the logical (interchange) layout, so moe_mxfp4_pack is a
  * validated device copy into it.
+ *
+ * MOE_LAYOUT_SCALE4_V1 -- the lossless scale4 side-car ("Deltafin's custom
+ * compiled runtime", section "Weight fidelity": scale side-cars coded
+ * reversibly, the MXFP4 values and reconstructed scales unchanged; the coding
+ * itself is this library's, the pages give none): codes as ROWMAJOR_V1; the
+ * scale buffer holds per expert (back to back, 2I + H + 3HI/64 bytes)
+ *   bases  : gate [I] | up [I] | down [H]                       (one byte per row)
+ *   deltas : gate [I][H/64] | up [I][H/64] | down [H][I/64]     (4 bits per block)
+ * Block b of row n has the E8M0 byte base[n] + delta, the even block in the
+ * low nibble of byte b/2.  H and I must be multiples of 64.  It is produced
+ * by moe_mxfp4_scale4_encode and read by the decode-form kernels and the
+ * dequant exports; a forward on it runs the decode form for every token
+ * count, and the grouped-GEMM and pack entries refuse it (MOE_ERR_LAYOUT).
  */
 
 /* Layer descriptor: the versioned, size-gated description every layer call
@@ -110,7 +124,7 @@ typedef struct moe_layer_desc {
     int32_t inter;         /* I: 32 <= I, I % 32 == 0 */
     int32_t n_experts;     /* E >= 1 */
     int32_t top_k_max;     /* largest k used with this layer: 1 <= k <= min(E, 64) */
-    uint32_t layout;       /* MOE_LAYOUT_ROWMAJOR_V1 */
+    uint32_t layout;       /* MOE_LAYOUT_ROWMAJOR_V1 or MOE_LAYOUT_SCALE4_V1 */
     uint32_t reserved;     /* must be 0 */
 } moe_layer_desc;
 
@@ -381,6 +395,20 @@ moe_status moe_mxfp4_dequant(const moe_layer_desc* desc, const void* packed_code
 moe_status moe_mxfp4_dequant_bf16(const moe_layer_desc* desc, const void* packed_codes,
                                   const void* packed_scales, int64_t expert, int32_t matrix, float* out,
                                   void* stream);
+
+/* scale4 encoding ("Deltafin's custom compiled runtime", section "Weight
+ * fidelity": lossless scale4 side-cars): desc has layout MOE_LAYOUT_SCALE4_V1;
+ * scales8 holds experts expert_begin .. expert_begin + expert_count - 1 back
+ * to back in the 8-bit table (3HI/32 bytes each, device memory); their scale4
+ * records are written into the layer's scale4 buffer `scale4`.  Each row's
+ * base is its smallest scale byte.  A row whose scales span more than 15
+ * cannot be coded: the call adds 1 to the device int32 *escapes for each such
+ * row (the caller zeroes it first and keeps the 8-bit layout for the layer if
+ * it is not 0 after the stream has run).  Errors: descriptor errors,
+ * MOE_ERR_LAYOUT (desc not scale4), MOE_ERR_NULL, MOE_ERR_RANGE,
+ * MOE_ERR_ALIGN, MOE_ERR_DEVICE. */
+moe_status moe_mxfp4_scale4_encode(const moe_layer_desc* desc, const void* scales8, int64_t expert_begin,
+                                   int64_t expert_count, void* scale4, int32_t* escapes, void* stream);
 
 /* RMSNorm with gain, n = r / sqrt(mean(r^2) + eps) * gamma, per token (not on
  * the pages; the 12-layer stack workload this library is measured on names

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mxfp4.so")
 
 MOE_ABI_VERSION = 1
 MOE_LAYOUT_ROWMAJOR_V1 = 1
+MOE_LAYOUT_SCALE4_V1 = 2
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 
 STATUS = {
@@ -36,7 +37,7 @@ EXPORTS = [
     "moe_stack_graph_destroy", "moe_cache_create", "moe_cache_destroy", "moe_cache_slots", "moe_cache_get_stats",
     "moe_cache_plan", "moe_cache_finish", "moe_cache_cancel", "moe_cache_workspace_bytes", "moe_cache_layer_forward",
     "moe_route_hint_workspace_bytes", "moe_route_hint", "moe_trace_open", "moe_trace_record", "moe_trace_close",
-    "moe_trace_count", "moe_int8_dequant", "moe_int8_gemv",
+    "moe_trace_count", "moe_int8_dequant", "moe_int8_gemv", "moe_mxfp4_scale4_encode",
 ]
 MOE_TRACE_BUFFERED, MOE_TRACE_SYNC = 0, 1
 MOE_CACHE_PREFETCH = 1
@@ -64,9 +65,9 @@ class LayerDesc(ctypes.Structure):
                 ("top_k_max", ctypes.c_int32), ("layout", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
     @classmethod
-    def make(cls, hidden: int, inter: int, n_experts: int, top_k_max: int) -> "LayerDesc":
-        return cls(MOE_ABI_VERSION, ctypes.sizeof(cls), hidden, inter, n_experts, top_k_max,
-                   MOE_LAYOUT_ROWMAJOR_V1, 0)
+    def make(cls, hidden: int, inter: int, n_experts: int, top_k_max: int,
+             layout: int = MOE_LAYOUT_ROWMAJOR_V1) -> "LayerDesc":
+        return cls(MOE_ABI_VERSION, ctypes.sizeof(cls), hidden, inter, n_experts, top_k_max, layout, 0)
 
 
 _lock = threading.Lock()
@@ -137,6 +138,7 @@ def lib():
                 "moe_trace_close": ([vp], ctypes.c_int),
                 "moe_trace_count": ([ctypes.c_char_p, i32, i32, vp, P(i64)], ctypes.c_int),
                 "moe_int8_dequant": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+                "moe_mxfp4_scale4_encode": ([D, vp, i64, i64, vp, vp, vp], ctypes.c_int),
                 "moe_int8_gemv": ([vp, vp, i32, i32, vp, i32, i32, vp, i32, vp], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
@@ -518,3 +520,26 @@ def moe_int8_gemv(q, scales_f16, x, y, rows_per_workgroup=0, stream=None):
     N, K = q.shape
     _check("moe_int8_gemv", lib().moe_int8_gemv(_ptr(q), _ptr(scales_f16), N, K, _ptr(x), _xdtype(x), x.shape[0],
                                                 _ptr(y), rows_per_workgroup, _stream(stream)))
+
+
+def moe_mxfp4_scale4_encode(desc4, scales8, expert_begin, expert_count, scale4, escapes, stream=None):
+    """desc4: a scale4 descriptor; scales8: the 8-bit table of the experts
+    (device); scale4: the layer's scale4 buffer; escapes: int32 [1] (device,
+    incremented per row that cannot be coded)."""
+    _check("moe_mxfp4_scale4_encode", lib().moe_mxfp4_scale4_encode(
+        ctypes.byref(desc4), _ptr(scales8), expert_begin, expert_count, _ptr(scale4), _ptr(escapes), _stream(stream)))
+
+
+def encode_scale4_layer(desc8, scales8, stream=None):
+    """The scale4 buffer of a whole layer from its 8-bit table (device tensors),
+    or None when some row cannot be coded (the layer keeps the 8-bit table).
+    Returns (desc4, scale4)."""
+    import torch
+    desc4 = LayerDesc.make(desc8.hidden, desc8.inter, desc8.n_experts, desc8.top_k_max, MOE_LAYOUT_SCALE4_V1)
+    _, sb4 = packed_bytes(desc4)
+    scale4 = torch.empty(sb4, dtype=torch.uint8, device=scales8.device)
+    esc = torch.zeros(1, dtype=torch.int32, device=scales8.device)
+    moe_mxfp4_scale4_encode(desc4, scales8, 0, desc8.n_experts, scale4, esc, stream)
+    if int(esc.item()) != 0:
+        return None
+    return desc4, scale4

@@ -35,21 +35,26 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->abi_version != MOE_ABI_VERSION || d->struct_size != sizeof(moe_layer_desc)) return MOE_ERR_ABI;
   if (d->reserved != 0) return MOE_ERR_ABI;
-  if (d->layout != MOE_LAYOUT_ROWMAJOR_V1) return MOE_ERR_LAYOUT;
+  if (d->layout != MOE_LAYOUT_ROWMAJOR_V1 && d->layout != MOE_LAYOUT_SCALE4_V1) return MOE_ERR_LAYOUT;
   if (d->hidden < 32 || d->inter < 32 || d->n_experts < 1 || d->top_k_max < 1) return MOE_ERR_SHAPE;
   if (d->hidden % 32 || d->inter % 32) return MOE_ERR_SHAPE;
   if (d->top_k_max > d->n_experts || d->top_k_max > kMaxTopK) return MOE_ERR_SHAPE;
   if (d->hidden > kMaxHidden || d->inter > kMaxInter || d->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  // scale4 packs two blocks per delta byte: whole bytes per row need K % 64 == 0
+  if (d->layout == MOE_LAYOUT_SCALE4_V1 && (d->hidden % 64 || d->inter % 64)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-// Per-expert byte counts; checked.
+inline bool is_s4(const moe_layer_desc* d) { return d->layout == MOE_LAYOUT_SCALE4_V1; }
+
+// Per-expert byte counts; checked.  scale4: row bases (2I + H bytes) and
+// 4-bit deltas (3HI/64 bytes) instead of the 3HI/32-byte table.
 moe_status expert_bytes(const moe_layer_desc* d, size_t* cb, size_t* sb) {
   size_t hi;
   if (!mul_ok((size_t)d->hidden, (size_t)d->inter, &hi)) return MOE_ERR_OVERFLOW;
   if (!mul_ok(hi, 3, &hi)) return MOE_ERR_OVERFLOW;
   *cb = hi / 2;
-  *sb = hi / 32;
+  *sb = is_s4(d) ? hi / 64 + (size_t)2 * d->inter + (size_t)d->hidden : hi / 32;
   return MOE_OK;
 }
 
@@ -133,7 +138,7 @@ bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
 // Tokens per batch of the prefill form (larger T runs in batches of this
 // many tokens, which are independent); 0 if the shape has no prefill form.
 int64_t grouped_batch(const moe_layer_desc* d, int32_t k) {
-  if (!moe::grouped_shape_ok(d->hidden, d->inter)) return 0;
+  if (is_s4(d) || !moe::grouped_shape_ok(d->hidden, d->inter)) return 0;  // scale4: decode form only
   const int64_t H = d->hidden, I = d->inter;
   int64_t tb = ((int64_t{1} << 30) - 1) / (H * 2);
   tb = std::min(tb, ((int64_t{1} << 30) - 1) / (k * I * 4));
@@ -189,8 +194,8 @@ moe_status run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const
     }
     return MOE_OK;
   }
-  MOE_TRY(dev(moe::launch_gateup_gemv(x, x_f32, idx, P, k, c, sc, H, I, E, h, s)));
-  MOE_TRY(dev(moe::launch_down_gemv(h, idx, P, c, sc, H, I, E, y, s)));
+  MOE_TRY(dev(moe::launch_gateup_gemv(x, x_f32, idx, P, k, c, sc, is_s4(d), H, I, E, h, s)));
+  MOE_TRY(dev(moe::launch_down_gemv(h, idx, P, c, sc, is_s4(d), H, I, E, y, s)));
   MOE_TRY(dev(moe::launch_combine(y, w, T, k, H, resid, out, s)));
   return MOE_OK;
 }
@@ -289,8 +294,8 @@ moe_status forward_impl(const moe_layer_desc* d, const void* x, moe_dtype x_dtyp
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  MOE_TRY(dev(moe::launch_gateup_select_gemv(x, xf, logits, T, k, c, sc, H, I, E, idx, w, h, s)));
-  MOE_TRY(dev(moe::launch_down_gemv(h, idx, T * k, c, sc, H, I, E, y, s)));
+  MOE_TRY(dev(moe::launch_gateup_select_gemv(x, xf, logits, T, k, c, sc, is_s4(d), H, I, E, idx, w, h, s)));
+  MOE_TRY(dev(moe::launch_down_gemv(h, idx, T * k, c, sc, is_s4(d), H, I, E, y, s)));
   return dev(moe::launch_combine(y, w, T, k, H, resid, out, s));
 }
 
@@ -350,6 +355,7 @@ moe_status moe_mxfp4_pack(const moe_layer_desc* d, const void* logical_codes, co
                    int64_t expert_begin, int64_t expert_count, void* packed_codes, void* packed_scales,
                    void* stream) {
   MOE_TRY(check_desc(d));
+  if (is_s4(d)) return MOE_ERR_LAYOUT;  // scale4 tables come from moe_mxfp4_scale4_encode
   if (!logical_codes || !logical_scales || !packed_codes || !packed_scales) return MOE_ERR_NULL;
   if (expert_begin < 0 || expert_count < 0 || expert_begin > d->n_experts ||
       expert_count > d->n_experts - expert_begin)
@@ -420,7 +426,7 @@ moe_status moe_mxfp4_gate_up(const moe_layer_desc* d, const void* x, moe_dtype x
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
   return dev(moe::launch_gateup_gemv(x, x_dtype == MOE_DTYPE_F32, pair_expert, n_pairs, k,
                                      static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
-                                     d->hidden, d->inter, d->n_experts, h, as_stream(stream)));
+                                     is_s4(d), d->hidden, d->inter, d->n_experts, h, as_stream(stream)));
 }
 
 moe_status moe_mxfp4_gate_up_select(const moe_layer_desc* d, const void* x, moe_dtype x_dtype, const float* logits,
@@ -434,7 +440,7 @@ moe_status moe_mxfp4_gate_up_select(const moe_layer_desc* d, const void* x, moe_
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
   return dev(moe::launch_gateup_select_gemv(x, x_dtype == MOE_DTYPE_F32, logits, n_tokens, k,
                                             static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
-                                            d->hidden, d->inter, d->n_experts, topk_idx, topk_w, h,
+                                            is_s4(d), d->hidden, d->inter, d->n_experts, topk_idx, topk_w, h,
                                             as_stream(stream)));
 }
 
@@ -445,8 +451,8 @@ moe_status moe_mxfp4_down(const moe_layer_desc* d, const float* h, const int32_t
   if (n_pairs < 1 || n_pairs > kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
   if (!aligned16(h) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGN;
   return dev(moe::launch_down_gemv(h, pair_expert, n_pairs, static_cast<const uint8_t*>(codes),
-                                   static_cast<const uint8_t*>(scales), d->hidden, d->inter, d->n_experts, y,
-                                   as_stream(stream)));
+                                   static_cast<const uint8_t*>(scales), is_s4(d), d->hidden, d->inter, d->n_experts,
+                                   y, as_stream(stream)));
 }
 
 moe_status moe_combine(const float* y, const float* w, int32_t n_tokens, int32_t k, int32_t hidden, const float* resid,
@@ -526,6 +532,7 @@ moe_status moe_mxfp4_grouped_gate_up(const moe_layer_desc* d, const void* x, int
                               int32_t max_blocks, const void* packed_codes, const void* packed_scales, void* hterm,
                               void* stream) {
   MOE_TRY(check_desc(d));
+  if (is_s4(d)) return MOE_ERR_LAYOUT;  // the grouped GEMMs read the 8-bit table
   if (!x || !pair_list || !blocks || !n_blocks || !packed_codes || !packed_scales || !hterm) return MOE_ERR_NULL;
   MOE_TRY(check_tokens(n_tokens, k, d));
   const int64_t P = (int64_t)n_tokens * k;
@@ -545,6 +552,7 @@ moe_status moe_mxfp4_grouped_down(const moe_layer_desc* d, const void* hterm, in
                            const int32_t* blocks, const int32_t* n_blocks, int32_t max_blocks,
                            const void* packed_codes, const void* packed_scales, float* y, void* stream) {
   MOE_TRY(check_desc(d));
+  if (is_s4(d)) return MOE_ERR_LAYOUT;  // the grouped GEMMs read the 8-bit table
   if (!hterm || !pair_list || !blocks || !n_blocks || !packed_codes || !packed_scales || !y) return MOE_ERR_NULL;
   if (n_pairs < 1 || (int64_t)n_pairs > (int64_t)kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
   if (!grouped_fits(d, 1, n_pairs)) return MOE_ERR_UNSUPPORTED;
@@ -566,12 +574,19 @@ static moe_status dequant_entry(const moe_layer_desc* d, const void* packed_code
   if (!aligned16(packed_codes) || !aligned16(packed_scales) || !aligned16(out)) return MOE_ERR_ALIGN;
   size_t cb, sb;
   MOE_TRY(expert_bytes(d, &cb, &sb));
-  const size_t mc = cb / 3, ms = sb / 3;
+  const size_t mc = cb / 3;
   const int rows = matrix == 2 ? d->hidden : d->inter;
   const int cols = matrix == 2 ? d->inter : d->hidden;
   const uint8_t* c = static_cast<const uint8_t*>(packed_codes) + (size_t)expert * cb + (size_t)matrix * mc;
-  const uint8_t* s = static_cast<const uint8_t*>(packed_scales) + (size_t)expert * sb + (size_t)matrix * ms;
-  return dev(moe::launch_dequant(c, s, rows, cols, out, via_bf16, as_stream(stream)));
+  const uint8_t* rec = static_cast<const uint8_t*>(packed_scales) + (size_t)expert * sb;
+  if (is_s4(d)) {  // row bases gate [I] | up [I] | down [H], then deltas [rows][cols/64] per matrix
+    const size_t I = (size_t)d->inter, H = (size_t)d->hidden, dm = I * H / 64;
+    const uint8_t* base = rec + (matrix == 2 ? 2 * I : (size_t)matrix * I);
+    const uint8_t* del = rec + 2 * I + H + (size_t)matrix * dm;
+    return dev(moe::launch_dequant(c, del, base, rows, cols, out, via_bf16, as_stream(stream)));
+  }
+  const uint8_t* s = rec + (size_t)matrix * (sb / 3);
+  return dev(moe::launch_dequant(c, s, nullptr, rows, cols, out, via_bf16, as_stream(stream)));
 }
 
 moe_status moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
@@ -582,6 +597,19 @@ moe_status moe_mxfp4_dequant(const moe_layer_desc* d, const void* packed_codes, 
 moe_status moe_mxfp4_dequant_bf16(const moe_layer_desc* d, const void* packed_codes, const void* packed_scales,
                                   int64_t expert, int32_t matrix, float* out, void* stream) {
   return dequant_entry(d, packed_codes, packed_scales, expert, matrix, out, true, stream);
+}
+
+moe_status moe_mxfp4_scale4_encode(const moe_layer_desc* d, const void* scales8, int64_t expert_begin,
+                                   int64_t expert_count, void* scale4, int32_t* escapes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!is_s4(d)) return MOE_ERR_LAYOUT;
+  if (!scales8 || !scale4 || !escapes) return MOE_ERR_NULL;
+  if (expert_begin < 0 || expert_count < 0 || expert_begin > d->n_experts ||
+      expert_count > d->n_experts - expert_begin)
+    return MOE_ERR_RANGE;
+  if (!aligned16(scale4)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_scale4_encode(static_cast<const uint8_t*>(scales8), expert_begin, expert_count, d->hidden,
+                                       d->inter, static_cast<uint8_t*>(scale4), escapes, as_stream(stream)));
 }
 
 moe_status moe_rmsnorm(const float* r, const float* gamma, float eps, int32_t n_tokens, int32_t hidden, float* n_out,

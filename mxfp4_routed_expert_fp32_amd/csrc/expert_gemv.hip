@@ -140,33 +140,102 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Scales of one matrix: the 8-bit table (one E8M0 byte per 32-element block,
+// [rows][nb]), or the scale4 side-car (one base byte per row, [rows], and a
+// 4-bit delta per block, two blocks per byte with the even block in the low
+// nibble, [rows][nb/2]; the block's E8M0 byte is base + delta).
+struct ScaleSrc {
+  rsrc_t tab;   // 8-bit table, or scale4 deltas
+  rsrc_t base;  // scale4 row bases
+  const uint8_t* bptr;  // the same bases, for scalar loads (4-byte aligned)
+};
+
+// Scalar (constant address space) view of the row bases: a wave-uniform
+// index becomes one s_load_dword, outside the vector memory pipeline.  (Two
+// other ways measured slower: a vector load of the base per row, +12% load
+// instructions; one vector load of 64 rows' bases read back with readlane,
+// which made the compiler wait for all loads every row.)
+typedef __attribute__((address_space(4))) const uint32_t scalar_u32;
+
+// The base bytes of rows 4j .. 4j + 3 (j wave-uniform) in one dword.
+__device__ __forceinline__ uint32_t bases4(const uint8_t* bptr, int j) {
+  return ((scalar_u32*)bptr)[j];  // an address-space cast (C style: reinterpret_cast refuses it)
+}
+
+// Scale source of matrix m (0 gate, 1 up, 2 down) of expert e.  scale4
+// record of one expert: bases gate [I] | up [I] | down [H], then deltas
+// gate [I][H/64] | up [I][H/64] | down [H][I/64].
+template <bool S4>
+__device__ __forceinline__ ScaleSrc matrix_scales(const uint8_t* scales, int e, int m, int H, int I) {
+  if constexpr (S4) {
+    const size_t dm = (size_t)I * H / 64;
+    const uint8_t* p = scales + (size_t)e * ((size_t)2 * I + H + 3 * dm);
+    const size_t boff = m == 2 ? (size_t)2 * I : (size_t)m * I;
+    return ScaleSrc{make_rsrc(p + (size_t)2 * I + H + (size_t)m * dm, (uint32_t)dm),
+                    make_rsrc(p + boff, (uint32_t)(m == 2 ? H : I)), p + boff};
+  } else {
+    const uint32_t ms = (uint32_t)((size_t)I * H / 32);
+    return ScaleSrc{make_rsrc(scales + (size_t)e * 3 * ms + (size_t)m * ms, ms), make_rsrc(scales, 0u), scales};
+  }
+}
+
 // One row's worth of a lane's blocks: NBL 16-byte code blocks + scale bytes.
 template <int NBL>
 struct RowBlocks {
   u32x4 q[NBL];
-  uint32_t s[NBL];
+  uint32_t s[NBL];  // E8M0 byte, or (scale4) the byte holding the block's delta
+  uint32_t base;    // scale4: the row's base byte
+  uint32_t valid;   // scale4: bit m set when block m exists (a block past the row has scale 0)
 };
 
 // Blocks b = c + LPR*m of row `row` (row < 0: none) of a [rows][nb*32] matrix.
-template <int LPR, int NBL>
-__device__ __forceinline__ void load_row(RowBlocks<NBL>& r, rsrc_t codes, rsrc_t scales, int row, int c,
+template <int LPR, int NBL, bool S4>
+__device__ __forceinline__ void load_row(RowBlocks<NBL>& r, rsrc_t codes, const ScaleSrc& sc, int row, int c,
                                          int nb) {
-  const uint32_t rc = (uint32_t)row * (uint32_t)(nb * 16), rsc = (uint32_t)row * (uint32_t)nb;
+  const uint32_t rc = (uint32_t)row * (uint32_t)(nb * 16);
+  const uint32_t rsc = (uint32_t)row * (uint32_t)(S4 ? nb / 2 : nb);
+  if constexpr (S4) {
+    if constexpr (LPR == kWave) {  // one row per wave: its base by a scalar load
+      const int rr = __builtin_amdgcn_readfirstlane(row >= 0 ? row : 0);
+      r.base = (bases4(sc.bptr, rr >> 2) >> ((rr & 3) * 8)) & 0xFFu;
+    } else {
+      r.base = __builtin_amdgcn_raw_buffer_load_b8(sc.base, row >= 0 ? (uint32_t)row : kOOB, 0, 2 /* nt */);
+    }
+    r.valid = 0u;
+  }
 #pragma unroll
   for (int m = 0; m < NBL; ++m) {
     const int b = c + LPR * m;
     const bool ok = row >= 0 && b < nb;
     r.q[m] = __builtin_amdgcn_raw_buffer_load_b128(codes, ok ? rc + 16u * b : kOOB, 0, 2 /* nt */);
-    r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(scales, ok ? rsc + b : kOOB, 0, 2 /* nt */);
+    if constexpr (S4) {
+      r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(sc.tab, ok ? rsc + (uint32_t)(b >> 1) : kOOB, 0, 2 /* nt */);
+      r.valid |= ok ? (1u << m) : 0u;
+    } else {
+      r.s[m] = __builtin_amdgcn_raw_buffer_load_b8(sc.tab, ok ? rsc + b : kOOB, 0, 2 /* nt */);
+    }
   }
 }
 
-template <bool XF32, int NBL>
-__device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t (*xr)[XF32 ? 32 : 16]) {
+// The E8M0 byte of block m.  scale4: the row base plus the block's nibble
+// (sh = 0 for an even block, 4 for an odd one; LPR is even, so all blocks of
+// a lane have the parity of its first), read only once the loads have landed;
+// a block past the row gets 0, like the 8-bit table's out-of-range read, so
+// a NaN or infinite base never meets the zero padding codes.
+template <bool S4, int NBL>
+__device__ __forceinline__ uint32_t scale_byte(const RowBlocks<NBL>& r, int m, int sh) {
+  if constexpr (S4)
+    return ((r.valid >> m) & 1u) ? r.base + ((r.s[m] >> sh) & 15u) : 0u;
+  else
+    return r.s[m];
+}
+
+template <bool XF32, int NBL, bool S4>
+__device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t (*xr)[XF32 ? 32 : 16], int sh) {
   float acc = 0.0f;
 #pragma unroll
   for (int m = 0; m < NBL; ++m) {
-    const float s = e8m0_operand(r.s[m]);
+    const float s = e8m0_operand(scale_byte<S4>(r, m, sh));
     const uint4 q = make_uint4(r.q[m].x, r.q[m].y, r.q[m].z, r.q[m].w);
     if constexpr (XF32)
       acc = block_dot_f32(q, s, xr[m], acc);
@@ -203,7 +272,7 @@ __device__ __forceinline__ float group_reduce(float v) {
 // token's k experts to route[] and their weights to wsel[] for the later
 // kernels.  Every workgroup of a token computes the same selection from the
 // same logits with the same code, so they agree.
-template <bool XF32, int NBL, int SEL>
+template <bool XF32, int NBL, int SEL, bool S4>
 __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
                                                      int32_t* __restrict__ route,
                                                      const float* __restrict__ logits,
@@ -245,20 +314,21 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
     e = __builtin_amdgcn_readfirstlane(route[p]);
   }
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const size_t cb = (size_t)3 * I * H / 2;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2);
   const rsrc_t gcod = make_rsrc(codes + (size_t)e * cb, mc);
   const rsrc_t ucod = make_rsrc(codes + (size_t)e * cb + mc, mc);
-  const rsrc_t gsc = make_rsrc(scales + (size_t)e * sb, ms);
-  const rsrc_t usc = make_rsrc(scales + (size_t)e * sb + ms, ms);
+  const ScaleSrc gsc = matrix_scales<S4>(scales, e, 0, H, I);
+  const ScaleSrc usc = matrix_scales<S4>(scales, e, 1, H, I);
+  const int sh = (lane & 1) * 4;
   // rows interleaved across the pair's waves
   const int i0 = part * 4 + wid;
   const int istep = parts * 4;
   const int nsteps = i0 < I ? (I - i0 + istep - 1) / istep : 0;
 
   RowBlocks<NBL> g0, u0, g1, u1;
-  load_row<kWave, NBL>(g0, gcod, gsc, nsteps > 0 ? i0 : -1, lane, nb);
-  load_row<kWave, NBL>(u0, ucod, usc, nsteps > 0 ? i0 : -1, lane, nb);
+  load_row<kWave, NBL, S4>(g0, gcod, gsc, nsteps > 0 ? i0 : -1, lane, nb);
+  load_row<kWave, NBL, S4>(u0, ucod, usc, nsteps > 0 ? i0 : -1, lane, nb);
 
   // stage this token's activations (already done when selecting), then keep
   // the lane's blocks in registers
@@ -280,17 +350,17 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   for (int st = 0; st < nsteps; st += 2) {
     const int i = i0 + st * istep, i1 = i + istep, i2 = i1 + istep;
     const bool has1 = st + 1 < nsteps;
-    load_row<kWave, NBL>(g1, gcod, gsc, has1 ? i1 : -1, lane, nb);
-    load_row<kWave, NBL>(u1, ucod, usc, has1 ? i1 : -1, lane, nb);
-    float ag = wave_sum(row_dot<XF32, NBL>(g0, xr));
-    float au = wave_sum(row_dot<XF32, NBL>(u0, xr));
+    load_row<kWave, NBL, S4>(g1, gcod, gsc, has1 ? i1 : -1, lane, nb);
+    load_row<kWave, NBL, S4>(u1, ucod, usc, has1 ? i1 : -1, lane, nb);
+    float ag = wave_sum(row_dot<XF32, NBL, S4>(g0, xr, sh));
+    float au = wave_sum(row_dot<XF32, NBL, S4>(u0, xr, sh));
     if (lane == 0) hbuf[(size_t)p * I + i] = silu_mul(ag, au);
     if (!has1) break;
     const bool has2 = st + 2 < nsteps;
-    load_row<kWave, NBL>(g0, gcod, gsc, has2 ? i2 : -1, lane, nb);
-    load_row<kWave, NBL>(u0, ucod, usc, has2 ? i2 : -1, lane, nb);
-    ag = wave_sum(row_dot<XF32, NBL>(g1, xr));
-    au = wave_sum(row_dot<XF32, NBL>(u1, xr));
+    load_row<kWave, NBL, S4>(g0, gcod, gsc, has2 ? i2 : -1, lane, nb);
+    load_row<kWave, NBL, S4>(u0, ucod, usc, has2 ? i2 : -1, lane, nb);
+    ag = wave_sum(row_dot<XF32, NBL, S4>(g1, xr, sh));
+    au = wave_sum(row_dot<XF32, NBL, S4>(u1, xr, sh));
     if (lane == 0) hbuf[(size_t)p * I + i1] = silu_mul(ag, au);
   }
 }
@@ -301,7 +371,7 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
 // groups interleaved across the pair's waves, weights loaded three steps
 // ahead from a ring of four.  The pair's h row is staged in LDS and each lane
 // keeps its NBL2 blocks in registers.
-template <int LPR, int NBL2>
+template <int LPR, int NBL2, bool S4>
 __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbuf,
                                                    const int32_t* __restrict__ pair_expert,
                                                    const uint8_t* __restrict__ codes,
@@ -317,10 +387,11 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
   int e = __builtin_amdgcn_readfirstlane(pair_expert[p]);
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nbk = I / 32;
-  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const size_t cb = (size_t)3 * I * H / 2;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2);
   const rsrc_t dcod = make_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
-  const rsrc_t dsc = make_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
+  const ScaleSrc dsc = matrix_scales<S4>(scales, e, 2, H, I);
+  const int sh = (c & 1) * 4;
   // row groups interleaved across the pair's waves (see k_gateup_gemv)
   const int n_begin = (part * 4 + wid) * RPS + rsub;
   const int n_step = parts * 4 * RPS;
@@ -329,7 +400,7 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) {
     const int n = n_begin + d * n_step;
-    load_row<LPR, NBL2>(ring[d], dcod, dsc, (d < steps && n < H) ? n : -1, c, nbk);
+    load_row<LPR, NBL2, S4>(ring[d], dcod, dsc, (d < steps && n < H) ? n : -1, c, nbk);
   }
 
   const float4* hsrc = reinterpret_cast<const float4*>(hbuf + (size_t)p * I);
@@ -354,9 +425,9 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
       if (st >= steps) break;
       const int sn = st + D - 1;
       const int nn = n_begin + sn * n_step;
-      load_row<LPR, NBL2>(ring[(d + D - 1) % D], dcod, dsc, (sn < steps && nn < H) ? nn : -1, c, nbk);
+      load_row<LPR, NBL2, S4>(ring[(d + D - 1) % D], dcod, dsc, (sn < steps && nn < H) ? nn : -1, c, nbk);
       const int n0 = n_begin + st * n_step;
-      const float acc = group_reduce<LPR>(row_dot<true, NBL2>(ring[d], hr));
+      const float acc = group_reduce<LPR>(row_dot<true, NBL2, S4>(ring[d], hr, sh));
       if (c == LPR - 1 && n0 < H) ybuf[(size_t)p * H + n0] = acc;
     }
   }
@@ -380,7 +451,7 @@ constexpr int kDnKsLdsCap = 16384;
 // adds the KS partials of each row in wave order (a fixed order, so results
 // are deterministic).  Weight loads run D-1 steps ahead; rows_per_wg is a
 // multiple of 4*D, so the unrolled ring has no exit inside.
-template <int KS, int D>
+template <int KS, int D, bool S4>
 __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ hbuf,
                                                      const int32_t* __restrict__ pair_expert,
                                                      const uint8_t* __restrict__ codes,
@@ -394,11 +465,12 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
   int e = __builtin_amdgcn_readfirstlane(pair_expert[p]);
   e = e < 0 ? 0 : (e >= E ? E - 1 : e);
   const int nbk = I / 32;
-  const size_t cb = (size_t)3 * I * H / 2, sb = (size_t)3 * I * H / 32;
-  const uint32_t mc = (uint32_t)((size_t)I * H / 2), ms = (uint32_t)((size_t)I * H / 32);
+  const size_t cb = (size_t)3 * I * H / 2;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2);
   const rsrc_t dcod = make_rsrc(codes + (size_t)e * cb + 2 * (size_t)mc, mc);
-  const rsrc_t dsc = make_rsrc(scales + (size_t)e * sb + 2 * (size_t)ms, ms);
+  const ScaleSrc dsc = matrix_scales<S4>(scales, e, 2, H, I);
   const int b = ks * 16 + c;  // this lane's block of every row
+  const int sh = (c & 1) * 4;
   const int r0 = part * rows_per_wg;
   const int steps = rows_per_wg / 4;
 
@@ -406,7 +478,16 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
     const int n = r0 + 4 * st + rsub;
     const bool ok = st < steps && n < H;
     r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(dcod, ok ? (uint32_t)n * (uint32_t)(I / 2) + 16u * b : kOOB, 0, 2);
-    r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 2 /* nt */);
+    if constexpr (S4) {
+      // rows r0 + 4 st .. + 3 (4-aligned) share one dword of bases: a scalar load
+      const int j = (st < steps && r0 + 4 * st < H) ? (r0 + 4 * st) >> 2 : 0;
+      r.base = (bases4(dsc.bptr, j) >> (rsub * 8)) & 0xFFu;
+      r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc.tab, ok ? (uint32_t)n * (uint32_t)(nbk / 2) + (uint32_t)(b >> 1) : kOOB,
+                                                   0, 2 /* nt */);
+      r.valid = ok ? 1u : 0u;
+    } else {
+      r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc.tab, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 2 /* nt */);
+    }
   };
   RowBlocks<1> ring[D];
 #pragma unroll
@@ -425,7 +506,7 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
     for (int d = 0; d < D; ++d) {
       const int st = s0 + d;
       load(ring[(d + D - 1) % D], st + D - 1);
-      const float v = lane_group_sum<16>(row_dot<true, 1>(ring[d], hr));
+      const float v = lane_group_sum<16>(row_dot<true, 1, S4>(ring[d], hr, sh));
       if (c == 15) partial[(4 * st + rsub) * KS + ks] = v;
     }
   }
@@ -505,15 +586,15 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
   *parts = (rows + 4 * pw - 1) / (4 * pw);
 }
 
-template <bool XF32, int SEL>
+template <bool XF32, int SEL, bool S4>
 static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
                                   const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
                                   int H, int I, int E, int k, float* hbuf) {
 #define MOE_GU(N)                                                                                    \
   {                                                                                                    \
     int parts, rpw;                                                                                    \
-    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N, SEL>, lds), &parts, &rpw);                \
-    k_gateup_gemv<XF32, N, SEL><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(                         \
+    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N, SEL, S4>, lds), &parts, &rpw);            \
+    k_gateup_gemv<XF32, N, SEL, S4><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(                     \
         x, route, logits, wsel, codes, scales, H, I, E, k, parts, rpw, hbuf);                          \
   }
   switch (nbl) {
@@ -528,23 +609,28 @@ static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, con
 }
 
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
-                              const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                              const uint8_t* codes, const uint8_t* scales, bool s4, int H, int I, int E,
                               float* hbuf, hipStream_t s) {
   const int nbl = (H / 32 + kWave - 1) / kWave;
   const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
   int32_t* r = const_cast<int32_t*>(route);  // read only when SEL == 0
-  if (x_f32) return gateup_dispatch<true, 0>(nbl, P, lds, s, x, r, nullptr, nullptr, codes, scales, H, I, E, k, hbuf);
-  return gateup_dispatch<false, 0>(nbl, P, lds, s, x, r, nullptr, nullptr, codes, scales, H, I, E, k, hbuf);
+#define MOE_GUR(XF, S4_) \
+  return gateup_dispatch<XF, 0, S4_>(nbl, P, lds, s, x, r, nullptr, nullptr, codes, scales, H, I, E, k, hbuf);
+  if (s4) {
+    if (x_f32) MOE_GUR(true, true)
+    MOE_GUR(false, true)
+  }
+  if (x_f32) MOE_GUR(true, false)
+  MOE_GUR(false, false)
+#undef MOE_GUR
 }
 
-hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* logits, int T, int k,
-                                     const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
-                                     int32_t* route, float* wsel, float* hbuf, hipStream_t s) {
-  const int nbl = (H / 32 + kWave - 1) / kWave;
-  const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
-  const int P = T * k;
+template <bool S4>
+static hipError_t gateup_select_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, bool x_f32,
+                                         const float* logits, int k, const uint8_t* codes, const uint8_t* scales,
+                                         int H, int I, int E, int32_t* route, float* wsel, float* hbuf) {
 #define MOE_GUS(XF, MV) \
-  return gateup_dispatch<XF, MV>(nbl, P, lds, s, x, route, logits, wsel, codes, scales, H, I, E, k, hbuf);
+  return gateup_dispatch<XF, MV, S4>(nbl, P, lds, s, x, route, logits, wsel, codes, scales, H, I, E, k, hbuf);
   if (x_f32) {
     if (E <= 256) MOE_GUS(true, 4)
     if (E <= 1024) MOE_GUS(true, 16)
@@ -554,6 +640,18 @@ hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* log
   if (E <= 1024) MOE_GUS(false, 16)
   MOE_GUS(false, 64)
 #undef MOE_GUS
+}
+
+hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* logits, int T, int k,
+                                     const uint8_t* codes, const uint8_t* scales, bool s4, int H, int I, int E,
+                                     int32_t* route, float* wsel, float* hbuf, hipStream_t s) {
+  const int nbl = (H / 32 + kWave - 1) / kWave;
+  const size_t lds = (size_t)H * (x_f32 ? 4 : 2);
+  const int P = T * k;
+  if (s4)
+    return gateup_select_dispatch<true>(nbl, P, lds, s, x, x_f32, logits, k, codes, scales, H, I, E, route, wsel,
+                                        hbuf);
+  return gateup_select_dispatch<false>(nbl, P, lds, s, x, x_f32, logits, k, codes, scales, H, I, E, route, wsel, hbuf);
 }
 
 // Lanes per row and blocks per lane for a reduction length of nbk blocks:
@@ -576,15 +674,16 @@ void down_shape(int nbk, int* lpr, int* nbl2) {
 #define MOE_DOWN_CASE(L, N)                                                                          \
   if (lpr == L && nbl2 == N) {                                                                     \
     int parts, rpw;                                                                                \
-    split_rows(H, P, kWave / L, resident_wgs(k_down_gemv<L, N>, lds), &parts, &rpw);              \
-    k_down_gemv<L, N><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(hbuf, pair_expert, codes, scales, \
+    split_rows(H, P, kWave / L, resident_wgs(k_down_gemv<L, N, S4>, lds), &parts, &rpw);          \
+    k_down_gemv<L, N, S4><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(hbuf, pair_expert, codes, scales, \
                                                                    H, I, E, parts, rpw / (kWave / L), \
                                                                    ybuf);                            \
     return hipGetLastError();                                                                        \
   }
 
-hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
-                            const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s) {
+template <bool S4>
+static hipError_t down_dispatch(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
+                                const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s) {
   const int ks = I % 512 == 0 ? I / 512 : 0;
   if (ks == 2 || ks == 3 || ks == 4 || ks == 6 || ks == 8) {
     // K split across I/512 waves; about kDnKsPerCu workgroups per CU
@@ -599,7 +698,7 @@ hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P
     const dim3 grid((unsigned)(P * parts));
 #define MOE_DN_KS(KS)                                                                                     \
   if (ks == KS)                                                                                            \
-    k_down_ks<KS, D><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E, parts, rows, ybuf);
+    k_down_ks<KS, D, S4><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E, parts, rows, ybuf);
     MOE_DN_KS(2) MOE_DN_KS(3) MOE_DN_KS(4) MOE_DN_KS(6) MOE_DN_KS(8)
 #undef MOE_DN_KS
     return hipGetLastError();
@@ -613,6 +712,12 @@ hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P
   MOE_DOWN_CASE(32, 1) MOE_DOWN_CASE(32, 2) MOE_DOWN_CASE(32, 3) MOE_DOWN_CASE(32, 4)
   MOE_DOWN_CASE(64, 1) MOE_DOWN_CASE(64, 2) MOE_DOWN_CASE(64, 3) MOE_DOWN_CASE(64, 4)
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
+                            const uint8_t* scales, bool s4, int H, int I, int E, float* ybuf, hipStream_t s) {
+  if (s4) return down_dispatch<true>(hbuf, pair_expert, P, codes, scales, H, I, E, ybuf, s);
+  return down_dispatch<false>(hbuf, pair_expert, P, codes, scales, H, I, E, ybuf, s);
 }
 
 hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,

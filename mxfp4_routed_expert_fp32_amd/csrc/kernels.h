@@ -30,17 +30,20 @@ hipError_t launch_sort_by_expert(const int32_t* idx, int T, int E, int k, int32_
                                  void* ws, hipStream_t s, int4* blocks = nullptr, int max_blocks = 0,
                                  int32_t* nblocks = nullptr);
 
+// Decode-form GEMVs.  s4: `scales` is the scale4 side-car (per expert: row
+// bases gate [I] | up [I] | down [H], then 4-bit deltas gate [I][H/64] |
+// up [I][H/64] | down [H][I/64]) instead of the 8-bit table.
 hipError_t launch_gateup_gemv(const void* x, bool x_f32, const int32_t* route, int P, int k,
-                              const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                              const uint8_t* codes, const uint8_t* scales, bool s4, int H, int I, int E,
                               float* hbuf, hipStream_t s);
 // Same with the selection fused in: each workgroup takes its pair's expert
 // from the exact top-k of its token's logits; route [T][k] and wsel [T][k]
 // receive the selection and the softmax weights.
 hipError_t launch_gateup_select_gemv(const void* x, bool x_f32, const float* logits, int T, int k,
-                                     const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                                     const uint8_t* codes, const uint8_t* scales, bool s4, int H, int I, int E,
                                      int32_t* route, float* wsel, float* hbuf, hipStream_t s);
 hipError_t launch_down_gemv(const float* hbuf, const int32_t* pair_expert, int P, const uint8_t* codes,
-                            const uint8_t* scales, int H, int I, int E, float* ybuf, hipStream_t s);
+                            const uint8_t* scales, bool s4, int H, int I, int E, float* ybuf, hipStream_t s);
 hipError_t launch_combine(const float* ybuf, const float* w, int T, int k, int H, const float* resid,
                           float* out, hipStream_t s);
 
@@ -86,9 +89,17 @@ hipError_t launch_int8_dequant(const int8_t* q, const uint16_t* s, int N, int K,
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // via_bf16: decode through the bf16 conversion of the bf16 GEMV and the MFMA
-// kernels (widened to fp32), else through the fp32 conversion.
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
-                          bool via_bf16, hipStream_t s);
+// kernels (widened to fp32), else through the fp32 conversion.  With s4_base
+// set, `scales` are the matrix's scale4 deltas [rows][cols/64] and s4_base its
+// row bases [rows].
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const uint8_t* s4_base, int rows, int cols,
+                          float* out, bool via_bf16, hipStream_t s);
+// scale4 encoding of experts [e0, e0 + n) from the 8-bit table (per expert
+// 3*H*I/32 bytes, back to back) into the layer's scale4 buffer; every row
+// whose block scales span more than 15 adds 1 to *escapes (that row is then
+// not representable and the layer must keep the 8-bit table).
+hipError_t launch_scale4_encode(const uint8_t* scales8, int64_t e0, int64_t n, int H, int I, uint8_t* scale4,
+                                int32_t* escapes, hipStream_t s);
 hipError_t launch_rmsnorm(const float* r, const float* gamma, float eps, int T, int H, float* out,
                           hipStream_t s);
 hipError_t launch_residual_add(float* r, const float* d, size_t n, hipStream_t s);

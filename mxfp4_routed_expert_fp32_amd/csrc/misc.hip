@@ -35,8 +35,17 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
 //    the bf16-activation decode GEMV and of both MFMA kernels, widened to fp32
 //    by placing the 16 bits in the top half.  Nothing is canonicalised: the
 //    export shows exactly the bits those kernels multiply with.
+// The E8M0 byte of block `blk` of row n: the 8-bit table, or (base != null)
+// the scale4 row base plus the block's 4-bit delta.
+__device__ __forceinline__ uint32_t block_scale(const uint8_t* __restrict__ scales, const uint8_t* __restrict__ base,
+                                                size_t n, int cols, int blk) {
+  if (!base) return scales[n * (cols / 32) + blk];
+  return base[n] + ((scales[n * (cols / 64) + blk / 2] >> ((blk & 1) * 4)) & 15u);
+}
+
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
-                                                 const uint8_t* __restrict__ scales, int rows, int cols,
+                                                 const uint8_t* __restrict__ scales,
+                                                 const uint8_t* __restrict__ s4_base, int rows, int cols,
                                                  float* __restrict__ out) {
   const size_t words = (size_t)rows * cols / 8;
   const int wpr = cols / 8;
@@ -44,7 +53,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
     const size_t n = q / wpr;
     const int c8 = (int)(q % wpr);
     const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[q];
-    const uint32_t sbyte = scales[n * (cols / 32) + (c8 * 8) / 32];
+    const uint32_t sbyte = block_scale(scales, s4_base, n, cols, (c8 * 8) / 32);
     float v[8];
     if (sbyte == 0xFFu) {
 #pragma unroll
@@ -62,7 +71,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
 }
 
 __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict__ codes,
-                                                      const uint8_t* __restrict__ scales, int rows, int cols,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const uint8_t* __restrict__ s4_base, int rows, int cols,
                                                       float* __restrict__ out) {
   const size_t words = (size_t)rows * cols / 8;
   const int wpr = cols / 8;
@@ -70,7 +80,7 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict_
     const size_t n = q / wpr;
     const int c8 = (int)(q % wpr);
     const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[q];
-    const uint32_t sbyte = scales[n * (cols / 32) + (c8 * 8) / 32];
+    const uint32_t sbyte = block_scale(scales, s4_base, n, cols, (c8 * 8) / 32);
     const bf16x8 b = decode8(w, e8m0_operand(sbyte));
     uint16_t u[8];
     __builtin_memcpy(u, &b, 16);
@@ -80,15 +90,73 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict_
   }
 }
 
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int rows, int cols, float* out,
-                          bool via_bf16, hipStream_t s) {
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const uint8_t* s4_base, int rows, int cols,
+                          float* out, bool via_bf16, hipStream_t s) {
   const size_t words = (size_t)rows * cols / 8;
   size_t blocks = (words + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (via_bf16)
-    k_dequant_bf16<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
+    k_dequant_bf16<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, s4_base, rows, cols, out);
   else
-    k_dequant<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, rows, cols, out);
+    k_dequant<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, scales, s4_base, rows, cols, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- scale4 encoding
+// One wave per matrix row: the row's smallest scale byte is its base, and
+// every block stores scale - base in 4 bits (two blocks per byte, the even
+// block in the low nibble).  A row whose scales span more than 15 cannot be
+// coded: it adds 1 to *escapes (its deltas are clamped, so the layer must
+// keep the 8-bit table).  Rows hold at most 256 blocks (K <= 8192).
+__global__ __launch_bounds__(256) void k_scale4_encode(const uint8_t* __restrict__ scales8, int64_t e0, int64_t n,
+                                                       int H, int I, uint8_t* __restrict__ scale4,
+                                                       int32_t* __restrict__ escapes) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t rows_per_expert = (int64_t)2 * I + H;
+  const int64_t total = n * rows_per_expert;
+  const size_t sb = (size_t)3 * I * H / 32, ms = (size_t)I * H / 32, dm = (size_t)I * H / 64;
+  const size_t rec = (size_t)2 * I + H + 3 * dm;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave; r < total; r += (int64_t)gridDim.x * 4) {
+    const int64_t e = e0 + r / rows_per_expert;
+    const int64_t rr = r % rows_per_expert;
+    const int m = rr < I ? 0 : (rr < 2 * I ? 1 : 2);
+    const int64_t row = m == 2 ? rr - 2 * I : rr - (int64_t)m * I;
+    const int nb = m == 2 ? I / 32 : H / 32;
+    const uint8_t* src = scales8 + (size_t)(e - e0) * sb + (size_t)m * ms + (size_t)row * nb;
+    uint32_t lo = 255, hi = 0;
+    for (int b = lane; b < nb; b += kWave) {
+      const uint32_t v = src[b];
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t ol = (uint32_t)__shfl_xor((int)lo, off, kWave), oh = (uint32_t)__shfl_xor((int)hi, off, kWave);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    uint8_t* dst = scale4 + (size_t)e * rec;
+    if (lane == 0) {
+      dst[m == 2 ? (size_t)2 * I + row : (size_t)m * I + row] = (uint8_t)lo;
+      if (hi - lo > 15u) atomicAdd(escapes, 1);
+    }
+    uint8_t* dd = dst + (size_t)2 * I + H + (size_t)m * dm + (size_t)row * (nb / 2);
+    for (int i = lane; i < nb / 2; i += kWave) {
+      uint32_t d0 = src[2 * i] - lo, d1 = src[2 * i + 1] - lo;
+      d0 = d0 > 15u ? 15u : d0;
+      d1 = d1 > 15u ? 15u : d1;
+      dd[i] = (uint8_t)(d0 | (d1 << 4));
+    }
+  }
+}
+
+hipError_t launch_scale4_encode(const uint8_t* scales8, int64_t e0, int64_t n, int H, int I, uint8_t* scale4,
+                                int32_t* escapes, hipStream_t s) {
+  const int64_t rows = n * ((int64_t)2 * I + H);
+  int64_t blocks = (rows + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks == 0) return hipSuccess;
+  k_scale4_encode<<<dim3((unsigned)blocks), 256, 0, s>>>(scales8, e0, n, H, I, scale4, escapes);
   return hipGetLastError();
 }
 
