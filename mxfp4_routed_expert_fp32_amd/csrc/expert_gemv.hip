@@ -260,6 +260,31 @@ __device__ __forceinline__ float group_reduce(float v) {
   }
 }
 
+// Copies n16 >= 1 16-byte chunks from global memory into LDS with the nthr
+// threads me = 0 .. nthr - 1: each thread issues 8 loads before its first LDS
+// write, so a batch costs one memory round trip (a load-then-store loop waits
+// for every load in turn).  No load or store sits in a branch (the compiler
+// would sink a load into its store's branch and wait there): an index past
+// the end is clamped to the last chunk, which is then read and written again
+// with its own value.
+__device__ __forceinline__ void stage_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16,
+                                             int me, int nthr) {
+  constexpr int B = 8;
+  for (int c0 = 0; c0 < n16; c0 += B * nthr) {
+    uint4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int c = c0 + me + u * nthr;
+      v[u] = src[c < n16 ? c : n16 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int c = c0 + me + u * nthr;
+      dst[c < n16 ? c : n16 - 1] = v[u];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // Workgroup (pair p, part): wave w takes rows part*4 + w, + 4*parts, ... of
 // the gate and up matrices of the pair's expert, LPR = 64 (one row per step),
@@ -291,22 +316,21 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (size_t)(p / k) * xbytes);
   int e;
   if constexpr (SEL > 0) {
-    __shared__ uint64_t cand[kWave];
-    __shared__ uint32_t sel_e[kWave];
+    __shared__ uint64_t cand[2 * kWave];
     __shared__ int32_t chosen;
     // wave 0 selects at once; the other waves stage the activations meanwhile
     if (wid == 0) {
       const int t = p / k;
       int sel;
       float wv;
-      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, sel_e, &sel, &wv);
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv);
       if (lane == p % k) chosen = sel;
       if (part == 0 && p % k == 0 && lane < k) {
         route[(size_t)t * k + lane] = sel;
         wsel[(size_t)t * k + lane] = wv;
       }
     } else {
-      for (int c = threadIdx.x - kWave; c < xbytes / 16; c += 256 - kWave) xs_lds[c] = xg[c];
+      stage_to_lds(xs_lds, xg, xbytes / 16, threadIdx.x - kWave, 256 - kWave);
     }
     __syncthreads();
     e = __builtin_amdgcn_readfirstlane(chosen);
@@ -333,7 +357,7 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   // stage this token's activations (already done when selecting), then keep
   // the lane's blocks in registers
   if constexpr (SEL == 0) {
-    for (int c = threadIdx.x; c < xbytes / 16; c += 256) xs_lds[c] = xg[c];
+    stage_to_lds(xs_lds, xg, xbytes / 16, threadIdx.x, 256);
     __syncthreads();
   }
   uint32_t xr[NBL][XW];
@@ -404,7 +428,7 @@ __global__ __launch_bounds__(256) void k_down_gemv(const float* __restrict__ hbu
   }
 
   const float4* hsrc = reinterpret_cast<const float4*>(hbuf + (size_t)p * I);
-  for (int q = threadIdx.x; q < I / 4; q += 256) reinterpret_cast<float4*>(hs_lds)[q] = hsrc[q];
+  stage_to_lds(reinterpret_cast<uint4*>(hs_lds), reinterpret_cast<const uint4*>(hsrc), I / 4, threadIdx.x, 256);
   __syncthreads();
   uint32_t hr[NBL2][32];
 #pragma unroll
@@ -586,6 +610,7 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
   *parts = (rows + 4 * pw - 1) / (4 * pw);
 }
 
+static int gu_target(int res) { const char* e = getenv("MOE_GU_PERCU"); return e ? atoi(e) * cu_count() : res; }
 template <bool XF32, int SEL, bool S4>
 static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
                                   const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
@@ -593,7 +618,7 @@ static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, con
 #define MOE_GU(N)                                                                                    \
   {                                                                                                    \
     int parts, rpw;                                                                                    \
-    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N, SEL, S4>, lds), &parts, &rpw);            \
+    split_rows(I, P, 1, gu_target(resident_wgs(k_gateup_gemv<XF32, N, SEL, S4>, lds)), &parts, &rpw); \
     k_gateup_gemv<XF32, N, SEL, S4><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(                     \
         x, route, logits, wsel, codes, scales, H, I, E, k, parts, rpw, hbuf);                          \
   }

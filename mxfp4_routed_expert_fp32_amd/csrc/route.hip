@@ -238,14 +238,13 @@ template <int MAXV>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E,
                                                       int k, int32_t* __restrict__ idx,
                                                       float* __restrict__ wout) {
-  __shared__ uint64_t cand[4][kWave];
-  __shared__ uint32_t sel_e[4][kWave];
+  __shared__ uint64_t cand[4][2 * kWave];
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
   int sel;
   float wsel;
-  topk_wave<MAXV>(logits + (size_t)t * E, E, k, cand[wid], sel_e[wid], &sel, &wsel);
+  topk_wave<MAXV>(logits + (size_t)t * E, E, k, cand[wid], &sel, &wsel);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
     wout[(size_t)t * k + lane] = wsel;
@@ -477,8 +476,7 @@ __global__ __launch_bounds__(kRedTopkThreads) void k_router_reduce_topk(const fl
                                                             float* __restrict__ wout) {
   constexpr int kMaxSplit = 32;  // K slices of 256 for H <= 8192
   __shared__ float lg[kWave * MAXV];
-  __shared__ uint64_t cand[kWave];
-  __shared__ uint32_t sel_e[kWave];
+  __shared__ uint64_t cand[2 * kWave];
   const int t = blockIdx.x;
   const size_t n = (size_t)T * E;
   for (int e = threadIdx.x; e < E; e += kRedTopkThreads) {
@@ -498,7 +496,7 @@ __global__ __launch_bounds__(kRedTopkThreads) void k_router_reduce_topk(const fl
   if (threadIdx.x >= kWave) return;
   int sel;
   float wsel;
-  topk_wave<MAXV>(lg, E, k, cand, sel_e, &sel, &wsel);
+  topk_wave<MAXV>(lg, E, k, cand, &sel, &wsel);
   const int lane = threadIdx.x;
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;

@@ -47,83 +47,118 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // Number of lanes whose 64-bit key is larger than this lane's (keys unique),
 // through a 64-entry LDS buffer of the wave: every lane writes its key, then
-// reads the first n back two at a time (the same address in every lane, a
-// broadcast).  Keys of lanes n and above must be 0 (they never count).  The
-// buffer is free again when the function returns.
+// reads entries back two at a time (the same address in every lane, a
+// broadcast).  Keys of lanes n and above must be 0 (they never count), so the
+// reads cover a fixed 32 or 64 entries, unrolled, and all of them are in
+// flight at once.  The buffer is free again when the function returns.
 __device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf, int n = kWave) {
   const int lane = threadIdx.x % kWave;
   buf[lane] = v;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   int r = 0;
-  for (int j = 0; j < n; j += 2) {
+#pragma unroll
+  for (int j = 0; j < kWave / 2; j += 2) {
     const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
     r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
+  }
+  if (n > kWave / 2) {
+#pragma unroll
+    for (int j = kWave / 2; j < kWave; j += 2) {
+      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
+      r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   return r;
 }
 
+// The logit a rank key was made from (rank_key inverted on its upper word):
+// exact, except that -0 comes back as +0 and every NaN as one NaN pattern.
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
 
-// One wavefront selects for one token; each lane owns experts lane + 64*v,
-// v < MAXV.  Selection: let L be the k-th largest of the 64 lane maxima.  The
-// k largest lane maxima are k keys >= L, so the top k keys are all >= L;
-// these candidates (usually a few more than k) are gathered into one key per
-// lane and each one's rank among them is its place in the route.  When more
-// than 64 keys are >= L (heavy skew inside a few lanes) the wave falls back to
-// k rounds of "take the largest remaining key".  Both give the unique order
-// defined by rank_key.  cand and sel_e are this wave's LDS scratch.
+// One wavefront selects for one token; lane l owns experts MAXV*l + v, v <
+// MAXV (contiguous, so a row of E % 4 == 0 logits is read with 16-byte
+// loads).  Selection: let T be the k-th largest of the 64 lane maxima's top
+// 16 key bits (sign, exponent and 7 mantissa bits of the logit; a 16-step
+// radix select on ballots), as a 32-bit bound.  At least k keys are >= T, so
+// the top k keys all are; these candidates (usually a few more than k) are
+// gathered into one key per lane, each lane writing its own at an offset from
+// a ballot prefix of the per-lane counts (the others into a dummy half of the
+// buffer, so the writes need no branches), and each one's rank among them is
+// its place in the route.  When more than 64 keys qualify (heavy ties or
+// skew) the wave falls back to k rounds of "take the largest remaining key".
+// Both give the unique order defined by rank_key.  cand is this wave's LDS
+// scratch (2 * 64 keys).
 // On return lane j < k holds the expert of rank j in *sel and its softmax
 // weight in *wsel (lanes >= k: expert 0, weight 0).
 template <int MAXV>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, uint64_t* cand,
-                                          uint32_t* sel_e, int* sel_out, float* w_out) {
+                                          int* sel_out, float* w_out) {
+  static_assert(MAXV % 4 == 0, "whole 16-byte loads");
   const int lane = threadIdx.x % kWave;
+  const int e0 = lane * MAXV;
   float lv[MAXV];
+  if ((E & 3) == 0 && (reinterpret_cast<uintptr_t>(l) & 15) == 0) {
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const int e = lane + kWave * v;
-    lv[v] = (e < E) ? l[e] : 0.0f;
+    for (int q = 0; q < MAXV / 4; ++q) {
+      const int e = e0 + 4 * q;  // e < E implies e + 3 < E
+      const float4 f = *reinterpret_cast<const float4*>(l + (e < E ? e : 0));
+      lv[4 * q] = f.x; lv[4 * q + 1] = f.y; lv[4 * q + 2] = f.z; lv[4 * q + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) lv[v] = l[e0 + v < E ? e0 + v : 0];
   }
   uint64_t key[MAXV];
-  uint64_t lmax = 0;
+  uint32_t mo = 0;  // upper word of this lane's largest key
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
-    const int e = lane + kWave * v;
+    const int e = e0 + v;
     key[v] = (e < E) ? rank_key(lv[v], (uint32_t)e) : 0ull;
-    lmax = umax64(lmax, key[v]);
+    const uint32_t o = (uint32_t)(key[v] >> 32);
+    mo = o > mo ? o : mo;
   }
-  // L = k-th largest lane maximum (the lane of rank k-1); 0 if fewer lanes hold keys
-  const int lrank = rank_in_wave_lds(lmax, cand);
-  const uint64_t sel_lane = __builtin_amdgcn_ballot_w64(lrank == k - 1);
-  uint64_t L = 0;
-  if (sel_lane) {
-    const int src = __builtin_ctzll(sel_lane);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)lmax, src);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(lmax >> 32), src);
-    L = ((uint64_t)hi << 32) | lo;
-  }
-  // candidates: keys >= L, compacted into cand[] in (slot, lane) order: one
-  // ballot per slot gives each candidate its position (no atomics)
-  uint32_t total = 0;  // the same in every lane
+  // T: the largest multiple of 2^16 with at least k lane maxima at or above
+  // it, built bit by bit from the top
+  uint32_t T = 0;
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const bool c = key[v] != 0ull && key[v] >= L;
-    const uint64_t b = __builtin_amdgcn_ballot_w64(c);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-    if (c && total + below < (uint32_t)kWave) cand[total + below] = key[v];
-    total += (uint32_t)__builtin_popcountll(b);
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(mo >= c)) >= k) T = c;
+  }
+  // candidates: present keys whose upper word is >= T; lane offsets from a
+  // prefix of the per-lane counts, one ballot per count bit
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) cnt += (key[v] != 0ull && (uint32_t)(key[v] >> 32) >= T) ? 1u : 0u;
+  uint32_t excl = 0, total = 0;
+#pragma unroll
+  for (int b = 0; (1 << b) <= MAXV; ++b) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64((cnt >> b) & 1u);
+    excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    total += (uint32_t)__builtin_popcountll(m) << b;
   }
 
-  int my_rank = kWave;          // rank of this lane's entry (>= k: not selected)
-  uint32_t my_e = 0;
+  int my_rank = kWave;  // rank of this lane's entry (>= k: not selected)
+  uint64_t my_key = 0;
   if (total <= (uint32_t)kWave) {
+    uint32_t ptr = excl;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const bool c = key[v] != 0ull && (uint32_t)(key[v] >> 32) >= T;
+      cand[c ? ptr : kWave + lane] = key[v];  // non-candidates go to the dummy half
+      ptr += c ? 1u : 0u;
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
     const int r = rank_in_wave_lds(c, cand, (int)total);  // candidates only (usually about k)
-    if ((uint32_t)lane < total) { my_rank = r; my_e = ~(uint32_t)c; }
+    if ((uint32_t)lane < total) { my_rank = r; my_key = c; }
   } else {
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
@@ -133,24 +168,18 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
 #pragma unroll
       for (int v = 0; v < MAXV; ++v)
         if (key[v] == win) key[v] = 0;
-      if (lane == j) { my_rank = j; my_e = ~(uint32_t)win; }
+      if (lane == j) { my_rank = j; my_key = win; }
     }
   }
-  // lane r < k receives the entry of rank r
-  if (my_rank < k) sel_e[my_rank] = my_e;
+  // lane r < k receives the key of rank r (cand is free again)
+  if (my_rank < k) cand[my_rank] = my_key;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int sel = (lane < k) ? (int)sel_e[lane] : 0;
-  // softmax over the selected logits, in rank order; each logit is read back
-  // from the registers of the lane that holds it (lane sel % 64, slot
-  // sel / 64), not from memory
-  float lj = 0.0f;
-#pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const float x = __shfl(lv[v], sel % kWave, kWave);
-    if (sel / kWave == v) lj = x;
-  }
-  if (lane >= k) lj = 0.0f;
+  const uint64_t kj = (lane < k) ? cand[lane] : 0ull;
+  const int sel = (lane < k) ? (int)~(uint32_t)kj : 0;
+  // softmax over the selected logits, in rank order, each logit decoded from
+  // its key; lane 0 holds the largest
+  const float lj = (lane < k) ? key_logit(kj) : 0.0f;
   const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
   const float ex = (lane < k) ? expf(lj - m) : 0.0f;
   const float s = wave_sum(ex);
