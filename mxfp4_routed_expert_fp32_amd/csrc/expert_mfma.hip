@@ -585,8 +585,13 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
 // of its expert block back to back: the weight and activation rings run on
 // across tile boundaries (the next tile's first weights are in flight while
 // this tile finishes), and only the first tile waits for a cold pipeline.
-// Scales come straight from memory here: a row's I/32 scale bytes are few
-// (48), so 16 rows share a handful of lines that stay in L2.
+// Scales: for blocks of up to 4 m-tiles, where it fits beside the activation
+// ring (I/32 + 8 <= 60 bytes per row, so I <= 1664, which holds the model's
+// I = 1536), each tile's 256 rows of scales are staged in an LDS table as in
+// gate/up, so a superchunk's 8 bytes per row come from LDS instead of a fresh
+// memory sector.  The next tile's scales are requested with the tile's last
+// superchunk and written to the table at the tile boundary.  Larger blocks
+// and wider I read them from memory per superchunk.
 constexpr int kDN_NT = 256;
 constexpr int kDnTiles = 4;
 // Weight ring: 3 superchunks (K = 1536 gives 6 per tile).
@@ -624,11 +629,31 @@ static_assert(dma_waits_exact(4, 2, 6, 3, 48) && dma_waits_exact(3, 4, 6, 3, 48)
                   dma_waits_exact(1, 8, 6, 2, 48) && dma_waits_exact(4, 2, 6, 3, 24) && dma_waits_exact(1, 8, 6, 2, 8) &&
                   dma_waits_exact(3, 4, 6, 3, 6),
               "down DMA wait counts");
+// with the LDS scale table: 4 code loads per even chunk
+static_assert(dma_waits_exact(4, 2, 4, 3, 48) && dma_waits_exact(3, 4, 4, 3, 48) && dma_waits_exact(2, 6, 4, 2, 48) &&
+                  dma_waits_exact(1, 8, 4, 2, 48) && dma_waits_exact(4, 2, 4, 3, 24) && dma_waits_exact(1, 8, 4, 2, 8) &&
+                  dma_waits_exact(3, 4, 4, 3, 6),
+              "down DMA wait counts (scale table)");
+// 16-byte scale pieces per thread for one tile's table (I/32 <= 52 bytes a row)
+constexpr int kDnScaleU = (kDN_NT * 52 + kThr * 16 - 1) / (kThr * 16);
+constexpr int kDnTableMaxNb = 52;
+static_assert(kDnActBytes + kDN_NT * (kDnTableMaxNb + 8) + 2 * kMB * 4 <= 160 * 1024, "scale table fits");
+
+// Barrier with the LDS drain only (no wait for loads in flight): for LDS
+// writes that other waves read after it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Tiles nt0 .. nt0 + kDnTiles - 1 (those below ntiles) of one expert block.
 // Superchunk index G runs over the tiles, nscp (the per-tile superchunk
 // count rounded up to the ring) per tile; superchunks past K read zeros.
-template <int MT, int DB, int NB>
+template <int MT, int DB, int NB, bool TAB>
 __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, int I, int P, rsrc_t rh,
                                            const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                            const int32_t* pid, const uint32_t* row_base, uint8_t* lds,
@@ -661,25 +686,36 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
     vcode[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)(nbk * 16) + 16u * g;
     vscale[j] = (uint32_t)(rbase + 16 * j) * (uint32_t)nbk;
   }
-  // load k (0..5) of superchunk G: n-tile k / 3, part k % 3
+  // scale table (TAB): the current tile's 256 rows, rows of pitch nbk + 8;
+  // this lane's rows are wid * 32 + nl (n-tile 0) and 16 further (n-tile 1)
+  uint8_t* tab = lds + kDnActBytes;
+  const int pitch = scale_row_pitch(nbk);
+  const uint8_t* srow = tab + (wid * 32 + nl) * pitch;
+  const uint32_t ttotal = (uint32_t)kDN_NT * (uint32_t)nbk;
+  SPieces<kDnScaleU> spc;
+  if constexpr (TAB) scales_fetch<kDnScaleU>(spc, rs, (uint32_t)(nt0 * kDN_NT) * (uint32_t)nbk, ttotal);
+  // NL weight loads per superchunk: per n-tile two code blocks (and, without
+  // the table, the 8 scale bytes); load k of superchunk G is n-tile k / PN,
+  // part k % PN
+  constexpr int PN = TAB ? 2 : 3, NL = 2 * PN;
   auto load_b_part = [&](BSuper (&b)[2], int G, int k) {
     const int t = G / nscp, sc = G - t * nscp;
     const bool ok = G < gend && sc < nsc;
     const uint32_t scode = (uint32_t)t * (uint32_t)(kDN_NT * nbk * 16) + (uint32_t)sc * 128u;
     const uint32_t sscale = (uint32_t)t * (uint32_t)(kDN_NT * nbk) + (uint32_t)sc * 8u;
-    load_bsuper_part(b[k / 3], rc, rs, vcode[k / 3], vscale[k / 3], scode, sscale, ok, k % 3);
+    load_bsuper_part(b[k / PN], rc, rs, vcode[k / PN], vscale[k / PN], scode, sscale, ok, k % PN);
   };
   auto load_b = [&](BSuper (&b)[2], int G) {
 #pragma unroll
-    for (int k = 0; k < 6; ++k) load_b_part(b, G, k);
+    for (int k = 0; k < NL; ++k) load_b_part(b, G, k);
   };
-  // As in gate/up, an even chunk's six weight loads go one at a time between
-  // its multiplies (pairs 1 + k WS, all before the chunk's closing wait) when
-  // it has enough pairs, else up front; they always follow the chunk's DMA.
+  // As in gate/up, an even chunk's weight loads go one at a time between its
+  // multiplies (pairs 1 + k WS, all before the chunk's closing wait) when it
+  // has enough pairs, else up front; they always follow the chunk's DMA.
   constexpr int kDnNQ = 4 * MT;
   constexpr bool kDnSpread = kDnNQ >= 8;
-  constexpr int kDnWS = kDnSpread ? (kDnNQ - 2) / 6 : 0;
-  static_assert(!kDnSpread || 1 + 5 * kDnWS < kDnNQ, "weight loads before the chunk's wait");
+  constexpr int kDnWS = kDnSpread ? (kDnNQ - 2) / NL : 0;
+  static_assert(!kDnSpread || 1 + (NL - 1) * kDnWS < kDnNQ, "weight loads before the chunk's wait");
   // activations of global chunk q (chunk q % (2 nscp) of its tile; past K or
   // past the last tile: zeros), both terms, into buffer `buf`
   uint32_t doff[MS / 2];
@@ -699,16 +735,24 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
     if (v + DA >= 0) dma_q(v + DA, lds + (v + DA) * kBuf);
     if (v % 2 == 0 && v / 2 + DB - 1 >= 0) load_b(rb[v / 2 + DB - 1], v / 2 + DB - 1);
   }
-  wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1)>();
+  if constexpr (TAB) scales_put<kDnScaleU>(spc, tab, nbk, ttotal);
+  wait_vm_barrier<dma_wait_ops(NB - 1, MS, NL, 1)>();  // (draining LDS: the table is written)
 
   f32x4 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int slot = 0;  // LDS buffer of the current chunk
+  uint32_t sv[2][2];  // TAB: the current superchunk's scale bytes [n-tile][chunk]
   for (int G0 = 0; G0 < gend; G0 += DB) {
+    const bool tile_end = (G0 + DB) % nscp == 0;
+    const bool more_tiles = G0 / nscp + 1 < ntw;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
+      // the next tile's scales, requested with this tile's last superchunk
+      if constexpr (TAB)
+        if (d == DB - 1 && tile_end && more_tiles)
+          scales_fetch<kDnScaleU>(spc, rs, (uint32_t)((nt0 + G0 / nscp + 1) * kDN_NT) * (uint32_t)nbk, ttotal);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int q = 2 * G0 + 2 * d + h;  // global chunk
@@ -721,8 +765,21 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint8_t* Ah = lds + slot * kBuf;
         const uint8_t* Al = Ah + kTerm;
-        const float s0v = e8m0_operand((rb[d][0].s[h] >> (8 * g)) & 0xFFu);
-        const float s1v = e8m0_operand((rb[d][1].s[h] >> (8 * g)) & 0xFFu);
+        if constexpr (TAB) {
+          if (h == 0) {  // the superchunk's 8 bytes of both rows, from the table
+            const int sc = (G0 + d) % nscp;
+            const bool ok = sc < nsc;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const u32x2 v = *reinterpret_cast<const u32x2*>(srow + j * 16 * pitch + (ok ? sc : 0) * 8);
+              sv[j][0] = ok ? v[0] : 0u;
+              sv[j][1] = ok ? v[1] : 0u;
+            }
+          }
+        }
+        const uint32_t sb0 = TAB ? sv[0][h] : rb[d][0].s[h], sb1 = TAB ? sv[1][h] : rb[d][1].s[h];
+        const float s0v = e8m0_operand((sb0 >> (8 * g)) & 0xFFu);
+        const float s1v = e8m0_operand((sb1 >> (8 * g)) & 0xFFu);
         // pair i = s*MT + m (step s, m-tile m); both terms' fragments of pair
         // i + kDnPF are requested before the four multiplies of pair i
         constexpr int kDnPF = dn_pf(MT);
@@ -744,7 +801,7 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           }
           if (kDnSpread && h == 0) {
 #pragma unroll
-            for (int k = 0; k < 6; ++k)
+            for (int k = 0; k < NL; ++k)
               if (i == 1 + k * kDnWS) load_b_part(rb[(d + DB - 1) % DB], G0 + d + DB - 1, k);
           }
           if (m == 0 && st > 0) {
@@ -758,8 +815,8 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
           acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[i % RF], b1, acc[m][1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == 0) wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 0), false>();
-        else wait_vm_barrier<dma_wait_ops(NB - 1, MS, 6, 1), false>();
+        if (h == 0) wait_vm_barrier<dma_wait_ops(NB - 1, MS, NL, 0), false>();
+        else wait_vm_barrier<dma_wait_ops(NB - 1, MS, NL, 1), false>();
         slot = slot + 1 == NB ? 0 : slot + 1;
       }
     }
@@ -779,11 +836,21 @@ __device__ __forceinline__ void down_block(int e, int nt0, int ntiles, int H, in
         }
         acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      if constexpr (TAB) {
+        if (more_tiles) {
+          // every wave has used this tile's table (its reads fed the
+          // multiplies above) before the next tile's rows replace it
+          lds_barrier();
+          scales_put<kDnScaleU>(spc, tab, nbk, ttotal);
+          lds_barrier();
+        }
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no LDS transfer outlives the loop
 }
 
+template <bool TAB>
 __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
     const uint16_t* __restrict__ hterm, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
@@ -809,15 +876,22 @@ __global__ __launch_bounds__(kThr, 1) void k_down_mfma(
   __syncthreads();
   const rsrc_t rh = mk_rsrc(hterm, (uint32_t)((size_t)P * I * 4));
   const int nt0 = ng * kDnTiles;
+  // TAB: the launch sized LDS for the scale table (I / 32 <= kDnTableMaxNb).
+  // Blocks of up to 4 m-tiles use it; larger ones read their scales per
+  // superchunk (measured at 4096 tokens, ~5 m-tiles a block: the table cost
+  // 2%; on 1-2 m-tile blocks it saved 5%)
+#define DN(M) \
+  down_block<M, dn_db(M), dn_nbuf(M), TAB && (M <= 4)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, \
+                                                       lds8, ybuf)
   switch ((cnt + 15) / 16) {
-    case 1: down_block<1, dn_db(1), dn_nbuf(1)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 2: down_block<2, dn_db(2), dn_nbuf(2)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 3: down_block<3, dn_db(3), dn_nbuf(3)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 4: down_block<4, dn_db(4), dn_nbuf(4)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 5: down_block<5, dn_db(5), dn_nbuf(5)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 6: down_block<6, dn_db(6), dn_nbuf(6)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    case 7: down_block<7, dn_db(7), dn_nbuf(7)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
-    default: down_block<8, dn_db(8), dn_nbuf(8)>(e, nt0, ntiles, H, I, P, rh, codes, scales, pid, row_base, lds8, ybuf); break;
+    case 1: DN(1); break;
+    case 2: DN(2); break;
+    case 3: DN(3); break;
+    case 4: DN(4); break;
+    case 5: DN(5); break;
+    case 6: DN(6); break;
+    case 7: DN(7); break;
+    default: DN(8); break;
   }
 }
 
@@ -1035,12 +1109,15 @@ constexpr size_t kStaticLds = 2 * kMB * 4;
 static size_t gu_table_bytes(int H) { return (size_t)2 * kGU_NT * scale_row_pitch(H / 32); }
 static bool gu_large(int H) { return kGuActLarge + gu_table_bytes(H) + kStaticLds <= kLdsBytes; }
 static size_t gateup_lds(int H) { return (size_t)(gu_large(H) ? kGuActLarge : kGuActSmall) + gu_table_bytes(H); }
-static size_t down_lds() { return (size_t)kDnActBytes; }
+static size_t down_lds(int I) {
+  const int nb = I / 32;
+  return (size_t)kDnActBytes + (nb <= kDnTableMaxNb ? (size_t)kDN_NT * scale_row_pitch(nb) : 0);
+}
 
 bool grouped_shape_ok(int64_t H, int64_t I) {
   if (H <= 0 || I <= 0 || H % 256 != 0 || I % 256 != 0) return false;
   if (H / 32 > 64 * kGuScaleU) return false;
-  return gateup_lds((int)H) + kStaticLds <= kLdsBytes && down_lds() + kStaticLds <= kLdsBytes;
+  return gateup_lds((int)H) + kStaticLds <= kLdsBytes && down_lds((int)I) + kStaticLds <= kLdsBytes;
 }
 
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
@@ -1058,9 +1135,13 @@ hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const i
                             float* ybuf, hipStream_t s) {
   const int ntiles = (H + kDN_NT - 1) / kDN_NT;
   const int ngroups = (ntiles + kDnTiles - 1) / kDnTiles;
-  const size_t lds = down_lds();
-  k_down_mfma<<<dim3(items_grid(max_blocks, ngroups)), kThr, lds, s>>>(hterm, pairs, blocks, nblocks, codes,
-                                                                        scales, H, I, E, P, max_blocks, ntiles, ybuf);
+  const size_t lds = down_lds(I);
+  if (I / 32 <= kDnTableMaxNb)
+    k_down_mfma<true><<<dim3(items_grid(max_blocks, ngroups)), kThr, lds, s>>>(
+        hterm, pairs, blocks, nblocks, codes, scales, H, I, E, P, max_blocks, ntiles, ybuf);
+  else
+    k_down_mfma<false><<<dim3(items_grid(max_blocks, ngroups)), kThr, lds, s>>>(
+        hterm, pairs, blocks, nblocks, codes, scales, H, I, E, P, max_blocks, ntiles, ybuf);
   return hipGetLastError();
 }
 
