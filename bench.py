@@ -73,6 +73,7 @@ KERNEL_SOURCES = {
     "k_down_ks": ["expert_gemv.hip", "common.h"],
     "k_gateup_mfma": ["expert_mfma.hip", "common.h"],
     "k_down_mfma": ["expert_mfma.hip", "common.h"],
+    "k_int8_gemv": ["int8_gemv.hip", "common.h"],
 }
 
 
@@ -740,7 +741,8 @@ def bench_int8(a, steps, warmup):
                               "GBps": dq_bytes / (dq_us * 1e-6) / 1e9,
                               "frac": dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
     roofline = {"bound": "hbm", "kernel": "k_int8_gemv (default split)", "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_per,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("k_int8_gemv", "spine_int8"),
+                "bytes_per_launch": bytes_per,
                 "avg_launch_us": us}
     return base_fields("packed-int8 spine GEMV rows/s (12288 x 7168)", N / (us * 1e-6), "rows/s", max(steps, 4 * NM),
                        warmup, us * 1e-3, None, cfg, roofline, parity_obj([0], nw_, ew_))
