@@ -107,20 +107,27 @@ __device__ __forceinline__ float quad_fma_f32(uint32_t q, float s, const uint32_
 }
 
 // Same with fp32 activations (32 floats, as bit patterns): exact fp32 weights,
-// fp32 FMA.
+// fp32 FMA.  PIN: a scheduling barrier after each code dword keeps the
+// conversions next to their FMAs (hoisted ahead, the 32 converted weights of
+// a block are all live at once, which costs the K-split down kernel two
+// waves per SIMD).
+template <bool PIN = false>
 __device__ __forceinline__ float block_dot_f32(uint4 q, float s, const uint32_t* xf, float acc) {
   acc = quad_fma_f32<0>(q.x, s, xf, acc);
   acc = quad_fma_f32<1>(q.x, s, xf, acc);
   acc = quad_fma_f32<2>(q.x, s, xf, acc);
   acc = quad_fma_f32<3>(q.x, s, xf, acc);
+  if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
   acc = quad_fma_f32<0>(q.y, s, xf + 8, acc);
   acc = quad_fma_f32<1>(q.y, s, xf + 8, acc);
   acc = quad_fma_f32<2>(q.y, s, xf + 8, acc);
   acc = quad_fma_f32<3>(q.y, s, xf + 8, acc);
+  if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
   acc = quad_fma_f32<0>(q.z, s, xf + 16, acc);
   acc = quad_fma_f32<1>(q.z, s, xf + 16, acc);
   acc = quad_fma_f32<2>(q.z, s, xf + 16, acc);
   acc = quad_fma_f32<3>(q.z, s, xf + 16, acc);
+  if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
   acc = quad_fma_f32<0>(q.w, s, xf + 24, acc);
   acc = quad_fma_f32<1>(q.w, s, xf + 24, acc);
   acc = quad_fma_f32<2>(q.w, s, xf + 24, acc);
@@ -230,7 +237,7 @@ __device__ __forceinline__ uint32_t scale_byte(const RowBlocks<NBL>& r, int m, i
     return r.s[m];
 }
 
-template <bool XF32, int NBL, bool S4>
+template <bool XF32, int NBL, bool S4, bool PIN = false>
 __device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t (*xr)[XF32 ? 32 : 16], int sh) {
   float acc = 0.0f;
 #pragma unroll
@@ -238,7 +245,7 @@ __device__ __forceinline__ float row_dot(const RowBlocks<NBL>& r, const uint32_t
     const float s = e8m0_operand(scale_byte<S4>(r, m, sh));
     const uint4 q = make_uint4(r.q[m].x, r.q[m].y, r.q[m].z, r.q[m].w);
     if constexpr (XF32)
-      acc = block_dot_f32(q, s, xr[m], acc);
+      acc = block_dot_f32<PIN>(q, s, xr[m], acc);
     else
       acc = block_dot_bf16(q, s, xr[m], acc);
   }
@@ -475,13 +482,19 @@ constexpr int kDnKsLdsCap = 16384;
 // adds the KS partials of each row in wave order (a fixed order, so results
 // are deterministic).  Weight loads run D-1 steps ahead; rows_per_wg is a
 // multiple of 4*D, so the unrolled ring has no exit inside.
-template <int KS, int D, bool S4>
+//
+// TAB (8-bit scales only): the workgroup's scale bytes, rows_per_wg rows x
+// I/32 contiguous bytes of the table, are copied into LDS once, before the
+// first row, by one 16-byte load per thread and chunk; each step then reads
+// its scale byte from LDS instead of issuing a one-byte load per code load.
+template <int KS, int D, bool S4, bool TAB>
 __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ hbuf,
                                                      const int32_t* __restrict__ pair_expert,
                                                      const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales, int H, int I, int E,
                                                      int parts, int rows_per_wg, float* __restrict__ ybuf) {
-  extern __shared__ float partial[];  // [rows_per_wg][KS]
+  static_assert(!(TAB && S4), "the LDS scale table holds 8-bit scales");
+  extern __shared__ float partial[];  // [rows_per_wg][KS], then (TAB) the scale table [rows_per_wg][I/32]
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, ks = threadIdx.x / kWave;
@@ -498,11 +511,27 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
   const int r0 = part * rows_per_wg;
   const int steps = rows_per_wg / 4;
 
+  // TAB: the table's 16-byte chunks, loaded first (the ring's loads behind
+  // them need not land before the table is written to LDS)
+  uint8_t* tab = reinterpret_cast<uint8_t*>(partial + rows_per_wg * KS);
+  const int tab_n16 = TAB ? (min(rows_per_wg, H - r0) * nbk) / 16 : 0;
+  constexpr int kTabLoads = 2;  // chunks per thread (rows_per_wg * I/32 <= 2 * 16 * 64 * KS)
+  u32x4 tv[kTabLoads];
+  if constexpr (TAB) {
+#pragma unroll
+    for (int u = 0; u < kTabLoads; ++u) {
+      const int t = threadIdx.x + u * 64 * KS;
+      tv[u] = __builtin_amdgcn_raw_buffer_load_b128(dsc.tab, t < tab_n16 ? (uint32_t)r0 * (uint32_t)nbk + 16u * t : kOOB,
+                                                    0, 2 /* nt */);
+    }
+  }
   auto load = [&](RowBlocks<1>& r, int st) {
     const int n = r0 + 4 * st + rsub;
     const bool ok = st < steps && n < H;
     r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(dcod, ok ? (uint32_t)n * (uint32_t)(I / 2) + 16u * b : kOOB, 0, 2);
-    if constexpr (S4) {
+    if constexpr (TAB) {
+      r.s[0] = 0u;  // read from LDS when the step is computed
+    } else if constexpr (S4) {
       // rows r0 + 4 st .. + 3 (4-aligned) share one dword of bases: a scalar load
       const int j = (st < steps && r0 + 4 * st < H) ? (r0 + 4 * st) >> 2 : 0;
       r.base = (bases4(dsc.bptr, j) >> (rsub * 8)) & 0xFFu;
@@ -513,9 +542,10 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
       r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(dsc.tab, ok ? (uint32_t)n * (uint32_t)nbk + b : kOOB, 0, 2 /* nt */);
     }
   };
-  RowBlocks<1> ring[D];
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d) load(ring[d], d);
+  // h before the ring: loads complete in issue order, so the first row's
+  // wait for h then leaves the ring's later loads in flight (issued after
+  // the ring, that wait would cover them too, and the compiler keeps it in
+  // every pass of the loop)
   uint32_t hr[1][32];
   const float4* hp = reinterpret_cast<const float4*>(hbuf + (size_t)p * I + 32 * b);
 #pragma unroll
@@ -524,13 +554,29 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
     hr[0][4 * v] = __float_as_uint(f.x); hr[0][4 * v + 1] = __float_as_uint(f.y);
     hr[0][4 * v + 2] = __float_as_uint(f.z); hr[0][4 * v + 3] = __float_as_uint(f.w);
   }
+  RowBlocks<1> ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) load(ring[d], d);
+
+  if constexpr (TAB) {
+#pragma unroll
+    for (int u = 0; u < kTabLoads; ++u) {
+      const int t = threadIdx.x + u * 64 * KS;
+      if (t < tab_n16) reinterpret_cast<u32x4*>(tab)[t] = tv[u];
+    }
+    __syncthreads();
+  }
 
   for (int s0 = 0; s0 < steps; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int st = s0 + d;
       load(ring[(d + D - 1) % D], st + D - 1);
-      const float v = lane_group_sum<16>(row_dot<true, 1, S4>(ring[d], hr, sh));
+      if constexpr (TAB) {
+        const int rr = 4 * st + rsub;  // a row past H reads a byte no result uses
+        ring[d].s[0] = tab[rr * nbk + b];
+      }
+      const float v = lane_group_sum<16>(row_dot<true, 1, S4, true>(ring[d], hr, sh));
       if (c == 15) partial[(4 * st + rsub) * KS + ks] = v;
     }
   }
@@ -610,7 +656,6 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
   *parts = (rows + 4 * pw - 1) / (4 * pw);
 }
 
-static int gu_target(int res) { const char* e = getenv("MOE_GU_PERCU"); return e ? atoi(e) * cu_count() : res; }
 template <bool XF32, int SEL, bool S4>
 static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
                                   const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
@@ -618,7 +663,7 @@ static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, con
 #define MOE_GU(N)                                                                                    \
   {                                                                                                    \
     int parts, rpw;                                                                                    \
-    split_rows(I, P, 1, gu_target(resident_wgs(k_gateup_gemv<XF32, N, SEL, S4>, lds)), &parts, &rpw); \
+    split_rows(I, P, 1, resident_wgs(k_gateup_gemv<XF32, N, SEL, S4>, lds), &parts, &rpw); \
     k_gateup_gemv<XF32, N, SEL, S4><<<dim3((unsigned)(P * parts)), 256, lds, s>>>(                     \
         x, route, logits, wsel, codes, scales, H, I, E, k, parts, rpw, hbuf);                          \
   }
@@ -719,11 +764,19 @@ static hipError_t down_dispatch(const float* hbuf, const int32_t* pair_expert, i
     const int max_rows = kDnKsLdsCap / (ks * 4) / (4 * D) * (4 * D);
     if (rows > max_rows) rows = max_rows;
     const int parts = (H + rows - 1) / rows;
-    const size_t lds = (size_t)rows * ks * 4;
+    // the LDS scale table when the workgroup's scales fit two 16-byte chunks per thread
+    const bool tab = !S4 && rows * (I / 32) <= 2 * 16 * 64 * ks;
+    const size_t lds = (size_t)rows * ks * 4 + (tab ? (size_t)rows * (I / 32) : 0);
     const dim3 grid((unsigned)(P * parts));
 #define MOE_DN_KS(KS)                                                                                     \
-  if (ks == KS)                                                                                            \
-    k_down_ks<KS, D, S4><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E, parts, rows, ybuf);
+  if (ks == KS) {                                                                                          \
+    if (tab)                                                                                               \
+      k_down_ks<KS, D, false, true><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E,  \
+                                                              parts, rows, ybuf);                          \
+    else                                                                                                   \
+      k_down_ks<KS, D, S4, false><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E,    \
+                                                            parts, rows, ybuf);                            \
+  }
     MOE_DN_KS(2) MOE_DN_KS(3) MOE_DN_KS(4) MOE_DN_KS(6) MOE_DN_KS(8)
 #undef MOE_DN_KS
     return hipGetLastError();
