@@ -31,11 +31,11 @@
 
 namespace moe {
 
-// Workgroups of `fn` (256 threads, `lds` bytes of LDS) the current device holds
-// at once.  Queried once per (kernel, LDS size, device) and remembered in a
-// fixed table (no heap use on a launch path; when the table is full the value
-// is simply queried again).
-static int resident_wgs_query(const void* fn, size_t lds) {
+// Workgroups of `fn` (`threads` threads, `lds` bytes of LDS) the current
+// device holds at once.  Queried once per (kernel, LDS size, device) and
+// remembered in a fixed table (no heap use on a launch path; when the table
+// is full the value is simply queried again).
+static int resident_wgs_query(const void* fn, size_t lds, int threads) {
   struct Entry { const void* fn; size_t lds; int dev; int value; };
   constexpr int kSlots = 256;
   static std::mutex mu;
@@ -50,7 +50,7 @@ static int resident_wgs_query(const void* fn, size_t lds) {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
   const int v = cus * per_cu;
   std::lock_guard<std::mutex> g(mu);
   if (used < kSlots) table[used++] = Entry{fn, lds, dev, v};
@@ -58,8 +58,8 @@ static int resident_wgs_query(const void* fn, size_t lds) {
 }
 
 template <typename F>
-static int resident_wgs(F fn, size_t lds) {
-  return resident_wgs_query(reinterpret_cast<const void*>(fn), lds);
+static int resident_wgs(F fn, size_t lds, int threads = 256) {
+  return resident_wgs_query(reinterpret_cast<const void*>(fn), lds, threads);
 }
 
 // Compute units of the current device (remembered per device in a fixed table).
@@ -396,6 +396,173 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------- gate/up + SwiGLU, K split across waves
+// For H = 1024*KS (KS in {1, 2, 4, 7, 8}; the model's H = 7168 gives 7): wave
+// ks of a 64*KS-thread workgroup takes code blocks 32 ks .. 32 ks + 31 of
+// every gate and up row of the workgroup's row range, 32 lanes per row and two
+// rows per step (512 contiguous code bytes per row and matrix), so a lane
+// keeps one 32-element block of x in registers, loaded straight from memory.
+// Low register use lets several waves per SIMD overlap the weight stream with
+// the decode and dot-product work.  Each wave reduces its 32 lanes per row and
+// leaves the partial sum in LDS; at the end the workgroup adds the KS partials
+// of each row in wave order (a fixed order, so results are deterministic) and
+// applies SwiGLU.  Weight loads run D - 1 steps ahead; rows_per_wg is a
+// multiple of 2 D, so the unrolled ring has no exit inside.
+// Scales: 8-bit, the workgroup's rows of both tables (contiguous bytes) are
+// copied into LDS once before the first row; scale4, the row base by a scalar
+// load and the block's delta by a byte load beside its code load.
+// SEL as in k_gateup_gemv: wave 0 selects while the other waves load x.
+constexpr int kGuKsRing = 4;       // weight steps in flight + 1
+constexpr int kGuKsTabLoads = 2;   // 16-byte scale chunks per thread and matrix
+// rows_per_wg * H/32 <= kGuKsTabLoads * 16 * 64 * KS (the table's capacity), in whole ring passes
+constexpr int kGuKsMaxRows = 32 * kGuKsTabLoads / (2 * kGuKsRing) * (2 * kGuKsRing);
+
+template <int KS, int D, bool XF32, int SEL, bool S4>
+__global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ x, int32_t* __restrict__ route,
+                                                       const float* __restrict__ logits, float* __restrict__ wsel,
+                                                       const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales, int H, int I, int E,
+                                                       int k, int parts, int rows_per_wg,
+                                                       float* __restrict__ hbuf) {
+  constexpr int XW = XF32 ? 32 : 16;  // registers per block of x
+  constexpr bool TAB = !S4;
+  // [rows_per_wg][2][KS] partials, then (TAB) the gate and up scale rows,
+  // [rows_per_wg][H/32] each
+  extern __shared__ float partial[];
+  const int p = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
+  const int lane = threadIdx.x % kWave, ks = threadIdx.x / kWave;
+  const int c = lane % 32, rsub = lane / 32;
+  const int nb = H / 32;
+  const int b = ks * 32 + c;  // this lane's block of every row
+  const int t = p / k;
+
+  // this lane's 32 activations (the selecting wave loads them after the
+  // selection, which then has the registers to itself)
+  uint32_t xr[1][XW];
+  auto load_x = [&]() {
+    const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) +
+                                                     (size_t)t * (XF32 ? H * 4 : H * 2) + (size_t)b * (XW * 4));
+#pragma unroll
+    for (int v = 0; v < XW / 4; ++v) {
+      const u32x4 u = xp[v];
+      xr[0][4 * v] = u.x; xr[0][4 * v + 1] = u.y; xr[0][4 * v + 2] = u.z; xr[0][4 * v + 3] = u.w;
+    }
+  };
+  int e;
+  if constexpr (SEL > 0) {
+    __shared__ uint64_t cand[2 * kWave];
+    __shared__ int32_t chosen;
+    if (ks != 0) load_x();
+    if (ks == 0) {
+      int sel;
+      float wv;
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv);
+      if (lane == p % k) chosen = sel;
+      if (part == 0 && p % k == 0 && lane < k) {
+        route[(size_t)t * k + lane] = sel;
+        wsel[(size_t)t * k + lane] = wv;
+      }
+    }
+    __syncthreads();
+    e = __builtin_amdgcn_readfirstlane(chosen);
+    if (ks == 0) load_x();
+  } else {
+    load_x();
+    e = __builtin_amdgcn_readfirstlane(route[p]);
+  }
+  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  const size_t cb = (size_t)3 * I * H / 2;
+  const uint32_t mc = (uint32_t)((size_t)I * H / 2);
+  const rsrc_t gcod = make_rsrc(codes + (size_t)e * cb, mc);
+  const rsrc_t ucod = make_rsrc(codes + (size_t)e * cb + mc, mc);
+  const ScaleSrc gsc = matrix_scales<S4>(scales, e, 0, H, I);
+  const ScaleSrc usc = matrix_scales<S4>(scales, e, 1, H, I);
+  const int sh = (c & 1) * 4;
+  const int r0 = part * rows_per_wg;
+  const int nrows = min(rows_per_wg, I - r0);
+  const int steps = rows_per_wg / 2;
+
+  // TAB: both matrices' scale rows r0 .. r0 + nrows - 1, loaded first (the
+  // ring's loads behind them need not land before the table is written)
+  uint8_t* tab = reinterpret_cast<uint8_t*>(partial + rows_per_wg * 2 * KS);
+  const int tab_n16 = TAB ? nrows * nb / 16 : 0;  // chunks per matrix
+  u32x4 tg[kGuKsTabLoads], tu[kGuKsTabLoads];
+  if constexpr (TAB) {
+#pragma unroll
+    for (int u = 0; u < kGuKsTabLoads; ++u) {
+      const int j = threadIdx.x + u * 64 * KS;
+      const uint32_t off = j < tab_n16 ? (uint32_t)r0 * (uint32_t)nb + 16u * j : kOOB;
+      tg[u] = __builtin_amdgcn_raw_buffer_load_b128(gsc.tab, off, 0, 2 /* nt */);
+      tu[u] = __builtin_amdgcn_raw_buffer_load_b128(usc.tab, off, 0, 2 /* nt */);
+    }
+  }
+  auto load = [&](RowBlocks<1>& r, rsrc_t cod, const ScaleSrc& sc, int st) {
+    const int n = r0 + 2 * st + rsub;
+    const bool ok = st < steps && n < I;
+    r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(cod, ok ? (uint32_t)n * (uint32_t)(H / 2) + 16u * b : kOOB, 0,
+                                                   2 /* nt */);
+    if constexpr (TAB) {
+      r.s[0] = 0u;  // read from LDS when the step is computed
+    } else {
+      // rows r0 + 2 st, + 1 (r0 and 2 st even) lie in one dword of bases: a scalar load
+      const int rr = (st < steps && r0 + 2 * st < I) ? r0 + 2 * st : 0;
+      r.base = (bases4(sc.bptr, rr >> 2) >> (((rr & 3) + rsub) * 8)) & 0xFFu;
+      r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(sc.tab, ok ? (uint32_t)n * (uint32_t)(nb / 2) + (uint32_t)(b >> 1)
+                                                              : kOOB,
+                                                   0, 2 /* nt */);
+      r.valid = ok ? 1u : 0u;
+    }
+  };
+  RowBlocks<1> gr[D], ur[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    load(gr[d], gcod, gsc, d);
+    load(ur[d], ucod, usc, d);
+  }
+  if constexpr (TAB) {
+#pragma unroll
+    for (int u = 0; u < kGuKsTabLoads; ++u) {
+      const int j = threadIdx.x + u * 64 * KS;
+      if (j < tab_n16) {
+        reinterpret_cast<u32x4*>(tab)[j] = tg[u];
+        reinterpret_cast<u32x4*>(tab + rows_per_wg * nb)[j] = tu[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int s0 = 0; s0 < steps; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int st = s0 + d;
+      load(gr[(d + D - 1) % D], gcod, gsc, st + D - 1);
+      load(ur[(d + D - 1) % D], ucod, usc, st + D - 1);
+      const int rr = 2 * st + rsub;  // a row past I reads table bytes no result uses
+      if constexpr (TAB) {
+        gr[d].s[0] = tab[rr * nb + b];
+        ur[d].s[0] = tab[(rows_per_wg + rr) * nb + b];
+      }
+      const float ag = group_reduce<32>(row_dot<XF32, 1, S4, true>(gr[d], xr, sh));
+      const float au = group_reduce<32>(row_dot<XF32, 1, S4, true>(ur[d], xr, sh));
+      if (c == 31) {
+        partial[(2 * rr) * KS + ks] = ag;
+        partial[(2 * rr + 1) * KS + ks] = au;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows; i += 64 * KS) {
+    float g = partial[(2 * i) * KS], u = partial[(2 * i + 1) * KS];
+#pragma unroll
+    for (int k2 = 1; k2 < KS; ++k2) {
+      g += partial[(2 * i) * KS + k2];
+      u += partial[(2 * i + 1) * KS + k2];
+    }
+    hbuf[(size_t)p * I + r0 + i] = silu_mul(g, u);
+  }
+}
+
 // ---------------------------------------------------------------- down
 // Workgroup (pair p, part): rows of Wd [H][I] of expert pair_expert[p]; LPR
 // lanes per row, RPS = 64/LPR rows per step, `steps` steps per wave, row
@@ -656,10 +823,44 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
   *parts = (rows + 4 * pw - 1) / (4 * pw);
 }
 
+// The K-split gate/up for H = 1024*KS: about as many workgroups as the GPU
+// holds at once share all pairs' rows equally (rows per workgroup a multiple
+// of two ring passes, at most kGuKsMaxRows so the scale table fits).
+template <int KS, bool XF32, int SEL, bool S4>
+static hipError_t gateup_ks_launch(int P, hipStream_t s, const void* x, int32_t* route, const float* logits,
+                                   float* wsel, const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
+                                   int k, float* hbuf) {
+  constexpr int D = kGuKsRing;
+  auto lds_for = [&](int rows) { return (size_t)rows * 2 * KS * 4 + (S4 ? 0 : (size_t)2 * rows * (H / 32)); };
+  const int target = resident_wgs(k_gateup_ks<KS, D, XF32, SEL, S4>, lds_for(kGuKsMaxRows), 64 * KS);
+  const int want = (target + P - 1) / P;
+  int rows = (I + want - 1) / want;
+  rows = (rows + 2 * D - 1) / (2 * D) * (2 * D);
+  if (rows > kGuKsMaxRows) rows = kGuKsMaxRows;
+  const int parts = (I + rows - 1) / rows;
+  k_gateup_ks<KS, D, XF32, SEL, S4><<<dim3((unsigned)(P * parts)), 64 * KS, lds_for(rows), s>>>(
+      x, route, logits, wsel, codes, scales, H, I, E, k, parts, rows, hbuf);
+  return hipGetLastError();
+}
+
 template <bool XF32, int SEL, bool S4>
 static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
                                   const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
                                   int H, int I, int E, int k, float* hbuf) {
+  static_assert(kGuKsMaxRows % (2 * kGuKsRing) == 0, "whole ring passes");
+  if (SEL <= 16 && H % 1024 == 0) {  // K split across H/1024 waves
+#define MOE_GUK(KS) \
+  return gateup_ks_launch<KS, XF32, (SEL <= 16 ? SEL : 16), S4>(P, s, x, route, logits, wsel, codes, scales, H, I, E, k, hbuf);
+    switch (H / 1024) {
+      case 1: MOE_GUK(1)
+      case 2: MOE_GUK(2)
+      case 4: MOE_GUK(4)
+      case 7: MOE_GUK(7)
+      case 8: MOE_GUK(8)
+      default: break;
+    }
+#undef MOE_GUK
+  }
 #define MOE_GU(N)                                                                                    \
   {                                                                                                    \
     int parts, rpw;                                                                                    \

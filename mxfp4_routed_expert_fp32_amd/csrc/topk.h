@@ -3,6 +3,8 @@
 // kernel, which selects its own experts.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -10,17 +12,17 @@ namespace moe {
 // Rank key of a logit: larger key = earlier in route order.  Higher value
 // first; -0 and +0 are equal; NaN is below every number (-inf included); equal
 // values go to the lower expert id.  Key 0 is never a valid key.
-__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
+// The key's upper word: the logit's order as an unsigned integer.
+__device__ __forceinline__ uint32_t rank_ord(float v) {
   uint32_t u = __float_as_uint(v);
-  uint32_t ord;
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
-    ord = 0;                                  // NaN
-  } else {
-    if ((u << 1) == 0) u = 0;                 // -0 -> +0
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)ord << 32) | (uint32_t)(~e);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0;  // NaN
+  if ((u << 1) == 0) u = 0;                      // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+__device__ __forceinline__ uint64_t make_key(uint32_t ord, uint32_t e) { return ((uint64_t)ord << 32) | (uint32_t)(~e); }
+
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) { return make_key(rank_ord(v), e); }
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
@@ -114,14 +116,19 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) lv[v] = l[e0 + v < E ? e0 + v : 0];
   }
-  uint64_t key[MAXV];
+  // upper key words only (the lower word is ~expert, implicit in v); bit v
+  // of `alive`: expert e0 + v exists (in the fallback: and is not taken yet)
+  using Mask = typename std::conditional<(MAXV > 32), uint64_t, uint32_t>::type;
+  constexpr Mask kOne = 1;
+  uint32_t ord[MAXV];
+  Mask alive = 0;
   uint32_t mo = 0;  // upper word of this lane's largest key
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
-    const int e = e0 + v;
-    key[v] = (e < E) ? rank_key(lv[v], (uint32_t)e) : 0ull;
-    const uint32_t o = (uint32_t)(key[v] >> 32);
-    mo = o > mo ? o : mo;
+    const bool here = e0 + v < E;
+    ord[v] = here ? rank_ord(lv[v]) : 0u;
+    alive |= here ? (kOne << v) : Mask(0);
+    mo = ord[v] > mo ? ord[v] : mo;
   }
   // T: the largest multiple of 2^16 with at least k lane maxima at or above
   // it, built bit by bit from the top
@@ -135,7 +142,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   // prefix of the per-lane counts, one ballot per count bit
   uint32_t cnt = 0;
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) cnt += (key[v] != 0ull && (uint32_t)(key[v] >> 32) >= T) ? 1u : 0u;
+  for (int v = 0; v < MAXV; ++v) cnt += (((alive >> v) & kOne) && ord[v] >= T) ? 1u : 0u;
   uint32_t excl = 0, total = 0;
 #pragma unroll
   for (int b = 0; (1 << b) <= MAXV; ++b) {
@@ -150,8 +157,8 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     uint32_t ptr = excl;
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) {
-      const bool c = key[v] != 0ull && (uint32_t)(key[v] >> 32) >= T;
-      cand[c ? ptr : kWave + lane] = key[v];  // non-candidates go to the dummy half
+      const bool c = ((alive >> v) & kOne) && ord[v] >= T;
+      cand[c ? ptr : kWave + lane] = make_key(ord[v], (uint32_t)(e0 + v));  // non-candidates: the dummy half
       ptr += c ? 1u : 0u;
     }
     __builtin_amdgcn_wave_barrier();
@@ -163,11 +170,11 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
 #pragma unroll
-      for (int v = 0; v < MAXV; ++v) best = umax64(best, key[v]);
-      const uint64_t win = wave_max_u64(best);
-#pragma unroll
       for (int v = 0; v < MAXV; ++v)
-        if (key[v] == win) key[v] = 0;
+        best = umax64(best, ((alive >> v) & kOne) ? make_key(ord[v], (uint32_t)(e0 + v)) : 0ull);
+      const uint64_t win = wave_max_u64(best);
+      const uint32_t we = ~(uint32_t)win;  // the winner's expert
+      if (we - (uint32_t)e0 < (uint32_t)MAXV) alive &= ~(kOne << (we - (uint32_t)e0));
       if (lane == j) { my_rank = j; my_key = win; }
     }
   }
