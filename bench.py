@@ -69,7 +69,7 @@ def log(msg):
 # rocprofv3 counters is reported only while these files still hash to the
 # value recorded next to the counters.
 KERNEL_SOURCES = {
-    "k_gateup_gemv": ["expert_gemv.hip", "common.h", "topk.h"],
+    "k_gateup_ks": ["expert_gemv.hip", "common.h", "topk.h"],
     "k_down_ks": ["expert_gemv.hip", "common.h"],
     "k_gateup_mfma": ["expert_mfma.hip", "common.h"],
     "k_down_mfma": ["expert_mfma.hip", "common.h"],
@@ -328,18 +328,18 @@ def bench_decode(a, ctx, steps, warmup):
     assert gu_w + dn_w == expert_bytes
     ach = expert_bytes / ((gu_us + dn_us) * 1e-6) / 1e9
     roofline = {
-        "bound": "hbm", "kernel": "expert phase as the forward runs it: k_gateup_gemv (selecting) + k_down_ks",
+        "bound": "hbm", "kernel": "expert phase as the forward runs it: k_gateup_ks (selecting) + k_down_ks",
         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-        "traffic": sum_traffic([("k_gateup_gemv", "decode"), ("k_down_ks", "decode")]),
+        "traffic": sum_traffic([("k_gateup_ks", "decode"), ("k_down_ks", "decode")]),
         "bytes_per_launch": expert_bytes, "avg_launch_us": gu_us + dn_us,
         "kernels": {
-            "k_gateup_gemv_select": {"avg_launch_us": gu_us, "weight_bytes": gu_w,
+            "k_gateup_ks_select": {"avg_launch_us": gu_us, "weight_bytes": gu_w,
                                      "frac": gu_w / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                     "traffic": measured_traffic("k_gateup_gemv", "decode")},
+                                     "traffic": measured_traffic("k_gateup_ks", "decode")},
             "k_down_ks": {"avg_launch_us": dn_us, "weight_bytes": dn_w,
                           "frac": dn_w / (dn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                           "traffic": measured_traffic("k_down_ks", "decode")},
-            "k_gateup_gemv_routes_given": {"avg_launch_us": gv_us,
+            "k_gateup_ks_routes_given": {"avg_launch_us": gv_us,
                                            "frac": gu_w / (gv_us * 1e-6) / 1e9 / HBM_PEAK_GBS}},
     }
     # the same layer with the lossless scale4 side-car (2.88% fewer expert
@@ -370,7 +370,7 @@ def bench_decode(a, ctx, steps, warmup):
         eb4 = k * (sum(moe.packed_bytes(desc4)) // E)
         s4 = {"tokens_per_s": 1.0 / (ms4 * 1e-3), "ms_per_step": ms4, "ms_per_step_spread": spread4,
               "expert_bytes_per_token": eb4, "bytes_saved_frac": 1.0 - eb4 / expert_bytes,
-              "expert_phase_us": {"k_gateup_gemv_select": gu4, "k_down_ks": dn4},
+              "expert_phase_us": {"k_gateup_ks_select": gu4, "k_down_ks": dn4},
               "expert_phase_GBps": eb4 / ((gu4 + dn4) * 1e-6) / 1e9,
               "expert_phase_frac": eb4 / ((gu4 + dn4) * 1e-6) / 1e9 / HBM_PEAK_GBS,
               "expert_phase_speedup": (gu_us + dn_us) / (gu4 + dn4), "bit_identical_to_8bit": True}
