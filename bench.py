@@ -390,6 +390,36 @@ def bench_decode(a, ctx, steps, warmup):
                        parity_obj([0, 1], *gate))
 
 
+# --------------------------------------------------------------------------- matrix-core ceiling
+
+def mfma_ceiling(reps=3, n_wg=1024, iters=2000):
+    """The rate the matrix cores sustain on random operands with no memory
+    traffic (moe_mfma_rate), per MFMA kind: TFLOP/s, best of reps launches of
+    n_wg workgroups x 8 waves x iters x 8 MFMAs.  The ceiling under the clock
+    the chip holds at that load, beside the nominal dense peaks."""
+    import numpy as np
+    import torch
+    import mxfp4_routed_expert_fp32_amd as moe
+
+    ops = torch.from_numpy(np.random.default_rng(2024).integers(0, 256, 65536, dtype=np.uint8)).to("cuda")
+    sink = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for kind, (name, flops_per_mfma) in moe.MFMA_RATE_KINDS.items():
+        moe.moe_mfma_rate(kind, ops, n_wg, 20, sink)
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record()
+            moe.moe_mfma_rate(kind, ops, n_wg, iters, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) * 1e-3
+            best = sec if best is None else min(best, sec)
+        out[name] = n_wg * 8 * iters * 8 * flops_per_mfma / best / 1e12
+    return out
+
+
 # --------------------------------------------------------------------------- batched decode / prefill
 
 def bench_batch(a, ctx, name, steps, warmup):
@@ -500,6 +530,11 @@ def bench_batch(a, ctx, name, steps, warmup):
                     "frac_hbm_weights": wbytes / (exp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, **roof_common}
         for kn, us, fl in (("k_gateup_mfma", gu_us, 4.0 * H * I * P_), ("k_down_mfma", dn_us, 2.0 * H * I * P_)):
             roofline["kernels"][kn]["frac"] = fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
+        ceil = mfma_ceiling()
+        roofline["mfma_ceiling_measured_TFLOPs"] = ceil
+        roofline["frac_of_measured_bf16_ceiling"] = ach / ceil["bf16"]
+        log("%s: matrix cores on random operands: %s TFLOP/s" % (
+            name, ", ".join("%s %.0f" % kv for kv in ceil.items())))
     else:
         ach = wbytes / (exp_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": "expert phase as the forward runs it: k_gateup_mfma + k_down_mfma",

@@ -563,6 +563,24 @@ moe_status moe_int8_gemv(const int8_t* q, const uint16_t* scales_f16, int32_t ro
                          moe_dtype x_dtype, int32_t n_tokens, float* y, int32_t rows_per_workgroup, void* stream);
 
 /*
+ * Matrix-core rate on random operands (a measurement aid, not on the pages):
+ * n_workgroups workgroups of 512 threads each run iters rounds of 8
+ * independent MFMAs of one kind, with no memory traffic in the loop, and
+ * write one float per thread to sink.  kind 0: bf16 16x16x32 (16,384 flops
+ * per MFMA); kind 1: fp8 e4m3 x fp4 e2m1, 16x16x128 with unit E8M0 scales
+ * (65,536 flops); kind 2: fp4 x fp4, 16x16x128 (65,536 flops).  Timing the
+ * call gives the rate the chip sustains under that load, the ceiling of the
+ * prefill form's bf16 MFMA and of the MXFP4 alternatives.  operands: 65536
+ * random bytes on the device (16-byte aligned; every bit pattern is allowed,
+ * NaN operands included); sink: n_workgroups * 512 floats on the device.
+ * Errors: MOE_ERR_NULL, MOE_ERR_UNSUPPORTED (kind), MOE_ERR_SHAPE
+ * (n_workgroups outside 1 .. 65536, iters outside 1 .. 10^6), MOE_ERR_ALIGN,
+ * MOE_ERR_DEVICE.
+ */
+moe_status moe_mfma_rate(int32_t kind, const void* operands, int32_t n_workgroups, int32_t iters, float* sink,
+                         void* stream);
+
+/*
  * Next-layer route hint ("Deltafin's custom compiled runtime", section "Exact
  * next-layer expert prefetch"; "How the native runtime works", section
  * "Automatic PILOT prefetch and CUDA expert residency"): the k experts the

@@ -37,7 +37,7 @@ EXPORTS = [
     "moe_stack_graph_destroy", "moe_cache_create", "moe_cache_destroy", "moe_cache_slots", "moe_cache_get_stats",
     "moe_cache_plan", "moe_cache_finish", "moe_cache_cancel", "moe_cache_workspace_bytes", "moe_cache_layer_forward",
     "moe_route_hint_workspace_bytes", "moe_route_hint", "moe_trace_open", "moe_trace_record", "moe_trace_close",
-    "moe_trace_count", "moe_int8_dequant", "moe_int8_gemv", "moe_mxfp4_scale4_encode",
+    "moe_trace_count", "moe_int8_dequant", "moe_int8_gemv", "moe_mxfp4_scale4_encode", "moe_mfma_rate",
 ]
 MOE_TRACE_BUFFERED, MOE_TRACE_SYNC = 0, 1
 MOE_CACHE_PREFETCH = 1
@@ -140,6 +140,7 @@ def lib():
                 "moe_int8_dequant": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
                 "moe_mxfp4_scale4_encode": ([D, vp, i64, i64, vp, vp, vp], ctypes.c_int),
                 "moe_int8_gemv": ([vp, vp, i32, i32, vp, i32, i32, vp, i32, vp], ctypes.c_int),
+                "moe_mfma_rate": ([i32, vp, i32, i32, vp, vp], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -520,6 +521,16 @@ def moe_int8_gemv(q, scales_f16, x, y, rows_per_workgroup=0, stream=None):
     N, K = q.shape
     _check("moe_int8_gemv", lib().moe_int8_gemv(_ptr(q), _ptr(scales_f16), N, K, _ptr(x), _xdtype(x), x.shape[0],
                                                 _ptr(y), rows_per_workgroup, _stream(stream)))
+
+
+MFMA_RATE_KINDS = {0: ("bf16", 16384), 1: ("fp8_x_fp4", 65536), 2: ("fp4_x_fp4", 65536)}  # name, flops per MFMA
+
+
+def moe_mfma_rate(kind, operands, n_workgroups, iters, sink, stream=None):
+    """Enqueue n_workgroups x 512 threads x iters x 8 MFMAs of one kind on
+    random operands (operands: 65536 bytes; sink: n_workgroups * 512 floats)."""
+    _check("moe_mfma_rate", lib().moe_mfma_rate(kind, _ptr(operands), n_workgroups, iters, _ptr(sink),
+                                                _stream(stream)))
 
 
 def moe_mxfp4_scale4_encode(desc4, scales8, expert_begin, expert_count, scale4, escapes, stream=None):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mxfp4.so")
-SOURCES = ["abi.hip", "route.hip", "expert_gemv.hip", "expert_mfma.hip", "misc.hip", "residency.hip", "route_trace.hip", "int8_gemv.hip"]
+SOURCES = ["abi.hip", "route.hip", "expert_gemv.hip", "expert_mfma.hip", "misc.hip", "residency.hip", "route_trace.hip", "int8_gemv.hip", "mfma_rate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -657,6 +657,17 @@ moe_status moe_int8_dequant(const int8_t* q, const uint16_t* scales_f16, int32_t
   return dev(moe::launch_int8_dequant(q, scales_f16, rows, cols, out, as_stream(stream)));
 }
 
+// ---------------------------------------------------------------- matrix-core rate
+
+moe_status moe_mfma_rate(int32_t kind, const void* operands, int32_t n_workgroups, int32_t iters, float* sink,
+                         void* stream) {
+  if (kind < 0 || kind > 2) return MOE_ERR_UNSUPPORTED;
+  if (!operands || !sink) return MOE_ERR_NULL;
+  if (n_workgroups < 1 || n_workgroups > 65536 || iters < 1 || iters > 1000000) return MOE_ERR_SHAPE;
+  if (!aligned16(operands) || !aligned16(sink)) return MOE_ERR_ALIGN;
+  return dev(moe::launch_mfma_rate(kind, operands, n_workgroups, iters, sink, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- next-layer route hint
 
 static moe_status hint_layout(const moe_layer_desc* d, int32_t T, int32_t k, size_t* nout_off, size_t* w_off,

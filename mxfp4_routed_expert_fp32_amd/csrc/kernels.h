@@ -87,6 +87,12 @@ hipError_t launch_int8_gemv(const int8_t* q, const uint16_t* s, int N, int K, co
                             float* y, int rows_per_wg, hipStream_t st);
 hipError_t launch_int8_dequant(const int8_t* q, const uint16_t* s, int N, int K, float* out, hipStream_t st);
 
+// Matrix-core rate on random operands (kind 0 bf16, 1 fp8 x fp4, 2 fp4 x fp4):
+// n_workgroups of 512 threads, iters rounds of 8 MFMAs per thread; operands
+// 65536 random bytes, sink n_workgroups * 512 floats.
+hipError_t launch_mfma_rate(int kind, const void* operands, int n_workgroups, int iters, float* sink,
+                            hipStream_t s);
+
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // via_bf16: decode through the bf16 conversion of the bf16 GEMV and the MFMA
 // kernels (widened to fp32), else through the fp32 conversion.  With s4_base

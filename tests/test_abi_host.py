@@ -208,3 +208,19 @@ def test_grouped_stage_entry_points_reject_before_launch():
     assert L.moe_mxfp4_grouped_down(ctypes.byref(odd), *dn) == -7
     assert L.moe_mxfp4_grouped_down(ctypes.byref(d), 16, 0, *dn[2:]) == -2
     assert L.moe_mxfp4_grouped_down(ctypes.byref(d), 16, 65536, 16, 16, 16, 1408, 16, 16, 24, None) == -4
+
+
+def test_mfma_rate_rejects_before_launch():
+    """The matrix-core rate entry checks kind, pointers, sizes and alignment on
+    the host (fake device addresses: nothing is launched)."""
+    f = moe.lib().moe_mfma_rate
+    assert f(3, 16, 1, 1, 16, None) == -7      # MOE_ERR_UNSUPPORTED
+    assert f(-1, 16, 1, 1, 16, None) == -7
+    assert f(0, None, 1, 1, 16, None) == -1    # MOE_ERR_NULL
+    assert f(1, 16, 1, 1, None, None) == -1
+    assert f(2, 16, 0, 1, 16, None) == -2      # MOE_ERR_SHAPE
+    assert f(2, 16, 65537, 1, 16, None) == -2
+    assert f(0, 16, 1, 0, 16, None) == -2
+    assert f(0, 16, 1, 1000001, 16, None) == -2
+    assert f(0, 8, 1, 1, 16, None) == -4       # MOE_ERR_ALIGN
+    assert f(0, 16, 1, 1, 24, None) == -4

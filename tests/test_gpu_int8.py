@@ -57,3 +57,4 @@ def test_int8_gemv_matches_oracle(N, K, T, xd, rpw):
     A = np.abs(x).astype(np.float64) @ np.abs(W).T
     P.assert_out_close(got, ref)
     P.assert_elementwise(got, ref, A)
+
