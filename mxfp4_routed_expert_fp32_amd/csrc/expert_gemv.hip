@@ -12,17 +12,25 @@
 //
 // Weight layout (row-major, per expert gate | up | down): a row of a
 // [rows][K] matrix is K/2 code bytes, plus K/32 scale bytes in the scale
-// buffer.  Lane l of a wave owns the 32-element blocks b = c + LPR*m of its row
-// (c = l % LPR, m < NBL), so each 16-byte load instruction of a wave reads LPR
-// consecutive blocks of each of 64/LPR rows, and the lane's slice of the
-// activation vector stays in registers for every row the wave streams.
+// buffer.
 //
-// Work split: a workgroup (4 waves) owns one (token, rank) pair and a share of
-// its rows; the grid is sized to the number of workgroups the GPU holds at
-// once (occupancy x CUs), so every workgroup runs once and there is no tail.
-// Rows are interleaved across the pair's waves, so at any moment the waves of
-// a pair stream neighbouring rows.  Weight loads run ahead of the compute
-// (two rows for gate/up, three row groups for down).
+// Two forms of each GEMV:
+//  - K split across waves (k_gateup_ks for H = 1024 KS, k_down_ks for
+//    I = 512 KS, the model's widths): each wave of a workgroup takes a fixed
+//    range of 32-element blocks of every row of the workgroup's row range
+//    (one block per lane, 32 or 16 lanes per row), so a lane holds one block
+//    of activations in registers; the waves' partial sums of a row are added
+//    in LDS in wave order, and the workgroup's 8-bit scale rows are copied
+//    into LDS once.
+//  - Whole rows per wave (k_gateup_gemv, k_down_gemv, other widths): lane l
+//    of a wave owns the blocks b = c + LPR*m of its row (c = l % LPR,
+//    m < NBL), so each 16-byte load instruction of a wave reads LPR
+//    consecutive blocks of each of 64/LPR rows, and the lane's slice of the
+//    activation vector stays in registers for every row the wave streams.
+// In both, a workgroup owns one (token, rank) pair and a share of its rows;
+// the grid is sized to the number of workgroups the GPU holds at once
+// (occupancy x CUs), so every workgroup runs once, and weight loads run
+// several steps ahead of the compute.
 #include <mutex>
 
 #include "common.h"
