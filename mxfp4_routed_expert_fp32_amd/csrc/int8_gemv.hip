@@ -59,50 +59,73 @@ __global__ __launch_bounds__(1024) void k_int8_gemv(const int8_t* __restrict__ q
     return __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? (uint32_t)r * (uint32_t)K + (uint32_t)k0 : kOOB8, 0,
                                                  2 /* nt */);
   };
-  u32x4 ring[D];
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d) ring[d] = load(d);
+  // the lane's 16 activations per token first, in 16-byte loads (K is a
+  // multiple of 16, so a lane's columns are all in range or all past K):
+  // loads complete in issue order, so the first row's wait for x then leaves
+  // the ring's loads in flight (issued after the ring, that wait would cover
+  // them too, in every pass of the loop)
   float xr[TT][16];
+  const bool xin = k0 < K;
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
+    if constexpr (XF32) {
+      const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * K + (xin ? k0 : 0));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = k0 + i;
-      float v = 0.0f;
-      if (k < K) {
-        if constexpr (XF32)
-          v = static_cast<const float*>(x)[(size_t)t * K + k];
-        else
-          v = bf16_bits_to_f32(static_cast<const uint16_t*>(x)[(size_t)t * K + k]);
+      for (int v = 0; v < 4; ++v) {
+        const float4 f = xp[v];
+        xr[t][4 * v] = xin ? f.x : 0.0f;
+        xr[t][4 * v + 1] = xin ? f.y : 0.0f;
+        xr[t][4 * v + 2] = xin ? f.z : 0.0f;
+        xr[t][4 * v + 3] = xin ? f.w : 0.0f;
       }
-      xr[t][i] = v;
+    } else {
+      const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)t * K + (xin ? k0 : 0));
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const uint4 u = xp[v];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xr[t][8 * v + 2 * j] = xin ? bf16_bits_to_f32(w[j] & 0xFFFFu) : 0.0f;
+          xr[t][8 * v + 2 * j + 1] = xin ? bf16_bits_to_f32(w[j] >> 16) : 0.0f;
+        }
+      }
     }
   }
-  for (int r = 0; r < nrows; r += D) {
+  // the prologue's loads in ring order (the scheduler may not reorder them:
+  // the loop's wait counts assume the oldest load holds the first row)
+  u32x4 ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    ring[d] = load(d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // every row of the workgroup's range in whole ring passes (rows_per_wg is
+  // a multiple of D, so the unrolled ring has no exit inside); rows past N
+  // read zeros and their sums are never used
+  for (int r = 0; r < rows_per_wg; r += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int row = r + d;
       ring[(d + D - 1) % D] = load(row + D - 1);
-      if (row < nrows) {
-        const u32x4 v = ring[d];
-        float acc[TT];
+      const u32x4 v = ring[d];
+      float acc[TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+      for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t w = v[wd];
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t w = v[wd];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float qv = sext_byte(w, b);
+        for (int b = 0; b < 4; ++b) {
+          const float qv = sext_byte(w, b);
 #pragma unroll
-            for (int t = 0; t < TT; ++t) acc[t] = fmaf(qv, xr[t][4 * wd + b], acc[t]);
-          }
+          for (int t = 0; t < TT; ++t) acc[t] = fmaf(qv, xr[t][4 * wd + b], acc[t]);
         }
+      }
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          const float sum = wave_sum(acc[t]);
-          if (lane == 0) part[((size_t)t * rows_per_wg + row) * nw + wv] = sum;
-        }
+      for (int t = 0; t < TT; ++t) {
+        const float sum = wave_sum(acc[t]);
+        if (lane == 0) part[((size_t)t * rows_per_wg + row) * nw + wv] = sum;
       }
     }
   }
@@ -116,24 +139,37 @@ __global__ __launch_bounds__(1024) void k_int8_gemv(const int8_t* __restrict__ q
   }
 }
 
-// out[n][k] = q[n][k] * s[n]: 16 int8 in, 16 fp32 out per thread step.
+// out[n][k] = q[n][k] * s[n].  A wave takes 1 KB of q per step: lane l
+// loads dwords l, l + 64, l + 128 and l + 192 of it (four independent
+// 256-byte loads per wave, in flight together) and writes each as 4 fp32, so
+// every store instruction of the wave writes 1 KB of out contiguously.
 __global__ __launch_bounds__(256) void k_int8_dequant(const int8_t* __restrict__ q, const uint16_t* __restrict__ s,
                                                       int N, int K, float* __restrict__ out) {
-  const size_t n16 = (size_t)N * K / 16;
-  const int per_row = K / 16;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
-    const size_t n = i / per_row;
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q) + i);
-    const float sc = f16_bits_to_f32(s[n]);
-    f32x4* o = reinterpret_cast<f32x4*>(out) + 4 * i;
+  const size_t ndw = (size_t)N * K / 4;  // dwords of q (K is a multiple of 16)
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(q);
+  f32x4* o4 = reinterpret_cast<f32x4*>(out);
+  for (size_t c0 = ((size_t)blockIdx.x * 4 + wave) * 256; c0 < ndw; c0 += (size_t)gridDim.x * 4 * 256) {
+    uint32_t w[4];
+    float sc[4];
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      f32x4 r;
-      r.x = sext_byte(v[wd], 0) * sc;
-      r.y = sext_byte(v[wd], 1) * sc;
-      r.z = sext_byte(v[wd], 2) * sc;
-      r.w = sext_byte(v[wd], 3) * sc;
-      o[wd] = r;
+    for (int j = 0; j < 4; ++j) {
+      const size_t i = c0 + 64 * j + lane;
+      const bool ok = i < ndw;
+      w[j] = __builtin_nontemporal_load(q32 + (ok ? i : 0));
+      sc[j] = f16_bits_to_f32(s[ok ? (i * 4) / K : 0]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t i = c0 + 64 * j + lane;
+      if (i < ndw) {
+        f32x4 r;
+        r.x = sext_byte(w[j], 0) * sc[j];
+        r.y = sext_byte(w[j], 1) * sc[j];
+        r.z = sext_byte(w[j], 2) * sc[j];
+        r.w = sext_byte(w[j], 3) * sc[j];
+        o4[i] = r;
+      }
     }
   }
 }
@@ -169,8 +205,8 @@ hipError_t launch_int8_gemv(const int8_t* q, const uint16_t* s, int N, int K, co
 }
 
 hipError_t launch_int8_dequant(const int8_t* q, const uint16_t* s, int N, int K, float* out, hipStream_t st) {
-  const size_t n16 = (size_t)N * K / 16;
-  size_t blocks = (n16 + 255) / 256;
+  const size_t nkb = ((size_t)N * K + 1023) / 1024;  // 1 KB steps of one wave
+  size_t blocks = (nkb + 3) / 4;
   if (blocks > 8192) blocks = 8192;
   if (blocks == 0) return hipSuccess;
   k_int8_dequant<<<dim3((unsigned)blocks), 256, 0, st>>>(q, s, N, K, out);
