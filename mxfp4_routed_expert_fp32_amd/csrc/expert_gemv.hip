@@ -338,9 +338,10 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
       const int t = p / k;
       int sel;
       float wv;
-      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv);
+      const bool writer = part == 0 && p % k == 0;  // the token's workgroup that publishes the selection
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv, writer);
       if (lane == p % k) chosen = sel;
-      if (part == 0 && p % k == 0 && lane < k) {
+      if (writer && lane < k) {
         route[(size_t)t * k + lane] = sel;
         wsel[(size_t)t * k + lane] = wv;
       }
@@ -465,9 +466,10 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     if (ks == 0) {
       int sel;
       float wv;
-      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv);
+      const bool writer = part == 0 && p % k == 0;  // the token's workgroup that publishes the selection
+      topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv, writer);
       if (lane == p % k) chosen = sel;
-      if (part == 0 && p % k == 0 && lane < k) {
+      if (writer && lane < k) {
         route[(size_t)t * k + lane] = sel;
         wsel[(size_t)t * k + lane] = wv;
       }

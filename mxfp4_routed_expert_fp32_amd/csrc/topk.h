@@ -97,10 +97,12 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 // Both give the unique order defined by rank_key.  cand is this wave's LDS
 // scratch (2 * 64 keys).
 // On return lane j < k holds the expert of rank j in *sel and its softmax
-// weight in *wsel (lanes >= k: expert 0, weight 0).
+// weight in *wsel (lanes >= k: expert 0, weight 0).  weights = false (a
+// wave-uniform flag) skips the softmax and leaves every weight 0, for callers
+// that need the experts only.
 template <int MAXV>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, uint64_t* cand,
-                                          int* sel_out, float* w_out) {
+                                          int* sel_out, float* w_out, bool weights = true) {
   static_assert(MAXV % 4 == 0, "whole 16-byte loads");
   const int lane = threadIdx.x % kWave;
   const int e0 = lane * MAXV;
@@ -184,13 +186,15 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const uint64_t kj = (lane < k) ? cand[lane] : 0ull;
   const int sel = (lane < k) ? (int)~(uint32_t)kj : 0;
+  *sel_out = sel;
+  *w_out = 0.0f;
+  if (!weights) return;
   // softmax over the selected logits, in rank order, each logit decoded from
   // its key; lane 0 holds the largest
   const float lj = (lane < k) ? key_logit(kj) : 0.0f;
   const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
   const float ex = (lane < k) ? expf(lj - m) : 0.0f;
   const float s = wave_sum(ex);
-  *sel_out = sel;
   *w_out = lane < k ? ex / s : 0.0f;
 }
 
