@@ -9,20 +9,21 @@
 
 namespace moe {
 
-// Rank key of a logit: larger key = earlier in route order.  Higher value
-// first; -0 and +0 are equal; NaN is below every number (-inf included); equal
-// values go to the lower expert id.  Key 0 is never a valid key.
-// The key's upper word: the logit's order as an unsigned integer.
+// Rank key of expert e's logit v: larger key = earlier in route order.
+// Higher value first; -0 and +0 are equal; NaN is below every number (-inf
+// included); equal values go to the lower expert id.  The upper word is the
+// logit's order as an unsigned integer (rank_ord: x + 0 is x except that -0
+// becomes +0, under IEEE round to nearest with denormals kept; then the sign
+// bit flips the order of the magnitude bits; NaN gives 0), the lower word is
+// ~e.  Key 0 is never a valid key.
 __device__ __forceinline__ uint32_t rank_ord(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0;  // NaN
-  if ((u << 1) == 0) u = 0;                      // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const float y = v + 0.0f;
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return y == y ? o : 0u;
 }
 
 __device__ __forceinline__ uint64_t make_key(uint32_t ord, uint32_t e) { return ((uint64_t)ord << 32) | (uint32_t)(~e); }
-
-__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) { return make_key(rank_ord(v), e); }
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
@@ -47,36 +48,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Number of lanes whose 64-bit key is larger than this lane's (keys unique),
-// through a 64-entry LDS buffer of the wave: every lane writes its key, then
-// reads entries back two at a time (the same address in every lane, a
-// broadcast).  Keys of lanes n and above must be 0 (they never count), so the
-// reads cover a fixed 32 or 64 entries, unrolled, and all of them are in
-// flight at once.  The buffer is free again when the function returns.
-__device__ __forceinline__ int rank_in_wave_lds(uint64_t v, uint64_t* buf, int n = kWave) {
-  const int lane = threadIdx.x % kWave;
-  buf[lane] = v;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  int r = 0;
-#pragma unroll
-  for (int j = 0; j < kWave / 2; j += 2) {
-    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
-    r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
-  }
-  if (n > kWave / 2) {
-#pragma unroll
-    for (int j = kWave / 2; j < kWave; j += 2) {
-      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
-      r += (kk.x > v ? 1 : 0) + (kk.y > v ? 1 : 0);
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  return r;
-}
-
-// The logit a rank key was made from (rank_key inverted on its upper word):
+// The logit a rank key was made from (rank_ord inverted on its upper word):
 // exact, except that -0 comes back as +0 and every NaN as one NaN pattern.
 __device__ __forceinline__ float key_logit(uint64_t key) {
   const uint32_t ord = (uint32_t)(key >> 32);
@@ -91,10 +63,12 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 // the top k keys all are; these candidates (usually a few more than k) are
 // gathered into one key per lane, each lane writing its own at an offset from
 // a ballot prefix of the per-lane counts (the others into a dummy half of the
-// buffer, so the writes need no branches), and each one's rank among them is
-// its place in the route.  When more than 64 keys qualify (heavy ties or
-// skew) the wave falls back to k rounds of "take the largest remaining key".
-// Both give the unique order defined by rank_key.  cand is this wave's LDS
+// buffer, so the writes need no branches; the first half is zeroed before,
+// so it holds 0 past the candidates), and each one's rank among them, read in
+// place, is its place in the route.  When more than 64 keys qualify (heavy
+// ties or skew), or fewer than k lanes hold a number (T = 0), the wave falls
+// back to k rounds of "take the largest remaining key".
+// Both give the unique order of the rank keys.  cand is this wave's LDS
 // scratch (2 * 64 keys).
 // On return lane j < k holds the expert of rank j in *sel and its softmax
 // weight in *wsel (lanes >= k: expert 0, weight 0).  weights = false (a
@@ -122,16 +96,18 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   // of `alive`: expert e0 + v exists (in the fallback: and is not taken yet)
   using Mask = typename std::conditional<(MAXV > 32), uint64_t, uint32_t>::type;
   constexpr Mask kOne = 1;
+  constexpr Mask kAll = MAXV >= 64 ? ~Mask(0) : (kOne << MAXV) - 1;
+  const int nh = E - e0;  // experts this lane holds (may be <= 0 or >= MAXV)
+  const Mask alive = nh >= MAXV ? kAll : (nh <= 0 ? Mask(0) : (kOne << nh) - 1);
   uint32_t ord[MAXV];
-  Mask alive = 0;
   uint32_t mo = 0;  // upper word of this lane's largest key
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
-    const bool here = e0 + v < E;
-    ord[v] = here ? rank_ord(lv[v]) : 0u;
-    alive |= here ? (kOne << v) : Mask(0);
-    mo = ord[v] > mo ? ord[v] : mo;
+    const uint32_t o = v < nh ? rank_ord(lv[v]) : 0u;  // absent experts: 0, like NaN
+    ord[v] = o;
+    mo = o > mo ? o : mo;
   }
+  cand[lane] = 0ull;  // candidates overwrite [0, total); the rest stays 0 for the rank reads
   // T: the largest multiple of 2^16 with at least k lane maxima at or above
   // it, built bit by bit from the top
   uint32_t T = 0;
@@ -142,9 +118,11 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   }
   // candidates: present keys whose upper word is >= T; lane offsets from a
   // prefix of the per-lane counts, one ballot per count bit
+  // (with T > 0, the usual case, absent experts and NaN have key word 0 < T;
+  // T = 0, fewer than k lanes hold a number, goes to the fallback below)
   uint32_t cnt = 0;
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) cnt += (((alive >> v) & kOne) && ord[v] >= T) ? 1u : 0u;
+  for (int v = 0; v < MAXV; ++v) cnt += ord[v] >= T ? 1u : 0u;
   uint32_t excl = 0, total = 0;
 #pragma unroll
   for (int b = 0; (1 << b) <= MAXV; ++b) {
@@ -155,28 +133,49 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
 
   int my_rank = kWave;  // rank of this lane's entry (>= k: not selected)
   uint64_t my_key = 0;
-  if (total <= (uint32_t)kWave) {
+  if (T != 0 && total <= (uint32_t)kWave) {
     uint32_t ptr = excl;
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) {
-      const bool c = ((alive >> v) & kOne) && ord[v] >= T;
+      const bool c = ord[v] >= T;
       cand[c ? ptr : kWave + lane] = make_key(ord[v], (uint32_t)(e0 + v));  // non-candidates: the dummy half
       ptr += c ? 1u : 0u;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
-    const int r = rank_in_wave_lds(c, cand, (int)total);  // candidates only (usually about k)
+    // each candidate's rank among the candidates (usually about k), read in
+    // place: entries past `total` are 0 and never count.  16 entries (8
+    // reads) are requested at a time, then compared, so the reads' latency
+    // is paid once per batch.
+    int r = 0;
+    auto batch = [&](int j0) {
+      ulonglong2 kk[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) kk[q] = *reinterpret_cast<const ulonglong2*>(cand + j0 + 2 * q);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r += (kk[q].x > c ? 1 : 0) + (kk[q].y > c ? 1 : 0);
+    };
+    batch(0);
+    if (total > 16) batch(16);
+    if (total > 32) {
+      batch(32);
+      batch(48);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if ((uint32_t)lane < total) { my_rank = r; my_key = c; }
   } else {
+    Mask left = alive;  // present and not taken yet
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
 #pragma unroll
       for (int v = 0; v < MAXV; ++v)
-        best = umax64(best, ((alive >> v) & kOne) ? make_key(ord[v], (uint32_t)(e0 + v)) : 0ull);
+        best = umax64(best, ((left >> v) & kOne) ? make_key(ord[v], (uint32_t)(e0 + v)) : 0ull);
       const uint64_t win = wave_max_u64(best);
       const uint32_t we = ~(uint32_t)win;  // the winner's expert
-      if (we - (uint32_t)e0 < (uint32_t)MAXV) alive &= ~(kOne << (we - (uint32_t)e0));
+      if (we - (uint32_t)e0 < (uint32_t)MAXV) left &= ~(kOne << (we - (uint32_t)e0));
       if (lane == j) { my_rank = j; my_key = win; }
     }
   }
