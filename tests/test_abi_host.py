@@ -135,8 +135,9 @@ def test_forward_rejects_before_launch():
 
 def test_noalloc_forward_rejects_before_launch():
     """The allocation-free forward checks like the forward and refuses a call
-    whose workspace would not fit its 64 MiB static scratch (101 tokens fit at
-    the K3 shape, 102 do not) before touching the device."""
+    whose workspace would not fit its 64 MiB static scratch (at the K3 shape,
+    the largest token count that fits is found from moe_workspace_bytes; one
+    more is refused) before touching the device."""
     L = moe.lib()
     d = D()
 
@@ -145,8 +146,9 @@ def test_noalloc_forward_rejects_before_launch():
                                            None, None)
     assert call(x=None) == -1 and call(wr=None) == -1 and call(dtype=4) == -3
     assert call(T=0) == -2 and call(k=17) == -2 and call(out=24) == -4
-    assert moe.workspace_bytes(d, 101, 16) <= 64 << 20 < moe.workspace_bytes(d, 102, 16)
-    assert call(T=102) == -12 and call(T=4096) == -12
+    fits = max(t for t in range(1, 400) if moe.workspace_bytes(d, t, 16) <= 64 << 20)
+    assert 64 <= fits < 399 and moe.workspace_bytes(d, fits + 1, 16) > 64 << 20
+    assert call(T=fits + 1) == -12 and call(T=4096) == -12
 
 
 def test_other_entry_points_reject_before_launch():

@@ -574,7 +574,7 @@ def test_grouped_stages_equal_forward_and_skip_malformed_blocks():
 
 # ------------------------------------------------------------------ extreme scale bytes through the forward
 
-def hostile_layer():
+def hostile_layer(H=512):
     """A layer whose routed experts carry extreme E8M0 scale bytes.
 
     Expert 1 (every token selects it, through its bias):
@@ -590,9 +590,12 @@ def hostile_layer():
     has scale 255, so every h of that pair, and token 2's whole output, is NaN.
     Activations are N(0,1) * 2^-20 (exact in bf16), so no finite sum comes near
     the fp32 overflow threshold and every non-finite output is fixed by the
-    weights alone, whatever the summation order."""
-    H, I, E, k, T = 512, 256, 8, 2, 5
-    w = synth.Workload("hs", 69, T, H, I, E, k, "bf16", weight_seed=8100)
+    weights alone, whatever the summation order.  H = 1024 takes the decode
+    form whose down projection runs on the scaled MXFP4 matrix cores (its
+    fp32 fallback for tiles with scale bytes >= 253 and for the pair whose h
+    is NaN); H = 512 the plain fp32 GEMVs."""
+    I, E, k, T = 256, 8, 2, 5
+    w = synth.Workload("hs", 69, T, H, I, E, k, "bf16", weight_seed=8100 if H == 512 else 8100 + H)
     c, s, _ = experts_host(w)
     ce, se = w.code_bytes_per_expert, w.scale_bytes_per_expert
     mc, ms = I * H // 2, I * H // 32
@@ -633,8 +636,9 @@ def hostile_layer():
     return w, c, s, ex, x, wr, b
 
 
+@pytest.mark.parametrize("H", [512, 1024])
 @pytest.mark.parametrize("form", ["decode_bf16", "decode_f32", "prefill_mfma"])
-def test_forward_extreme_scale_bytes(form):
+def test_forward_extreme_scale_bytes(form, H):
     """Scale bytes 0, 1, 253, 254 and 255 in selected experts, through each
     kernel form of the forward: NaN and +-inf land where the oracle puts them
     and every finite element meets both readings of the output bar.  The
@@ -643,7 +647,7 @@ def test_forward_extreme_scale_bytes(form):
     an infinite weight times a zero or opposite-signed lo term is NaN, so there
     an element the oracle gives as +-inf may come out NaN (never finite, never
     the other sign)."""
-    w, c, s, ex, x, wr, b = hostile_layer()
+    w, c, s, ex, x, wr, b = hostile_layer(H)
     desc, codes, scales = pack_whole(w, c, s)
     wr_d, b_d = torch.from_numpy(wr).to(DEV), torch.from_numpy(b).to(DEV)
     xb_bits = synth.f32_to_bf16_bits(x)
