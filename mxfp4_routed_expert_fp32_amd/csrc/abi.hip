@@ -73,10 +73,24 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, rpart, sortws, total;
+  size_t logits, idx, w, h, y, offsets, pairs, blocks, nblocks, rpart, sortws, xsplit, total;
   int max_blocks;
   bool has_rpart;
 };
+
+int64_t grouped_batch(const moe_layer_desc* d, int32_t k, int x_terms);
+
+// fp32 activations take the grouped (prefill) form from this many tokens on,
+// as three exact bf16 terms; fewer tokens stream each pair's expert in the
+// decode-form GEMVs.
+constexpr int32_t kF32GroupedMinTokens = 9;
+
+// The grouped form: bf16 x from two tokens on, fp32 x from
+// kF32GroupedMinTokens on (when the shape has one).
+bool grouped_form(const moe_layer_desc* d, int32_t T, int32_t k, bool x_f32) {
+  if (x_f32) return T >= kF32GroupedMinTokens && grouped_batch(d, k, 3) > 0;
+  return T > 1 && grouped_batch(d, k, 1) > 0;
+}
 
 moe_status forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayout* L) {
   size_t TE, Tk, TkI, TkH;
@@ -104,6 +118,13 @@ moe_status forward_layout(const moe_layer_desc* d, int32_t T, int32_t k, FwdLayo
   if (L->has_rpart && !mul_ok(TE, (size_t)moe::router_mfma_splits(T, d->hidden) * 4, &rp)) return MOE_ERR_OVERFLOW;
   L->rpart = c.take(rp);
   L->sortws = c.take(moe::sort_workspace_bytes(T, d->n_experts));
+  // fp32 x in the grouped form: one batch of x as three bf16 terms
+  size_t xs = 0;
+  if (T >= kF32GroupedMinTokens) {
+    const int64_t tb = grouped_batch(d, k, 3);
+    if (tb > 0 && !mul_ok((size_t)std::min<int64_t>(T, tb), (size_t)6 * d->hidden, &xs)) return MOE_ERR_OVERFLOW;
+  }
+  L->xsplit = c.take(xs);
   L->total = c.take(0);
   if (c.overflow) return MOE_ERR_OVERFLOW;
   // pair indices are int32 on the device; MFMA-path byte offsets are 32-bit
@@ -130,6 +151,7 @@ moe_status check_tokens(int32_t T, int32_t k, const moe_layer_desc* d) {
 // with 32-bit buffer offsets and an out-of-range sentinel at 1 GiB: x (bf16)
 // and the two bf16 terms of h must each stay below that; y (fp32) is stored
 // through 32-bit offsets below 2 GiB.
+
 bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
   return moe::grouped_shape_ok(d->hidden, d->inter) && T * d->hidden * 2 < (int64_t{1} << 30) &&
          P * d->inter * 4 < (int64_t{1} << 30) && P * d->hidden * 4 < (int64_t{1} << 31);
@@ -137,10 +159,11 @@ bool grouped_fits(const moe_layer_desc* d, int64_t T, int64_t P) {
 
 // Tokens per batch of the prefill form (larger T runs in batches of this
 // many tokens, which are independent); 0 if the shape has no prefill form.
-int64_t grouped_batch(const moe_layer_desc* d, int32_t k) {
+// x_terms: bf16 terms per activation (1 for bf16 x, 3 for fp32 x).
+int64_t grouped_batch(const moe_layer_desc* d, int32_t k, int x_terms) {
   if (is_s4(d) || !moe::grouped_shape_ok(d->hidden, d->inter)) return 0;  // scale4: decode form only
   const int64_t H = d->hidden, I = d->inter;
-  int64_t tb = ((int64_t{1} << 30) - 1) / (H * 2);
+  int64_t tb = ((int64_t{1} << 30) - 1) / (H * 2 * x_terms);
   tb = std::min(tb, ((int64_t{1} << 30) - 1) / (k * I * 4));
   tb = std::min(tb, ((int64_t{1} << 31) - 1) / (k * H * 4));
   return tb >= 2 ? tb : 0;
@@ -168,18 +191,25 @@ moe_status run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const
   float* y = reinterpret_cast<float*>(ws + L.y);
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  const int64_t tb = grouped_batch(d, k);
-  if (T > 1 && !x_f32 && tb > 0) {
-    // prefill form, per batch of tokens: sort pairs by expert, grouped GEMMs on MFMA, combine
+  if (grouped_form(d, T, k, x_f32)) {
+    // prefill form, per batch of tokens: sort pairs by expert, grouped GEMMs on
+    // MFMA, combine; fp32 x goes to the GEMMs as three exact bf16 terms
+    const int xt = x_f32 ? 3 : 1;
+    const int64_t tb = grouped_batch(d, k, xt);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
     int4* blocks = reinterpret_cast<int4*>(ws + L.blocks);
     int32_t* nblocks = reinterpret_cast<int32_t*>(ws + L.nblocks);
     uint16_t* hterm = reinterpret_cast<uint16_t*>(h);  // [2][n*k][I] bf16, same bytes as h
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xsplit);
     for (int64_t t0 = 0; t0 < T; t0 += tb) {
       const int n = (int)std::min<int64_t>(tb, T - t0);
       const int Pn = n * k;
+      const uint16_t* xb = static_cast<const uint16_t*>(x) + t0 * H;
+      if (x_f32) {
+        MOE_TRY(dev(moe::launch_split3(static_cast<const float*>(x) + t0 * H, n, H, xs, s)));
+        xb = xs;
+      }
       if (moe::sort_is_one_workgroup(n, ws + L.sortws)) {  // the sort also cuts the blocks
         MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s, blocks,
                                                L.max_blocks, nblocks)));
@@ -187,8 +217,8 @@ moe_status run_experts(const moe_layer_desc* d, const void* x, bool x_f32, const
         MOE_TRY(dev(moe::launch_sort_by_expert(idx + t0 * k, n, E, k, offsets, pairs, ws + L.sortws, s)));
         MOE_TRY(dev(moe::launch_expert_blocks(offsets, E, L.max_blocks, blocks, nblocks, s)));
       }
-      MOE_TRY(dev(moe::launch_gateup_mfma(xb + t0 * H, n, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, k,
-                                          Pn, hterm, s)));
+      MOE_TRY(dev(moe::launch_gateup_mfma(xb, n, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, k, Pn, hterm,
+                                          s, xt)));
       MOE_TRY(dev(moe::launch_down_mfma(hterm, pairs, blocks, nblocks, L.max_blocks, c, sc, H, I, E, Pn, y, s)));
       MOE_TRY(dev(moe::launch_combine(y, w + t0 * k, n, k, H, resid ? resid + t0 * H : nullptr, out + t0 * H, s)));
     }
@@ -266,11 +296,11 @@ moe_status forward_impl(const moe_layer_desc* d, const void* x, moe_dtype x_dtyp
                                                router_bias, T, d->hidden, d->n_experts, logits, norm_out, s)));
     x = norm_out;
   }
-  const bool prefill = T > 1 && !xf && grouped_batch(d, k) > 0;
+  const bool prefill = grouped_form(d, T, k, xf);
   bool selected = false;
   if (!norm_gamma) {
     float* rpart = L.has_rpart ? reinterpret_cast<float*>(ws + L.rpart) : nullptr;
-    if (prefill && rpart && T > 8) {
+    if (prefill && !xf && rpart && T > 8) {
       // the MFMA router runs its K slices in workgroups of their own; their
       // sum and the top-k run as one launch
       MOE_TRY(dev(moe::launch_router_mfma(static_cast<const uint16_t*>(x), router_w, router_bias, T, d->hidden,

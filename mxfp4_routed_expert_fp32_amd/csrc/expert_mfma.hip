@@ -334,7 +334,7 @@ constexpr int dma_wait_ops(int da, int dmaops, int codeops, int h) {
 // chunk be read before it is in LDS.  (Stores issued between, at the down
 // kernel's tile ends, only lengthen a wait.)
 constexpr bool dma_waits_exact(int da, int dmaops, int codeops, int db, int nchunks) {
-  int last[160] = {};  // op count when the DMA of a chunk was issued
+  int last[256] = {};  // op count when the DMA of a chunk was issued
   int n = 0;
   const int v0 = 2 * (db - 1) > da ? 2 * (db - 1) : da;
   for (int v = -v0; v < 0; ++v) {
@@ -356,11 +356,14 @@ constexpr bool dma_waits_exact(int da, int dmaops, int codeops, int db, int nchu
 // gate/up: MS/2 DMA instructions and 4 code loads per chunk; (da, MS) as used
 static_assert(dma_waits_exact(3, 1, 4, 4, 56) && dma_waits_exact(2, 2, 4, 4, 56) && dma_waits_exact(2, 3, 4, 4, 56) &&
                   dma_waits_exact(1, 3, 4, 4, 56) && dma_waits_exact(1, 4, 4, 4, 56) && dma_waits_exact(3, 1, 4, 4, 2) &&
-                  dma_waits_exact(1, 4, 4, 4, 2) && dma_waits_exact(2, 3, 4, 4, 64) && dma_waits_exact(2, 2, 4, 4, 18),
+                  dma_waits_exact(1, 4, 4, 4, 2) && dma_waits_exact(2, 3, 4, 4, 64) && dma_waits_exact(2, 2, 4, 4, 18) &&
+                  // three-term activations (fp32 x): K' = 3 H
+                  dma_waits_exact(3, 1, 4, 4, 168) && dma_waits_exact(2, 3, 4, 4, 168) &&
+                  dma_waits_exact(1, 4, 4, 4, 168) && dma_waits_exact(3, 1, 4, 4, 6),
               "gate/up DMA wait counts");
 
 template <int MT, int DB, int NB, bool MID>
-__device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, rsrc_t rx,
+__device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P, int xt, rsrc_t rx,
                                              const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                              const int32_t* pid, const uint32_t* row_base, uint8_t* lds,
                                              int act_bytes, uint16_t* __restrict__ hterm) {
@@ -382,7 +385,12 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   const int row = nt * kGU_NT + wid * 16 + nl;
   const bool rok = row < I;
   const uint32_t boff = rok ? (uint32_t)row * (uint32_t)(nb * 16) + 16u * g : kOOB;
-  const int nchunks = H / kKC, nsc = nchunks / 2;
+  // K' = xt H: the activation row holds xt terms of x back to back (xt = 3:
+  // an fp32 x as three bf16 terms), and superchunk sn of K' multiplies weight
+  // superchunk sn mod (H / 256); past K' a superchunk reads nothing
+  const int nsc_w = H / (2 * kKC);
+  const int nchunks = xt * (H / kKC), nsc = nchunks / 2;
+  auto wsc = [&](int sn) { return sn < nsc ? sn % nsc_w : nsc_w; };
   // scale table: gate rows, then up rows, of this row tile
   uint8_t* tab = lds + act_bytes;
   const int pitch = scale_row_pitch(nb);
@@ -407,8 +415,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
     if (v + DA >= 0) dma_chunk<MS>(rx, doff, kb_of(v + DA), lds + (v + DA) * kBuf);
     if (v % 2 == 0 && v / 2 + DB - 1 >= 0) {
       const int sn = v / 2 + DB - 1;
-      load_bcodes(rg[sn], rcg, boff, sn, nsc);
-      load_bcodes(ru[sn], rcu, boff, sn, nsc);
+      load_bcodes(rg[sn], rcg, boff, wsc(sn), nsc_w);
+      load_bcodes(ru[sn], rcu, boff, wsc(sn), nsc_w);
     }
   }
   scales_put<kGuScaleU>(spg, tab, nb, ttotal);
@@ -416,8 +424,8 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
   wait_vm_barrier<dma_wait_ops(DA, MS / 2, 4, 1)>();  // chunk 0 (and the scale table) in LDS, as at the end of chunk -1
 #pragma unroll
   for (int d = 0; d < DB - 1; ++d) {
-    load_bscales(rg[d], tg, d, nsc);
-    load_bscales(ru[d], tu, d, nsc);
+    load_bscales(rg[d], tg, wsc(d), nsc_w);
+    load_bscales(ru[d], tu, wsc(d), nsc_w);
   }
 
   f32x4 acc[MT][2];
@@ -464,13 +472,14 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           dma_chunk<MS>(rx, doff, kb_of(c + DA), lds + nslot * kBuf);
         }
         const int sn = sc0 + d + DB - 1;  // the superchunk an even chunk requests
+        const int sw = wsc(sn);           // its weight superchunk
         if (h == 0) {
           if constexpr (!kSpread) {
-            load_bcodes(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc);
-            load_bcodes(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc);
+            load_bcodes(rg[(d + DB - 1) % DB], rcg, boff, sw, nsc_w);
+            load_bcodes(ru[(d + DB - 1) % DB], rcu, boff, sw, nsc_w);
           }
-          load_bscales(rg[(d + DB - 1) % DB], tg, sn, nsc);
-          load_bscales(ru[(d + DB - 1) % DB], tu, sn, nsc);
+          load_bscales(rg[(d + DB - 1) % DB], tg, sw, nsc_w);
+          load_bscales(ru[(d + DB - 1) % DB], tu, sw, nsc_w);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
         const uint8_t* A = lds + slot * kBuf;
@@ -495,10 +504,10 @@ __device__ __forceinline__ void gateup_block(int e, int nt, int H, int I, int P,
           if (j < NQ) fa[(q0 + j) % RF] = lds_frag_sw(A, j % MT, nl, 4 * g + j / MT);
           else if (MID) fa[(q0 + j) % RF] = lds_frag_sw(An, (j - NQ) % MT, nl, 4 * g + (j - NQ) / MT);
           if (kSpread && h == 0) {
-            if (i == WP0) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc, 0);
-            if (i == WP0 + WS) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sn, nsc, 1);
-            if (i == WP0 + 2 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc, 0);
-            if (i == WP0 + 3 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sn, nsc, 1);
+            if (i == WP0) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sw, nsc_w, 0);
+            if (i == WP0 + WS) load_bcode_half(rg[(d + DB - 1) % DB], rcg, boff, sw, nsc_w, 1);
+            if (i == WP0 + 2 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sw, nsc_w, 0);
+            if (i == WP0 + 3 * WS) load_bcode_half(ru[(d + DB - 1) % DB], rcu, boff, sw, nsc_w, 1);
           }
           if (m == 0 && st > 0) {
             bg = decode8(rg[d].q[h][st], sgv);
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const int4* __restrict__ blocks,
     const int32_t* __restrict__ nblocks, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int T, int H, int I, int E, int k, int P, int max_blocks, int ntiles,
-    int large, uint16_t* __restrict__ hterm) {
+    int large, int xt, uint16_t* __restrict__ hterm) {
   extern __shared__ uint4 lds_dyn[];  // activation buffers, then the scale table
   uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds_dyn);
   const int act = large ? kGuActLarge : kGuActSmall;
@@ -556,23 +565,23 @@ __global__ __launch_bounds__(kThr, 1) void k_gateup_mfma(
     int p = i < cnt ? pairs[blk.y + i] : -1;
     if (p >= P) p = -1;
     pid[i] = p;
-    row_base[i] = p >= 0 ? (uint32_t)(p / k) * (uint32_t)(H * 2) : kFar;
+    row_base[i] = p >= 0 ? (uint32_t)(p / k) * (uint32_t)(xt * H * 2) : kFar;
   }
   __syncthreads();
-  const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * H * 2));
+  const rsrc_t rx = mk_rsrc(x, (uint32_t)((size_t)T * xt * H * 2));
   switch ((cnt + 15) / 16) {
-    case 1: gateup_block<1, kGuDB, gu_nbuf_small(1), (gu_nbuf_small(1) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 2: gateup_block<2, kGuDB, gu_nbuf_small(2), (gu_nbuf_small(2) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 3: gateup_block<3, kGuDB, gu_nbuf_small(3), (gu_nbuf_small(3) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 4: gateup_block<4, kGuDB, gu_nbuf_small(4), (gu_nbuf_small(4) >= 3)>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
-    case 5: (large ? gateup_block<5, kGuDB, 4, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<5, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    case 6: (large ? gateup_block<6, kGuDB, 4, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<6, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    case 7: (large ? gateup_block<7, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<7, kGuDB, 2, false>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
-    default: (large ? gateup_block<8, kGuDB, 3, true>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)
-                   : gateup_block<8, kGuDB, 2, false>(e, nt, H, I, P, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 1: gateup_block<1, kGuDB, gu_nbuf_small(1), (gu_nbuf_small(1) >= 3)>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 2: gateup_block<2, kGuDB, gu_nbuf_small(2), (gu_nbuf_small(2) >= 3)>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 3: gateup_block<3, kGuDB, gu_nbuf_small(3), (gu_nbuf_small(3) >= 3)>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 4: gateup_block<4, kGuDB, gu_nbuf_small(4), (gu_nbuf_small(4) >= 3)>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm); break;
+    case 5: (large ? gateup_block<5, kGuDB, 4, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<5, kGuDB, 3, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 6: (large ? gateup_block<6, kGuDB, 4, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<6, kGuDB, 3, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    case 7: (large ? gateup_block<7, kGuDB, 3, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<7, kGuDB, 2, false>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
+    default: (large ? gateup_block<8, kGuDB, 3, true>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)
+                   : gateup_block<8, kGuDB, 2, false>(e, nt, H, I, P, xt, rx, codes, scales, pid, row_base, lds8, act, hterm)); break;
   }
 }
 
@@ -1122,11 +1131,13 @@ bool grouped_shape_ok(int64_t H, int64_t I) {
 
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
                               const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
-                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s) {
+                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s, int x_terms) {
+  if (x_terms != 1 && x_terms != 3) return hipErrorInvalidValue;
   const int ntiles = (I + kGU_NT - 1) / kGU_NT;
   const size_t lds = gateup_lds(H);
   k_gateup_mfma<<<dim3(items_grid(max_blocks, ntiles)), kThr, lds, s>>>(
-      x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, gu_large(H) ? 1 : 0, hterm);
+      x, pairs, blocks, nblocks, codes, scales, T, H, I, E, k, P, max_blocks, ntiles, gu_large(H) ? 1 : 0, x_terms,
+      hterm);
   return hipGetLastError();
 }
 

@@ -56,9 +56,11 @@ bool grouped_shape_ok(int64_t H, int64_t I);
 int max_expert_blocks(int P, int E);
 hipError_t launch_expert_blocks(const int32_t* offsets, int E, int max_blocks, int4* blocks, int32_t* nblocks,
                                 hipStream_t s);
+// x_terms = 1: x is [T][H] bf16; 3: x is [T][3H], the three exact bf16 terms
+// of an fp32 x back to back along K (launch_split3).
 hipError_t launch_gateup_mfma(const uint16_t* x, int T, const int32_t* pairs, const int4* blocks,
                               const int32_t* nblocks, int max_blocks, const uint8_t* codes, const uint8_t* scales,
-                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s);
+                              int H, int I, int E, int k, int P, uint16_t* hterm, hipStream_t s, int x_terms = 1);
 hipError_t launch_down_mfma(const uint16_t* hterm, const int32_t* pairs, const int4* blocks, const int32_t* nblocks,
                             int max_blocks, const uint8_t* codes, const uint8_t* scales, int H, int I, int E, int P,
                             float* ybuf, hipStream_t s);
@@ -110,5 +112,10 @@ hipError_t launch_rmsnorm(const float* r, const float* gamma, float eps, int T, 
                           hipStream_t s);
 hipError_t launch_residual_add(float* r, const float* d, size_t n, hipStream_t s);
 hipError_t launch_widen(const void* x, bool x_f32, size_t n, float* out, hipStream_t s);
+// fp32 rows x [T][H] as three bf16 terms per element, out [T][3][H] (row t:
+// hi of every element, then mid, then lo): hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid), round to nearest even; hi + mid + lo == x exactly
+// for every finite x whose terms stay in bf16's normal range.
+hipError_t launch_split3(const float* x, int T, int H, uint16_t* out, hipStream_t s);
 
 }  // namespace moe

@@ -227,4 +227,41 @@ hipError_t launch_widen(const void* x, bool x_f32, size_t n, float* out, hipStre
   return hipGetLastError();
 }
 
+// Three bf16 terms of fp32 rows (the grouped expert GEMMs' activation operand
+// for fp32 x).  x - hi has at most 16 significant bits and x - hi - mid at
+// most 8, so both subtractions are exact in fp32 and the three terms add up to
+// x (above bf16's largest finite value hi is that value).  A NaN or an
+// infinity goes whole into hi (mid and lo are 0).
+__global__ __launch_bounds__(256) void k_split3(const float* __restrict__ x, int T, int H,
+                                                uint16_t* __restrict__ out) {
+  const size_t n = (size_t)T * H;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const float v = x[i];
+    uint16_t hi = f32_to_bf16_rne(v);
+    uint16_t mid = 0, lo = 0;
+    if (isfinite(v)) {
+      // above bf16's largest finite value hi would round to infinity: take the
+      // largest finite bf16 instead (the rest still fits mid and lo)
+      if ((hi & 0x7FFFu) == 0x7F80u) hi = (uint16_t)((hi & 0x8000u) | 0x7F7Fu);
+      const float r1 = v - bf16_bits_to_f32(hi);
+      mid = f32_to_bf16_rne(r1);
+      lo = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mid));
+    }
+    const size_t t = i / (size_t)H, c = i - t * (size_t)H;
+    uint16_t* o = out + t * 3 * (size_t)H + c;
+    o[0] = hi;
+    o[H] = mid;
+    o[2 * (size_t)H] = lo;
+  }
+}
+
+hipError_t launch_split3(const float* x, int T, int H, uint16_t* out, hipStream_t s) {
+  const size_t n = (size_t)T * H;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) return hipSuccess;
+  k_split3<<<dim3((unsigned)blocks), 256, 0, s>>>(x, T, H, out);
+  return hipGetLastError();
+}
+
 }  // namespace moe
