@@ -195,6 +195,10 @@ moe_status moe_mxfp4_pack(const moe_layer_desc* desc, const void* logical_codes,
  *                lower expert id, NaN below every number), or NULL
  *   topk_w_out   [n_tokens][k] fp32 combine weights, or NULL
  *   workspace    device buffer of at least moe_workspace_bytes(desc, n_tokens, k)
+ * Forms (same results within the output bar): one token, or fp32 x below 9
+ * tokens, runs the decode GEMVs; bf16 x from 2 tokens on, and fp32 x from 9
+ * on (as three exact bf16 terms), the grouped expert GEMMs, where the shape
+ * has them (H and I multiples of 256, 8-bit scales).
  * Deterministic: the same inputs give bit-identical outputs on every call.
  * Errors: descriptor errors, MOE_ERR_NULL, MOE_ERR_DTYPE, MOE_ERR_SHAPE,
  * MOE_ERR_ALIGN (x, router_w, the packed buffers, out or workspace not 16-byte
