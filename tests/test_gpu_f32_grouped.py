@@ -8,7 +8,9 @@ batch instead of once per (token, rank) pair.
 - on fp32 x whose values are exact in bf16 the three-term form gives the
   bf16 form's values (its two extra terms are zeros);
 - the layer stack (fp32 residual stream) with more than 8 tokens, layer by
-  layer against the oracle.
+  layer against the oracle;
+- activations above bf16's largest finite value, and near 1e30 and 1e-30,
+  in both the grouped and the per-token form.
 """
 import numpy as np
 import pytest
@@ -111,3 +113,47 @@ def test_stack_f32_tokens_grouped_layer_by_layer():
         o, *_ = oracle.moe_forward(n, wrs[l].cpu().numpy(), exs[l], H, I, k, logits_override=lg.cpu().numpy())
         r = oracle.residual_add(r, o)
     P.assert_out_close(got, r)
+
+
+def test_f32_grouped_extreme_magnitudes():
+    """fp32 activations far outside bf16's comfortable range, through the
+    expert entry on fixed routes: token 0 holds values above bf16's largest
+    finite value (3.3895e38, where the split keeps hi at that value and puts
+    the rest in mid and lo), token 1 values near 1e30, token 2 values near
+    1e-30, the rest N(0,1) times 1e29..1e31 per token.  Every weight has scale byte 27 (2^-100), so the
+    large tokens still give finite h and outputs.  The grouped form (12
+    tokens) and the per-token decode form both meet the bar against the
+    oracle's given-routing entry."""
+    H, I, E, k, T = 512, 256, 6, 3, 12
+    w = synth.Workload("g32x", 94, T, H, I, E, k, "f32", weight_seed=9910)
+    c, s, ex = experts_host(w)
+    s[:] = 27
+    ex = [(c[e * w.code_bytes_per_expert:(e + 1) * w.code_bytes_per_expert],
+           s[e * w.scale_bytes_per_expert:(e + 1) * w.scale_bytes_per_expert]) for e in range(E)]
+    desc, codes, scales = pack_whole(w, c, s)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0] = np.float32(3.395e38) * np.where(rng.random(H) < 0.5, -1.0, 1.0).astype(np.float32) \
+        * (1.0 + 0.001 * rng.random(H)).astype(np.float32)
+    assert np.all(np.isfinite(x[0])) and np.all(np.abs(x[0]) > np.float32(3.3895e38))
+    x[1] *= np.float32(1e30)
+    x[2] *= np.float32(1e-30)
+    x[3:] *= (10.0 ** rng.uniform(29, 31, (T - 3, 1))).astype(np.float32)
+    idx = np.array([[(t + j) % E for j in range(k)] for t in range(T)], np.int32)
+    wts = np.array([[0.5, 0.3, 0.2]] * T, np.float32)
+    r_out = oracle.moe_experts(x, idx, wts, ex, H, I, E)
+    assert np.all(np.isfinite(r_out))
+    xd = torch.from_numpy(x).to(DEV)
+    idx_d, wts_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(wts).to(DEV)
+    out = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe.workspace_bytes(desc, T, k), dtype=torch.uint8, device=DEV)
+    moe.moe_mxfp4_experts(desc, xd, idx_d, wts_d, codes, scales, k, out, ws)          # grouped form
+    torch.cuda.synchronize()
+    P.assert_layer_close(out.cpu().numpy(), r_out, x, idx, wts, ex, H, I, E)
+    one = torch.empty(1, H, dtype=torch.float32, device=DEV)
+    ws1 = torch.empty(moe.workspace_bytes(desc, 1, k), dtype=torch.uint8, device=DEV)
+    for t in (0, 1, 2):                                                               # decode form
+        moe.moe_mxfp4_experts(desc, xd[t:t + 1], idx_d[t:t + 1], wts_d[t:t + 1], codes, scales, k, one, ws1)
+        torch.cuda.synchronize()
+        P.assert_layer_close(one.cpu().numpy(), r_out[t:t + 1], x[t:t + 1], idx[t:t + 1], wts[t:t + 1], ex, H,
+                             I, E)
