@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
 // Scales: 8-bit, the workgroup's rows of both tables (contiguous bytes) are
 // copied into LDS once before the first row; scale4, the row base by a scalar
 // load and the block's delta by a byte load beside its code load.
-// SEL as in k_gateup_gemv: wave 0 selects while the other waves load x.
+// SEL as in k_gateup_gemv; with KS >= 2 waves the selection's per-logit work
+// is shared by all of them (topk_wg), and every wave loads x after it.
 constexpr int kGuKsRing = 4;       // weight steps in flight + 1
 constexpr int kGuKsTabLoads = 2;   // 16-byte scale chunks per thread and matrix
 // rows_per_wg * H/32 <= kGuKsTabLoads * 16 * 64 * KS (the table's capacity), in whole ring passes
@@ -446,8 +447,9 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
   const int b = ks * 32 + c;  // this lane's block of every row
   const int t = p / k;
 
-  // this lane's 32 activations (the selecting wave loads them after the
-  // selection, which then has the registers to itself)
+  // this lane's 32 activations (with selection, loaded after it: the
+  // selection's barriers then wait for nothing in flight, and x arrives
+  // alongside the first weights)
   uint32_t xr[1][XW];
   auto load_x = [&]() {
     const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) +
@@ -460,14 +462,19 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
   };
   int e;
   if constexpr (SEL > 0) {
-    __shared__ uint64_t cand[2 * kWave];
     __shared__ int32_t chosen;
-    if (ks != 0) load_x();
-    if (ks == 0) {
-      int sel;
-      float wv;
-      const bool writer = part == 0 && p % k == 0;  // the token's workgroup that publishes the selection
+    int sel;
+    float wv;
+    const bool writer = part == 0 && p % k == 0;  // the token's workgroup that publishes the selection
+    if constexpr (KS >= 2) {
+      // all waves share the per-logit work; wave 0 holds the result
+      __shared__ TopkWgLds<KS> tsm;
+      topk_wg<KS, (SEL + KS - 1) / KS, SEL>(logits + (size_t)t * E, E, k, tsm, &sel, &wv, writer);
+    } else {
+      __shared__ uint64_t cand[2 * kWave];
       topk_wave<SEL>(logits + (size_t)t * E, E, k, cand, &sel, &wv, writer);
+    }
+    if (ks == 0) {
       if (lane == p % k) chosen = sel;
       if (writer && lane < k) {
         route[(size_t)t * k + lane] = sel;
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     }
     __syncthreads();
     e = __builtin_amdgcn_readfirstlane(chosen);
-    if (ks == 0) load_x();
+    load_x();
   } else {
     load_x();
     e = __builtin_amdgcn_readfirstlane(route[p]);

@@ -55,6 +55,63 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
+// Each candidate's rank among the `total` (<= 64) candidates cand[0, total),
+// read in place: entries past `total` must be 0, which never counts.  16
+// entries (8 reads) are requested at a time, then compared, so the reads'
+// latency is paid once per batch.  Lane i < total gets the rank and key of
+// candidate i; other lanes keep theirs (rank kWave: not selected).
+__device__ __forceinline__ void rank_candidates(const uint64_t* cand, uint32_t total, int* my_rank,
+                                                uint64_t* my_key) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
+  int r = 0;
+  auto batch = [&](int j0) {
+    ulonglong2 kk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kk[q] = *reinterpret_cast<const ulonglong2*>(cand + j0 + 2 * q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r += (kk[q].x > c ? 1 : 0) + (kk[q].y > c ? 1 : 0);
+  };
+  batch(0);
+  if (total > 16) batch(16);
+  if (total > 32) {
+    batch(32);
+    batch(48);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if ((uint32_t)lane < total) {
+    *my_rank = r;
+    *my_key = c;
+  }
+}
+
+// From every lane's (rank, key) (rank >= k: not selected) to lane j < k
+// holding the expert of rank j and its softmax weight (lanes >= k: expert 0,
+// weight 0); cand (64 keys) is scratch.  weights = false leaves every weight
+// 0.
+__device__ __forceinline__ void topk_finish(uint64_t* cand, int my_rank, uint64_t my_key, int k, int* sel_out,
+                                            float* w_out, bool weights) {
+  const int lane = threadIdx.x % kWave;
+  // lane r < k receives the key of rank r
+  if (my_rank < k) cand[my_rank] = my_key;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const uint64_t kj = (lane < k) ? cand[lane] : 0ull;
+  const int sel = (lane < k) ? (int)~(uint32_t)kj : 0;
+  *sel_out = sel;
+  *w_out = 0.0f;
+  if (!weights) return;
+  // softmax over the selected logits, in rank order, each logit decoded from
+  // its key; lane 0 holds the largest
+  const float lj = (lane < k) ? key_logit(kj) : 0.0f;
+  const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
+  const float ex = (lane < k) ? expf(lj - m) : 0.0f;
+  const float s = wave_sum(ex);
+  *w_out = lane < k ? ex / s : 0.0f;
+}
+
 // One wavefront selects for one token; lane l owns experts MAXV*l + v, v <
 // MAXV (contiguous, so a row of E % 4 == 0 logits is read with 16-byte
 // loads).  Selection: let T be the k-th largest of the 64 lane maxima's top
@@ -143,29 +200,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const uint64_t c = ((uint32_t)lane < total) ? cand[lane] : 0ull;
-    // each candidate's rank among the candidates (usually about k), read in
-    // place: entries past `total` are 0 and never count.  16 entries (8
-    // reads) are requested at a time, then compared, so the reads' latency
-    // is paid once per batch.
-    int r = 0;
-    auto batch = [&](int j0) {
-      ulonglong2 kk[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) kk[q] = *reinterpret_cast<const ulonglong2*>(cand + j0 + 2 * q);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) r += (kk[q].x > c ? 1 : 0) + (kk[q].y > c ? 1 : 0);
-    };
-    batch(0);
-    if (total > 16) batch(16);
-    if (total > 32) {
-      batch(32);
-      batch(48);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if ((uint32_t)lane < total) { my_rank = r; my_key = c; }
+    rank_candidates(cand, total, &my_rank, &my_key);
   } else {
     Mask left = alive;  // present and not taken yet
     for (int j = 0; j < k; ++j) {
@@ -179,22 +214,104 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
       if (lane == j) { my_rank = j; my_key = win; }
     }
   }
-  // lane r < k receives the key of rank r (cand is free again)
-  if (my_rank < k) cand[my_rank] = my_key;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const uint64_t kj = (lane < k) ? cand[lane] : 0ull;
-  const int sel = (lane < k) ? (int)~(uint32_t)kj : 0;
-  *sel_out = sel;
+  topk_finish(cand, my_rank, my_key, k, sel_out, w_out, weights);
+}
+
+// LDS of topk_wg for a workgroup of KS waves.
+template <int KS>
+struct TopkWgLds {
+  uint32_t gmax[kWave * KS];  // [lane][wave]: each lane's largest key word
+  uint64_t cand[2 * kWave];   // candidates; then topk_finish's (and the fallback's) scratch
+  uint32_t bound;             // T
+  uint32_t count;             // candidate slots claimed
+};
+
+// topk_wave's selection with the per-logit work spread over the KS waves of a
+// workgroup (all of them call it; wave 0 returns the result, the others
+// expert 0 and weight 0).  Lane l of wave w holds experts
+// v * 64 KS + 64 w + l, v < MAXW, so each wave's loads are contiguous.
+//  1. Every lane makes its keys' upper words and their maximum.
+//  2. Wave 0 takes, for each of its lanes g, the largest of lane g's maxima
+//     over the waves (64 group maxima, each a distinct key) and finds T as
+//     topk_wave does on its lane maxima: at least k keys are >= T, so the top
+//     k keys all are.
+//  3. Every lane claims slots for its keys >= T with one LDS atomic and
+//     writes them there (in no particular order: ranks are counted).
+//  4. Wave 0 ranks the candidates and finishes as topk_wave does.
+// When more than 64 keys qualify, or T = 0, wave 0 runs topk_wave<MAXV>
+// instead.  Both give the unique order of the rank keys, so the result is
+// topk_wave's, bit for bit.  E <= 64 KS MAXW and E <= 64 MAXV.  Contains
+// workgroup barriers: every wave of the workgroup must call it.
+template <int KS, int MAXW, int MAXV>
+__device__ __forceinline__ void topk_wg(const float* __restrict__ l, int E, int k, TopkWgLds<KS>& sm, int* sel_out,
+                                        float* w_out, bool weights) {
+  static_assert(KS >= 2, "one wave: topk_wave");
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  // all loads first (an absent expert's load reads expert 0), then the keys
+  float lv[MAXW];
+#pragma unroll
+  for (int v = 0; v < MAXW; ++v) {
+    const int e = v * kWave * KS + wid * kWave + lane;
+    lv[v] = l[e < E ? e : 0];
+  }
+  uint32_t ord[MAXW];
+  uint32_t mo = 0;
+#pragma unroll
+  for (int v = 0; v < MAXW; ++v) {
+    const int e = v * kWave * KS + wid * kWave + lane;
+    const uint32_t o = e < E ? rank_ord(lv[v]) : 0u;  // absent experts: 0, like NaN
+    ord[v] = o;
+    mo = o > mo ? o : mo;
+  }
+  sm.gmax[lane * KS + wid] = mo;
+  if (wid == 0) sm.cand[lane] = 0ull;  // rank_candidates reads 0 past the candidates
+  if (threadIdx.x == 0) sm.count = 0u;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t g = 0;
+#pragma unroll
+    for (int w = 0; w < KS; ++w) {
+      const uint32_t m = sm.gmax[lane * KS + w];
+      g = m > g ? m : g;
+    }
+    uint32_t T = 0;
+#pragma unroll
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t c = T | (1u << bit);
+      if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(g >= c)) >= k) T = c;
+    }
+    if (lane == 0) sm.bound = T;
+  }
+  __syncthreads();
+  const uint32_t T = sm.bound;
+  if (T != 0) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int v = 0; v < MAXW; ++v) n += ord[v] >= T ? 1u : 0u;
+    if (n) {
+      uint32_t slot = atomicAdd(&sm.count, n);
+#pragma unroll
+      for (int v = 0; v < MAXW; ++v) {
+        if (ord[v] >= T) {
+          if (slot < (uint32_t)kWave) sm.cand[slot] = make_key(ord[v], (uint32_t)(v * kWave * KS + wid * kWave + lane));
+          ++slot;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  *sel_out = 0;
   *w_out = 0.0f;
-  if (!weights) return;
-  // softmax over the selected logits, in rank order, each logit decoded from
-  // its key; lane 0 holds the largest
-  const float lj = (lane < k) ? key_logit(kj) : 0.0f;
-  const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lj)));
-  const float ex = (lane < k) ? expf(lj - m) : 0.0f;
-  const float s = wave_sum(ex);
-  *w_out = lane < k ? ex / s : 0.0f;
+  if (wid != 0) return;
+  const uint32_t total = sm.count;
+  if (T == 0 || total > (uint32_t)kWave) {
+    topk_wave<MAXV>(l, E, k, sm.cand, sel_out, w_out, weights);
+    return;
+  }
+  int my_rank = kWave;
+  uint64_t my_key = 0;
+  rank_candidates(sm.cand, total, &my_rank, &my_key);
+  topk_finish(sm.cand, my_rank, my_key, k, sel_out, w_out, weights);
 }
 
 }  // namespace moe

@@ -736,3 +736,62 @@ def test_gate_up_select_stage(T, E, k, xd):
     assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
     assert np.array_equal(P.bits(wt.cpu().numpy()), P.bits(wt2.cpu().numpy()))
     assert np.array_equal(P.bits(h.cpu().numpy()), P.bits(h2.cpu().numpy()))
+
+
+def hostile_logit_rows(E, k, rng):
+    """Rows that take every branch of the selection: random; all equal (more
+    than 64 candidates); all NaN and fewer than k numbers (no bound); ties
+    with signed zeros, NaN and -inf; a tie at the top; -inf with a few
+    numbers; one huge and the rest tiny."""
+    rows = [rng.standard_normal(E)]
+    rows.append(np.full(E, 0.5))
+    rows.append(np.full(E, np.nan))
+    r = np.full(E, np.nan)
+    r[rng.choice(E, min(E, max(1, k // 2)), replace=False)] = rng.standard_normal(min(E, max(1, k // 2)))
+    rows.append(r)
+    pool = np.array([1.0, 0.0, -0.0, -1.0, np.nan, -np.inf, 0.5, 2.0])
+    rows.append(pool[rng.integers(0, len(pool), E)])
+    r = rng.standard_normal(E)
+    r[rng.choice(E, min(E, 5), replace=False)] = 10.0
+    rows.append(r)
+    r = np.full(E, -np.inf)
+    r[rng.choice(E, min(E, k + 3), replace=False)] = rng.standard_normal(min(E, k + 3))
+    rows.append(r)
+    r = rng.standard_normal(E) * 1e-30
+    r[E // 2] = 3e38
+    rows.append(r)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("H,E,k,xd", [(7168, 896, 16, "bf16"), (7168, 896, 16, "f32"), (2048, 1024, 16, "bf16"),
+                                      (3072, 1000, 64, "f32"), (2048, 8, 2, "bf16"), (8192, 130, 7, "bf16")])
+def test_gate_up_select_stage_split_k(H, E, k, xd):
+    """The selecting gate/up stage in its K-split form (H a multiple of 1024,
+    E <= 1024: the decode forward's form at the model's width), where all
+    the workgroup's waves share the selection: on hostile logit rows (ties,
+    signed zeros, NaN, -inf, more than 64 candidates, fewer than k numbers)
+    its selection and weights equal moe_topk_softmax bit for bit, and its h
+    equals the routes-given stage on that selection."""
+    I = 64
+    rng = np.random.default_rng(E + H + k)
+    lg_h = hostile_logit_rows(E, k, rng)
+    T = lg_h.shape[0]
+    w = synth.Workload("gsk", 75, T, H, I, E, k, xd, weight_seed=8600 + E + H)
+    c, s, _ = experts_host(w)
+    desc, codes, scales = pack_whole(w, c, s)
+    x = sd.tokens(w, range(T))
+    lg = torch.from_numpy(lg_h).to(DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    h = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_gate_up_select(desc, x, lg, k, codes, scales, idx, wt, h)
+    idx2 = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wt2 = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    moe.moe_topk_softmax(lg, k, idx2, wt2)
+    h2 = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+    moe.moe_mxfp4_gate_up(desc, x, idx2.reshape(-1), k, codes, scales, h2)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), oracle.topk(lg_h, k))
+    assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    assert np.array_equal(P.bits(wt.cpu().numpy()), P.bits(wt2.cpu().numpy()))
+    assert np.array_equal(P.bits(h.cpu().numpy()), P.bits(h2.cpu().numpy()))
