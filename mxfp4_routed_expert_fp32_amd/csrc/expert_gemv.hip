@@ -31,6 +31,7 @@
 // the grid is sized to the number of workgroups the GPU holds at once
 // (occupancy x CUs), so every workgroup runs once, and weight loads run
 // several steps ahead of the compute.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -437,8 +438,8 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
   constexpr int XW = XF32 ? 32 : 16;  // registers per block of x
   constexpr bool TAB = !S4;
   // [rows_per_wg][2][KS] partials, then (TAB) the gate and up scale rows,
-  // [rows_per_wg][H/32] each
-  extern __shared__ float partial[];
+  // [rows_per_wg][H/32] each; before them, the selection's scratch
+  extern __shared__ __align__(16) float partial[];
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, ks = threadIdx.x / kWave;
@@ -467,8 +468,11 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     float wv;
     const bool writer = part == 0 && p % k == 0;  // the token's workgroup that publishes the selection
     if constexpr (KS >= 2) {
-      // all waves share the per-logit work; wave 0 holds the result
-      __shared__ TopkWgLds<KS> tsm;
+      // all waves share the per-logit work; wave 0 holds the result.  The
+      // scratch is the dynamic LDS, which nothing uses before the selection
+      // ends (its size is at least sizeof(TopkWgLds<KS>), see the launcher):
+      // static LDS would cost a workgroup per CU.
+      TopkWgLds<KS>& tsm = *reinterpret_cast<TopkWgLds<KS>*>(partial);
       topk_wg<KS, (SEL + KS - 1) / KS, SEL>(logits + (size_t)t * E, E, k, tsm, &sel, &wv, writer);
     } else {
       __shared__ uint64_t cand[2 * kWave];
@@ -848,7 +852,11 @@ static hipError_t gateup_ks_launch(int P, hipStream_t s, const void* x, int32_t*
                                    float* wsel, const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
                                    int k, float* hbuf) {
   constexpr int D = kGuKsRing;
-  auto lds_for = [&](int rows) { return (size_t)rows * 2 * KS * 4 + (S4 ? 0 : (size_t)2 * rows * (H / 32)); };
+  // the selection (SEL > 0, KS >= 2) keeps its scratch in the same LDS first
+  constexpr size_t sel_lds = (SEL > 0 && KS >= 2) ? sizeof(TopkWgLds<KS>) : 0;
+  auto lds_for = [&](int rows) {
+    return std::max(sel_lds, (size_t)rows * 2 * KS * 4 + (S4 ? 0 : (size_t)2 * rows * (H / 32)));
+  };
   const int target = resident_wgs(k_gateup_ks<KS, D, XF32, SEL, S4>, lds_for(kGuKsMaxRows), 64 * KS);
   const int want = (target + P - 1) / P;
   int rows = (I + want - 1) / want;
