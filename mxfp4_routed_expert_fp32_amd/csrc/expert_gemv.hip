@@ -470,8 +470,8 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     if constexpr (KS >= 2) {
       // all waves share the per-logit work; wave 0 holds the result.  The
       // scratch is the dynamic LDS, which nothing uses before the selection
-      // ends (its size is at least sizeof(TopkWgLds<KS>), see the launcher):
-      // static LDS would cost a workgroup per CU.
+      // ends (the launcher makes it at least sizeof(TopkWgLds<KS>)), so the
+      // selection adds no LDS to the workgroup.
       TopkWgLds<KS>& tsm = *reinterpret_cast<TopkWgLds<KS>*>(partial);
       topk_wg<KS, (SEL + KS - 1) / KS, SEL>(logits + (size_t)t * E, E, k, tsm, &sel, &wv, writer);
     } else {
