@@ -418,9 +418,9 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
 // of each row in wave order (a fixed order, so results are deterministic) and
 // applies SwiGLU.  Weight loads run D - 1 steps ahead; rows_per_wg is a
 // multiple of 2 D, so the unrolled ring has no exit inside.
-// Scales: 8-bit, the workgroup's rows of both tables (contiguous bytes) are
-// copied into LDS once before the first row; scale4, the row base by a scalar
-// load and the block's delta by a byte load beside its code load.
+// Scales: the workgroup's rows of both tables (contiguous bytes: 8-bit
+// E8M0 bytes, or scale4 deltas and bases) are copied into LDS once before
+// the first row, so the only weight loads are the code loads.
 // SEL as in k_gateup_gemv; with KS >= 2 waves the selection's per-logit work
 // is shared by all of them (topk_wg), and every wave loads x after it.
 constexpr int kGuKsRing = 4;       // weight steps in flight + 1
@@ -436,9 +436,10 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
                                                        int k, int parts, int rows_per_wg,
                                                        float* __restrict__ hbuf) {
   constexpr int XW = XF32 ? 32 : 16;  // registers per block of x
-  constexpr bool TAB = !S4;
-  // [rows_per_wg][2][KS] partials, then (TAB) the gate and up scale rows,
-  // [rows_per_wg][H/32] each; before them, the selection's scratch
+  // [rows_per_wg][2][KS] partials, then the gate and up scale rows,
+  // [rows_per_wg][rb] each (8-bit: rb = H/32 E8M0 bytes; scale4: rb = H/64
+  // bytes of deltas, then the rows' bases, [rows_per_wg] each); before them,
+  // the selection's scratch
   extern __shared__ __align__(16) float partial[];
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
@@ -504,51 +505,53 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
   const int nrows = min(rows_per_wg, I - r0);
   const int steps = rows_per_wg / 2;
 
-  // TAB: both matrices' scale rows r0 .. r0 + nrows - 1, loaded first (the
-  // ring's loads behind them need not land before the table is written)
+  // Both matrices' scale rows r0 .. r0 + nrows - 1, loaded first (the
+  // ring's loads behind them need not land before the table is written);
+  // rb is a multiple of 16 (H = 1024 KS), so chunks never straddle rows.
+  const int rb = S4 ? nb / 2 : nb;
   uint8_t* tab = reinterpret_cast<uint8_t*>(partial + rows_per_wg * 2 * KS);
-  const int tab_n16 = TAB ? nrows * nb / 16 : 0;  // chunks per matrix
+  uint8_t* tab_base = tab + 2 * rows_per_wg * rb;  // scale4: gate bases, then up bases
+  const int tab_n16 = nrows * rb / 16;             // chunks per matrix
+  const int tab_nb4 = S4 ? (nrows + 3) / 4 : 0;    // dwords of bases per matrix
   u32x4 tg[kGuKsTabLoads], tu[kGuKsTabLoads];
-  if constexpr (TAB) {
+  uint32_t bg = 0u, bu = 0u;
 #pragma unroll
-    for (int u = 0; u < kGuKsTabLoads; ++u) {
-      const int j = threadIdx.x + u * 64 * KS;
-      const uint32_t off = j < tab_n16 ? (uint32_t)r0 * (uint32_t)nb + 16u * j : kOOB;
-      tg[u] = __builtin_amdgcn_raw_buffer_load_b128(gsc.tab, off, 0, 2 /* nt */);
-      tu[u] = __builtin_amdgcn_raw_buffer_load_b128(usc.tab, off, 0, 2 /* nt */);
-    }
+  for (int u = 0; u < kGuKsTabLoads; ++u) {
+    const int j = threadIdx.x + u * 64 * KS;
+    const uint32_t off = j < tab_n16 ? (uint32_t)r0 * (uint32_t)rb + 16u * j : kOOB;
+    tg[u] = __builtin_amdgcn_raw_buffer_load_b128(gsc.tab, off, 0, 2 /* nt */);
+    tu[u] = __builtin_amdgcn_raw_buffer_load_b128(usc.tab, off, 0, 2 /* nt */);
   }
-  auto load = [&](RowBlocks<1>& r, rsrc_t cod, const ScaleSrc& sc, int st) {
+  if constexpr (S4) {
+    const uint32_t off = (int)threadIdx.x < tab_nb4 ? (uint32_t)r0 + 4u * threadIdx.x : kOOB;
+    bg = __builtin_amdgcn_raw_buffer_load_b32(gsc.base, off, 0, 2 /* nt */);
+    bu = __builtin_amdgcn_raw_buffer_load_b32(usc.base, off, 0, 2 /* nt */);
+  }
+  auto load = [&](RowBlocks<1>& r, rsrc_t cod, int st) {
     const int n = r0 + 2 * st + rsub;
     const bool ok = st < steps && n < I;
     r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(cod, ok ? (uint32_t)n * (uint32_t)(H / 2) + 16u * b : kOOB, 0,
                                                    2 /* nt */);
-    if constexpr (TAB) {
-      r.s[0] = 0u;  // read from LDS when the step is computed
-    } else {
-      // rows r0 + 2 st, + 1 (r0 and 2 st even) lie in one dword of bases: a scalar load
-      const int rr = (st < steps && r0 + 2 * st < I) ? r0 + 2 * st : 0;
-      r.base = (bases4(sc.bptr, rr >> 2) >> (((rr & 3) + rsub) * 8)) & 0xFFu;
-      r.s[0] = __builtin_amdgcn_raw_buffer_load_b8(sc.tab, ok ? (uint32_t)n * (uint32_t)(nb / 2) + (uint32_t)(b >> 1)
-                                                              : kOOB,
-                                                   0, 2 /* nt */);
-      r.valid = ok ? 1u : 0u;
-    }
+    r.s[0] = 0u;  // read from LDS when the step is computed
   };
   RowBlocks<1> gr[D], ur[D];
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) {
-    load(gr[d], gcod, gsc, d);
-    load(ur[d], ucod, usc, d);
+    load(gr[d], gcod, d);
+    load(ur[d], ucod, d);
   }
-  if constexpr (TAB) {
 #pragma unroll
-    for (int u = 0; u < kGuKsTabLoads; ++u) {
-      const int j = threadIdx.x + u * 64 * KS;
-      if (j < tab_n16) {
-        reinterpret_cast<u32x4*>(tab)[j] = tg[u];
-        reinterpret_cast<u32x4*>(tab + rows_per_wg * nb)[j] = tu[u];
-      }
+  for (int u = 0; u < kGuKsTabLoads; ++u) {
+    const int j = threadIdx.x + u * 64 * KS;
+    if (j < tab_n16) {
+      reinterpret_cast<u32x4*>(tab)[j] = tg[u];
+      reinterpret_cast<u32x4*>(tab + rows_per_wg * rb)[j] = tu[u];
+    }
+  }
+  if constexpr (S4) {
+    if ((int)threadIdx.x < tab_nb4) {
+      reinterpret_cast<uint32_t*>(tab_base)[threadIdx.x] = bg;
+      reinterpret_cast<uint32_t*>(tab_base + rows_per_wg)[threadIdx.x] = bu;
     }
   }
   __syncthreads();
@@ -557,10 +560,16 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int st = s0 + d;
-      load(gr[(d + D - 1) % D], gcod, gsc, st + D - 1);
-      load(ur[(d + D - 1) % D], ucod, usc, st + D - 1);
+      load(gr[(d + D - 1) % D], gcod, st + D - 1);
+      load(ur[(d + D - 1) % D], ucod, st + D - 1);
       const int rr = 2 * st + rsub;  // a row past I reads table bytes no result uses
-      if constexpr (TAB) {
+      if constexpr (S4) {
+        gr[d].s[0] = tab[rr * rb + (b >> 1)];
+        ur[d].s[0] = tab[(rows_per_wg + rr) * rb + (b >> 1)];
+        gr[d].base = tab_base[rr];
+        ur[d].base = tab_base[rows_per_wg + rr];
+        gr[d].valid = ur[d].valid = 1u;  // b < H/32 always
+      } else {
         gr[d].s[0] = tab[rr * nb + b];
         ur[d].s[0] = tab[(rows_per_wg + rr) * nb + b];
       }
@@ -671,18 +680,19 @@ constexpr int kDnKsLdsCap = 16384;
 // are deterministic).  Weight loads run D-1 steps ahead; rows_per_wg is a
 // multiple of 4*D, so the unrolled ring has no exit inside.
 //
-// TAB (8-bit scales only): the workgroup's scale bytes, rows_per_wg rows x
-// I/32 contiguous bytes of the table, are copied into LDS once, before the
+// TAB: the workgroup's scale bytes are copied into LDS once, before the
 // first row, by one 16-byte load per thread and chunk; each step then reads
-// its scale byte from LDS instead of issuing a one-byte load per code load.
+// its scale from LDS instead of issuing a one-byte load per code load.  The
+// table holds rows_per_wg rows x rb contiguous bytes of the matrix's scales:
+// 8-bit, rb = I/32 E8M0 bytes; scale4, rb = I/64 bytes of deltas, followed
+// by the rows' bases (rows_per_wg bytes, loaded a dword per thread).
 template <int KS, int D, bool S4, bool TAB>
 __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ hbuf,
                                                      const int32_t* __restrict__ pair_expert,
                                                      const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales, int H, int I, int E,
                                                      int parts, int rows_per_wg, float* __restrict__ ybuf) {
-  static_assert(!(TAB && S4), "the LDS scale table holds 8-bit scales");
-  extern __shared__ float partial[];  // [rows_per_wg][KS], then (TAB) the scale table [rows_per_wg][I/32]
+  extern __shared__ float partial[];  // [rows_per_wg][KS], then (TAB) the scale table
   const int p = blockIdx.x / parts;
   const int part = blockIdx.x % parts;
   const int lane = threadIdx.x % kWave, ks = threadIdx.x / kWave;
@@ -699,19 +709,30 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
   const int r0 = part * rows_per_wg;
   const int steps = rows_per_wg / 4;
 
-  // TAB: the table's 16-byte chunks, loaded first (the ring's loads behind
-  // them need not land before the table is written to LDS)
+  // TAB: the table's 16-byte chunks (and scale4 bases), loaded first (the
+  // ring's loads behind them need not land before the table is written to
+  // LDS).  rows_per_wg * rb is a multiple of 16, so the last chunk of a
+  // short last part stays inside the delta rows.
+  const int rb = S4 ? nbk / 2 : nbk;
   uint8_t* tab = reinterpret_cast<uint8_t*>(partial + rows_per_wg * KS);
-  const int tab_n16 = TAB ? (min(rows_per_wg, H - r0) * nbk) / 16 : 0;
-  constexpr int kTabLoads = 2;  // chunks per thread (rows_per_wg * I/32 <= 2 * 16 * 64 * KS)
+  uint8_t* tab_base = tab + rows_per_wg * rb;  // scale4 bases
+  const int nrows = min(rows_per_wg, H - r0);
+  const int tab_n16 = TAB ? (nrows * rb + 15) / 16 : 0;
+  const int tab_nb4 = TAB && S4 ? (nrows + 3) / 4 : 0;
+  constexpr int kTabLoads = 2;  // chunks per thread (rows_per_wg * rb <= 2 * 16 * 64 * KS)
   u32x4 tv[kTabLoads];
+  uint32_t tbase = 0u;
   if constexpr (TAB) {
 #pragma unroll
     for (int u = 0; u < kTabLoads; ++u) {
       const int t = threadIdx.x + u * 64 * KS;
-      tv[u] = __builtin_amdgcn_raw_buffer_load_b128(dsc.tab, t < tab_n16 ? (uint32_t)r0 * (uint32_t)nbk + 16u * t : kOOB,
+      tv[u] = __builtin_amdgcn_raw_buffer_load_b128(dsc.tab, t < tab_n16 ? (uint32_t)r0 * (uint32_t)rb + 16u * t : kOOB,
                                                     0, 2 /* nt */);
     }
+    if constexpr (S4)
+      tbase = __builtin_amdgcn_raw_buffer_load_b32(dsc.base, (int)threadIdx.x < tab_nb4 ? (uint32_t)r0 + 4u * threadIdx.x
+                                                                                         : kOOB,
+                                                   0, 2 /* nt */);
   }
   auto load = [&](RowBlocks<1>& r, int st) {
     const int n = r0 + 4 * st + rsub;
@@ -752,6 +773,8 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
       const int t = threadIdx.x + u * 64 * KS;
       if (t < tab_n16) reinterpret_cast<u32x4*>(tab)[t] = tv[u];
     }
+    if constexpr (S4)
+      if ((int)threadIdx.x < tab_nb4) reinterpret_cast<uint32_t*>(tab_base)[threadIdx.x] = tbase;
     __syncthreads();
   }
 
@@ -761,8 +784,14 @@ __global__ __launch_bounds__(64 * KS) void k_down_ks(const float* __restrict__ h
       const int st = s0 + d;
       load(ring[(d + D - 1) % D], st + D - 1);
       if constexpr (TAB) {
-        const int rr = 4 * st + rsub;  // a row past H reads a byte no result uses
-        ring[d].s[0] = tab[rr * nbk + b];
+        const int rr = 4 * st + rsub;  // a row past H reads bytes no result uses
+        if constexpr (S4) {
+          ring[d].s[0] = tab[rr * rb + (b >> 1)];
+          ring[d].base = tab_base[rr];
+          ring[d].valid = 1u;  // b < I/32 always
+        } else {
+          ring[d].s[0] = tab[rr * nbk + b];
+        }
       }
       const float v = lane_group_sum<16>(row_dot<true, 1, S4, true>(ring[d], hr, sh));
       if (c == 15) partial[(4 * st + rsub) * KS + ks] = v;
@@ -855,7 +884,8 @@ static hipError_t gateup_ks_launch(int P, hipStream_t s, const void* x, int32_t*
   // the selection (SEL > 0, KS >= 2) keeps its scratch in the same LDS first
   constexpr size_t sel_lds = (SEL > 0 && KS >= 2) ? sizeof(TopkWgLds<KS>) : 0;
   auto lds_for = [&](int rows) {
-    return std::max(sel_lds, (size_t)rows * 2 * KS * 4 + (S4 ? 0 : (size_t)2 * rows * (H / 32)));
+    return std::max(sel_lds, (size_t)rows * 2 * KS * 4 +
+                                 (S4 ? (size_t)2 * rows * (H / 64 + 1) : (size_t)2 * rows * (H / 32)));
   };
   const int target = resident_wgs(k_gateup_ks<KS, D, XF32, SEL, S4>, lds_for(kGuKsMaxRows), 64 * KS);
   const int want = (target + P - 1) / P;
@@ -991,14 +1021,16 @@ static hipError_t down_dispatch(const float* hbuf, const int32_t* pair_expert, i
     if (rows > max_rows) rows = max_rows;
     const int parts = (H + rows - 1) / rows;
     // the LDS scale table when the workgroup's scales fit two 16-byte chunks per thread
-    const bool tab = !S4 && rows * (I / 32) <= 2 * 16 * 64 * ks;
-    const size_t lds = (size_t)rows * ks * 4 + (tab ? (size_t)rows * (I / 32) : 0);
+    // (scale4: deltas, I/64 bytes a row, then a base byte a row)
+    const int rb = S4 ? I / 64 : I / 32;
+    const bool tab = rows * rb <= 2 * 16 * 64 * ks && (!S4 || rows <= 4 * 64 * ks);
+    const size_t lds = (size_t)rows * ks * 4 + (tab ? (size_t)rows * rb + (S4 ? (size_t)rows : 0) : 0);
     const dim3 grid((unsigned)(P * parts));
 #define MOE_DN_KS(KS)                                                                                     \
   if (ks == KS) {                                                                                          \
     if (tab)                                                                                               \
-      k_down_ks<KS, D, false, true><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E,  \
-                                                              parts, rows, ybuf);                          \
+      k_down_ks<KS, D, S4, true><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E,     \
+                                                           parts, rows, ybuf);                             \
     else                                                                                                   \
       k_down_ks<KS, D, S4, false><<<grid, 64 * KS, lds, s>>>(hbuf, pair_expert, codes, scales, H, I, E,    \
                                                             parts, rows, ybuf);                            \

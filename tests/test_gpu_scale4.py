@@ -116,6 +116,43 @@ def test_scale4_forward_and_stages_bit_identical(T, xd):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+def test_scale4_split_k_stages_bit_identical(xd):
+    """H and I multiples of 1024 (the K-split GEMVs of the model's width, which
+    stage the scale4 deltas and bases in LDS): the routes-given and selecting
+    gate/up stages and the down stage over every expert, extreme rows
+    included, and the forward, equal the 8-bit table's bits.  The forward
+    runs one bf16 token (more would take the 8-bit layer's grouped form) or
+    three fp32 tokens (the decode form on both)."""
+    H, I, E, k, T = 2048, 1024, 6, 2, 3
+    _, c, s = layer_with_extreme_rows(H, I, E, k, 9250)
+    w = synth.Workload("s4k", 83, T, H, I, E, k, xd, weight_seed=9250)
+    desc, codes, scales, desc4, scale4 = upload(w, c, s)
+    x = sd.tokens(w, range(T))
+    pe = torch.arange(T * k, dtype=torch.int32, device=DEV) % E        # every expert, expert 1 included
+    lg = torch.from_numpy(np.random.default_rng(4).standard_normal((T, E)).astype(np.float32)).to(DEV)
+    wr = sd.router_w(w)
+    outs = []
+    for d, sc in ((desc, scales), (desc4, scale4)):
+        h = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+        moe.moe_mxfp4_gate_up(d, x, pe, k, codes, sc, h)
+        y = torch.empty(T * k, H, dtype=torch.float32, device=DEV)
+        moe.moe_mxfp4_down(d, h, pe, codes, sc, y)
+        hs = torch.empty(T * k, I, dtype=torch.float32, device=DEV)
+        idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+        wt = torch.empty(T, k, dtype=torch.float32, device=DEV)
+        moe.moe_mxfp4_gate_up_select(d, x, lg, k, codes, sc, idx, wt, hs)
+        tf = T if xd == "f32" else 1
+        out = torch.empty(tf, H, dtype=torch.float32, device=DEV)
+        ws = torch.empty(moe.workspace_bytes(d, tf, k), dtype=torch.uint8, device=DEV)
+        moe.moe_mxfp4_forward(d, x[:tf], wr, None, codes, sc, k, out, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (h, y, hs, idx, out)])
+    assert not np.all(np.isfinite(outs[0][1]))  # the extreme down rows reach y
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_scale4_many_bf16_tokens_decode_form_matches_oracle():
     H, I, E, k, T = 512, 256, 8, 2, 40
     w = synth.Workload("s4m", 82, T, H, I, E, k, "bf16", weight_seed=9300)
