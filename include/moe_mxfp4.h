@@ -219,7 +219,7 @@ moe_status moe_mxfp4_forward(const moe_layer_desc* desc, const void* x, moe_dtyp
  * ends; a call uses the array of the current device (stream must belong to
  * it).  A call whose moe_workspace_bytes(desc, n_tokens, k) exceeds 64 MiB
  * returns MOE_ERR_SCRATCH_LIMIT and enqueues nothing (at the K3 shape,
- * H = 7168, I = 1536, E = 896, k = 16, that admits up to 101 tokens).  The
+ * H = 7168, I = 1536, E = 896, k = 16, that admits up to 95 tokens).  The
  * array keeps the last call's contents; the forward needs none of it cleared.
  * Calls that overlap on one GPU (on different streams, or from different
  * threads, without ordering between them) race on the array and give
