@@ -590,10 +590,9 @@ def hostile_layer(H=512):
     has scale 255, so every h of that pair, and token 2's whole output, is NaN.
     Activations are N(0,1) * 2^-20 (exact in bf16), so no finite sum comes near
     the fp32 overflow threshold and every non-finite output is fixed by the
-    weights alone, whatever the summation order.  H = 1024 takes the decode
-    form whose down projection runs on the scaled MXFP4 matrix cores (its
-    fp32 fallback for tiles with scale bytes >= 253 and for the pair whose h
-    is NaN); H = 512 the plain fp32 GEMVs."""
+    weights alone, whatever the summation order.  H = 1024 takes the K-split
+    gate/up GEMV (one wave per 1024 columns) on the decode forms; H = 512 the
+    row-per-wave GEMVs."""
     I, E, k, T = 256, 8, 2, 5
     w = synth.Workload("hs", 69, T, H, I, E, k, "bf16", weight_seed=8100 if H == 512 else 8100 + H)
     c, s, _ = experts_host(w)
@@ -676,6 +675,35 @@ def test_forward_extreme_scale_bytes(form, H):
         assert np.array_equal(P.bits(out[inf]), P.bits(r_out[inf]))
     A = oracle.moe_abs_scale(x, r_idx, r_w, ex, w.H, w.I, w.E)
     for t in range(w.T):
+        f = fin[t]
+        if f.any():
+            P.assert_out_close(out[t][f][None], r_out[t][f][None])
+            P.assert_elementwise(out[t][f], r_out[t][f], A[t][f])
+
+
+@pytest.mark.parametrize("H", [512, 1024])
+def test_forward_extreme_scale_bytes_f32_grouped(H):
+    """The hostile layer with its five fp32 tokens given twice (10 tokens), so
+    the forward takes the grouped form on three exact bf16 terms of x: NaN
+    where the oracle has NaN (tokens 2 and 7 whole, column 10), +-inf or NaN
+    where it has +-inf (as on the bf16 grouped form), and every finite
+    element within both readings of the bar."""
+    w, c, s, ex, x, wr, b = hostile_layer(H)
+    desc, codes, scales = pack_whole(w, c, s)
+    x2 = np.concatenate([x, x])
+    out, logits, idx, wt = run_forward(desc, w, torch.from_numpy(x2).to(DEV), torch.from_numpy(wr).to(DEV),
+                                       torch.from_numpy(b).to(DEV), codes, scales, w.k)
+    r_out, _, r_idx, r_w = oracle.moe_forward(x2, wr, ex, w.H, w.I, w.k, bias=b, logits_override=logits)
+    assert np.array_equal(idx, r_idx)
+    assert np.all(idx[:, 0] == 1) and idx[2, 1] == 5 and idx[7, 1] == 5
+    assert np.all(np.isnan(r_out[[2, 7]])) and np.all(np.isnan(out[[2, 7]]))
+    fin = np.isfinite(r_out)
+    assert np.array_equal(np.isfinite(out), fin)
+    assert np.all(np.isnan(out[np.isnan(r_out)]))
+    inf = np.isinf(r_out)
+    assert inf.any() and np.all((out[inf] == r_out[inf]) | np.isnan(out[inf]))
+    A = oracle.moe_abs_scale(x2, r_idx, r_w, ex, w.H, w.I, w.E)
+    for t in range(x2.shape[0]):
         f = fin[t]
         if f.any():
             P.assert_out_close(out[t][f][None], r_out[t][f][None])
