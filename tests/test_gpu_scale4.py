@@ -153,6 +153,34 @@ def test_scale4_split_k_stages_bit_identical(xd):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_scale4_stack_bit_identical():
+    """A two-layer stack (RMSNorm inside the router kernel, fp32 residual,
+    fp32 activations into the K-split GEMVs) on scale4 side-cars equals the
+    stack on the 8-bit tables bit for bit, one token and three."""
+    H, I, E, k = 2048, 1024, 8, 2
+    for T in (1, 3):
+        w = synth.Workload("s4s", 84, T, H, I, E, k, "bf16", weight_seed=9260)
+        layers8, layers4 = [], []
+        for l in range(2):
+            c, s = synth.experts(w, l)
+            desc, codes, scales, desc4, scale4 = upload(w, c, s)
+            layers8.append((codes, scales))
+            layers4.append((codes, scale4))
+        wrs = [sd.router_w(w, l) for l in range(2)]
+        gam = [sd.gamma(w, l) for l in range(2)]
+        x = sd.tokens(w, range(T))
+        res = []
+        for d, layers in ((desc, layers8), (desc4, layers4)):
+            resid = torch.empty(T, H, dtype=torch.float32, device=DEV)
+            ws = torch.empty(moe.stack_workspace_bytes(d, T, k), dtype=torch.uint8, device=DEV)
+            moe.moe_mxfp4_stack_forward(d, [a for a, _ in layers], [b for _, b in layers], wrs, None, gam, w.eps, x, k,
+                                        resid, ws)
+            torch.cuda.synchronize()
+            res.append(resid.cpu().numpy())
+        assert np.all(np.isfinite(res[0]))
+        assert np.array_equal(P.bits(res[0]), P.bits(res[1])), T
+
+
 def test_scale4_many_bf16_tokens_decode_form_matches_oracle():
     H, I, E, k, T = 512, 256, 8, 2, 40
     w = synth.Workload("s4m", 82, T, H, I, E, k, "bf16", weight_seed=9300)
