@@ -423,10 +423,15 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(const void* __restrict__ x,
 // the first row, so the only weight loads are the code loads.
 // SEL as in k_gateup_gemv; with KS >= 2 waves the selection's per-logit work
 // is shared by all of them (topk_wg), and every wave loads x after it.
-constexpr int kGuKsRing = 4;       // weight steps in flight + 1
+// Weight steps in flight + 1: 3 with bf16 x, 4 with fp32 x.  Measured on the
+// selecting kernel (decode): bf16 31.7-31.9 us at 3 against 32.3 at 4 and
+// 32.9 at 5; fp32 (the 12-layer stack) 0.771 ms per token at 4 against 0.788
+// at 3 and 0.781 at 5.
+template <bool XF32>
+constexpr int gu_ks_ring() { return XF32 ? 4 : 3; }
 constexpr int kGuKsTabLoads = 2;   // 16-byte scale chunks per thread and matrix
 // rows_per_wg * H/32 <= kGuKsTabLoads * 16 * 64 * KS (the table's capacity), in whole ring passes
-constexpr int kGuKsMaxRows = 32 * kGuKsTabLoads / (2 * kGuKsRing) * (2 * kGuKsRing);
+constexpr int gu_ks_max_rows(int ring) { return 32 * kGuKsTabLoads / (2 * ring) * (2 * ring); }
 
 template <int KS, int D, bool XF32, int SEL, bool S4>
 __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ x, int32_t* __restrict__ route,
@@ -512,9 +517,8 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
   uint8_t* tab = reinterpret_cast<uint8_t*>(partial + rows_per_wg * 2 * KS);
   uint8_t* tab_base = tab + 2 * rows_per_wg * rb;  // scale4: gate bases, then up bases
   const int tab_n16 = nrows * rb / 16;             // chunks per matrix
-  const int tab_nb4 = S4 ? (nrows + 3) / 4 : 0;    // dwords of bases per matrix
   u32x4 tg[kGuKsTabLoads], tu[kGuKsTabLoads];
-  uint32_t bg = 0u, bu = 0u;
+  uint32_t bg = 0u, bu = 0u;                       // scale4: this thread's row base (one byte a thread)
 #pragma unroll
   for (int u = 0; u < kGuKsTabLoads; ++u) {
     const int j = threadIdx.x + u * 64 * KS;
@@ -523,9 +527,10 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     tu[u] = __builtin_amdgcn_raw_buffer_load_b128(usc.tab, off, 0, 2 /* nt */);
   }
   if constexpr (S4) {
-    const uint32_t off = (int)threadIdx.x < tab_nb4 ? (uint32_t)r0 + 4u * threadIdx.x : kOOB;
-    bg = __builtin_amdgcn_raw_buffer_load_b32(gsc.base, off, 0, 2 /* nt */);
-    bu = __builtin_amdgcn_raw_buffer_load_b32(usc.base, off, 0, 2 /* nt */);
+    // byte loads: r0 is a multiple of two ring passes, not necessarily of 4
+    const uint32_t off = (int)threadIdx.x < nrows ? (uint32_t)r0 + threadIdx.x : kOOB;
+    bg = __builtin_amdgcn_raw_buffer_load_b8(gsc.base, off, 0, 2 /* nt */);
+    bu = __builtin_amdgcn_raw_buffer_load_b8(usc.base, off, 0, 2 /* nt */);
   }
   auto load = [&](RowBlocks<1>& r, rsrc_t cod, int st) {
     const int n = r0 + 2 * st + rsub;
@@ -549,9 +554,9 @@ __global__ __launch_bounds__(64 * KS) void k_gateup_ks(const void* __restrict__ 
     }
   }
   if constexpr (S4) {
-    if ((int)threadIdx.x < tab_nb4) {
-      reinterpret_cast<uint32_t*>(tab_base)[threadIdx.x] = bg;
-      reinterpret_cast<uint32_t*>(tab_base + rows_per_wg)[threadIdx.x] = bu;
+    if ((int)threadIdx.x < nrows) {
+      tab_base[threadIdx.x] = (uint8_t)bg;
+      tab_base[rows_per_wg + threadIdx.x] = (uint8_t)bu;
     }
   }
   __syncthreads();
@@ -875,23 +880,25 @@ static void split_rows(int rows, int P, int unit, int target, int* parts, int* p
 
 // The K-split gate/up for H = 1024*KS: about as many workgroups as the GPU
 // holds at once share all pairs' rows equally (rows per workgroup a multiple
-// of two ring passes, at most kGuKsMaxRows so the scale table fits).
+// of two ring passes, at most gu_ks_max_rows so the scale table fits).
 template <int KS, bool XF32, int SEL, bool S4>
 static hipError_t gateup_ks_launch(int P, hipStream_t s, const void* x, int32_t* route, const float* logits,
                                    float* wsel, const uint8_t* codes, const uint8_t* scales, int H, int I, int E,
                                    int k, float* hbuf) {
-  constexpr int D = kGuKsRing;
+  constexpr int D = gu_ks_ring<XF32>();
+  constexpr int kMaxRows = gu_ks_max_rows(D);
+  static_assert(kMaxRows % (2 * D) == 0, "whole ring passes");
   // the selection (SEL > 0, KS >= 2) keeps its scratch in the same LDS first
   constexpr size_t sel_lds = (SEL > 0 && KS >= 2) ? sizeof(TopkWgLds<KS>) : 0;
   auto lds_for = [&](int rows) {
     return std::max(sel_lds, (size_t)rows * 2 * KS * 4 +
                                  (S4 ? (size_t)2 * rows * (H / 64 + 1) : (size_t)2 * rows * (H / 32)));
   };
-  const int target = resident_wgs(k_gateup_ks<KS, D, XF32, SEL, S4>, lds_for(kGuKsMaxRows), 64 * KS);
+  const int target = resident_wgs(k_gateup_ks<KS, D, XF32, SEL, S4>, lds_for(kMaxRows), 64 * KS);
   const int want = (target + P - 1) / P;
   int rows = (I + want - 1) / want;
   rows = (rows + 2 * D - 1) / (2 * D) * (2 * D);
-  if (rows > kGuKsMaxRows) rows = kGuKsMaxRows;
+  if (rows > kMaxRows) rows = kMaxRows;
   const int parts = (I + rows - 1) / rows;
   k_gateup_ks<KS, D, XF32, SEL, S4><<<dim3((unsigned)(P * parts)), 64 * KS, lds_for(rows), s>>>(
       x, route, logits, wsel, codes, scales, H, I, E, k, parts, rows, hbuf);
@@ -902,7 +909,6 @@ template <bool XF32, int SEL, bool S4>
 static hipError_t gateup_dispatch(int nbl, int P, size_t lds, hipStream_t s, const void* x, int32_t* route,
                                   const float* logits, float* wsel, const uint8_t* codes, const uint8_t* scales,
                                   int H, int I, int E, int k, float* hbuf) {
-  static_assert(kGuKsMaxRows % (2 * kGuKsRing) == 0, "whole ring passes");
   if (SEL <= 16 && H % 1024 == 0) {  // K split across H/1024 waves
 #define MOE_GUK(KS) \
   return gateup_ks_launch<KS, XF32, (SEL <= 16 ? SEL : 16), S4>(P, s, x, route, logits, wsel, codes, scales, H, I, E, k, hbuf);
